@@ -1,0 +1,20 @@
+"""CPU oracle of the BitLinear (W1.58A8) forward: test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path never does.
+"""
+
+from .bitlinear_ref import (  # noqa: F401
+    EPS_A,
+    EPS_W,
+    QB,
+    absmean_gamma,
+    contract,
+    forward,
+    pack_ternary,
+    pack_weights,
+    quant_act,
+    rescale,
+    ternarize,
+    widen_bf16,
+)

@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each pin is a function ``pin(o)`` taking an oracle-like namespace ``o`` (the
+real oracle package, or a copy with a planted mistake) and raising
+AssertionError when ``o`` disagrees with the fact it checks.  The facts are:
+hand-derived worked examples (tests/golden/worked_examples.json), exact
+rational arithmetic (fractions.Fraction), one-operation-at-a-time binary64
+routes that round once to binary32, brute force on tiny inputs, invariants
+of the definitions (permutation, power-of-two scaling, sign symmetry, zero
+rows), and the ternary zero fraction of Gaussian weights.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
+    GOLD = json.load(f)
+
+F32_EPS = float(np.float32(1e-5))
+
+
+def f32(v):
+    return float(np.float32(v))
+
+
+# ---------------------------------------------------------------- worked examples
+
+def pin_e1_ternarize(o):
+    e = GOLD["E1_ternarize"]
+    w = np.array(e["W"], np.float32)
+    g = o.absmean_gamma(w)
+    assert float(g) == e["gamma"]
+    d = np.float32(g) + np.float32(1e-5)
+    assert int(np.float32(d).view(np.uint32)) == int(e["d_bits"], 16)
+    assert o.ternarize(w, g).tolist() == e["t"]
+
+
+def pin_e2_epsilon(o):
+    e = GOLD["E2_epsilon_moves_threshold"]
+    w = np.array(e["W"], np.float32)
+    assert o.ternarize(w, o.absmean_gamma(w)).tolist() == e["t"]
+
+
+def pin_e3_layout(o):
+    e = GOLD["E3_layout"]
+    t = np.array([e["t_row"]], np.int8)
+    assert o.pack_ternary(t)[0].tolist() == e["bytes"]
+
+
+def pin_e4_act_quant(o):
+    e = GOLD["E4_act_quant"]
+    q, a, rs = o.quant_act(np.array(e["x"], np.float32))
+    assert q.tolist() == e["q"]
+    assert a.tolist() == e["absmax"]
+    assert rs.tolist() == e["rowsum"]
+
+
+def pin_e5_contract_rescale(o):
+    e1, e4, e5 = GOLD["E1_ternarize"], GOLD["E4_act_quant"], GOLD["E5_contract_rescale"]
+    t = np.array(e1["t"], np.int8)
+    q = np.array(e4["q"], np.int8)
+    acc = o.contract(q, t)
+    assert acc.tolist() == e5["acc"]
+    y = o.rescale(acc, np.float32(e1["gamma"]), np.array(e4["absmax"], np.float32))
+    assert np.array_equal(np.asarray(y, np.float64), np.array(e5["y"]))
+
+
+# ---------------------------------------------------------------- gamma
+
+def _gamma_by_fractions(w):
+    s = sum(Fraction(float(v)) for v in np.abs(w).ravel())
+    mean = float(s) / float(w.size)          # float(Fraction) rounds to nearest
+    return np.float32(mean)
+
+
+def _awkward_weights(rng, n, k):
+    """Magnitudes spread over many binades, including subnormals, so that any
+    inexact or order-dependent sum shows up in the rounded result."""
+    mant = rng.random((n, k)) + 0.5
+    expo = rng.integers(-140, 90, size=(n, k))
+    w = (mant * np.exp2(expo.astype(np.float64))).astype(np.float32)
+    w *= np.where(rng.random((n, k)) < 0.5, -1, 1).astype(np.float32)
+    w[rng.random((n, k)) < 0.1] = 0.0
+    return w
+
+
+def pin_gamma_exact_fraction(o):
+    rng = np.random.default_rng(11)
+    cases = [_awkward_weights(rng, 3, 16), _awkward_weights(rng, 7, 32),
+             rng.standard_normal((5, 48)).astype(np.float32) * np.float32(0.02)]
+    # one huge value beside many small ones: a naive float sum loses the small ones
+    big = np.full((4, 64), 1.0, np.float32)
+    big[0, 0] = np.float32(2.0 ** 60)
+    cases.append(big)
+    # S = 2**60 + 2**36 + 254: RN64(S) = 2**60 + 2**36 + 256, so the mean lies
+    # just above a binary32 midpoint and rounds up; a running binary64 sum
+    # drops every 1.0, lands on the midpoint itself and rounds to even (down).
+    tie = np.ones((16, 16), np.float32)
+    tie[0, 0] = np.float32(2.0 ** 60)
+    tie[0, 1] = np.float32(2.0 ** 36)
+    cases.append(tie)
+    small = np.full((2, 16), np.float32(1e-3), np.float32)
+    small[1, 3] = np.float32(3.0e7)
+    cases.append(small)
+    for w in cases:
+        g = o.absmean_gamma(w)
+        assert np.float32(g).view(np.uint32) == _gamma_by_fractions(w).view(np.uint32)
+
+
+def pin_gamma_constant(o):
+    for c in (0.02, -0.75, 3.0e-20, 1.0, 12345.678):
+        for shape in ((1, 16), (3, 7), (64, 96)):
+            w = np.full(shape, np.float32(c), np.float32)
+            assert np.float32(o.absmean_gamma(w)) == np.float32(abs(np.float32(c)))
+
+
+def pin_gamma_pow2_scaling(o):
+    rng = np.random.default_rng(12)
+    w = rng.standard_normal((33, 64)).astype(np.float32)
+    g = np.float32(o.absmean_gamma(w))
+    for k in (-7, -1, 3, 20):
+        gk = np.float32(o.absmean_gamma(w * np.float32(2.0 ** k)))
+        assert gk == g * np.float32(2.0 ** k)
+
+
+def pin_gamma_permutation(o):
+    rng = np.random.default_rng(13)
+    w = _awkward_weights(rng, 16, 64)
+    g = np.float32(o.absmean_gamma(w)).view(np.uint32)
+    for _ in range(3):
+        p = rng.permutation(w.ravel()).reshape(w.shape)
+        assert np.float32(o.absmean_gamma(p)).view(np.uint32) == g
+    # row and column reversal as well (a transposed reading of W)
+    assert np.float32(o.absmean_gamma(np.ascontiguousarray(w.T))).view(np.uint32) == g
+
+
+# ---------------------------------------------------------------- ternarize
+
+def _ternarize_scalar(wv, gamma):
+    d = f32(f32(gamma) + F32_EPS)            # one binary32 addition
+    u = f32(float(wv) / d)                   # binary64 quotient, rounded once to binary32
+    r = round(u)                             # Python rounds half to even
+    return max(-1, min(1, r))
+
+
+def pin_ternarize_independent(o):
+    rng = np.random.default_rng(14)
+    gamma = np.float32(0.0161)
+    d = np.float32(gamma) + np.float32(1e-5)
+    w = rng.standard_normal(2000).astype(np.float32) * np.float32(0.02)
+    # exact ties and their neighbours: u = 0.5 and u = 1.5 exactly
+    ties = np.array([0.5, 1.5, 2.5], np.float32) * d
+    nbrs = np.concatenate([np.nextafter(ties, np.float32(1)), np.nextafter(ties, np.float32(0))])
+    w = np.concatenate([w, ties, -ties, nbrs, -nbrs, [0.0, -0.0]]).astype(np.float32)
+    t = o.ternarize(w.reshape(1, -1), gamma)[0]
+    ref = [_ternarize_scalar(v, gamma) for v in w]
+    assert t.tolist() == ref
+
+
+def pin_ternarize_sign_symmetry(o):
+    rng = np.random.default_rng(15)
+    w = rng.standard_normal((8, 64)).astype(np.float32) * np.float32(0.02)
+    g = o.absmean_gamma(w)
+    assert np.array_equal(o.ternarize(-w, g), -o.ternarize(w, g))
+
+
+def pin_zero_fraction(o):
+    """For W ~ N(0, s) the absmean is s*sqrt(2/pi) and the threshold half of
+    it, so P(t = 0) = erf(sqrt(2/pi) / (2 sqrt 2)) = 0.3101 (each sign 0.345)."""
+    rng = np.random.default_rng(16)
+    w = rng.standard_normal((512, 2048)).astype(np.float32) * np.float32(0.02)
+    t = o.ternarize(w, o.absmean_gamma(w))
+    p0 = math.erf(math.sqrt(2 / math.pi) / (2 * math.sqrt(2)))
+    assert abs(float(np.mean(t == 0)) - p0) < 0.005
+    assert abs(float(np.mean(t == 1)) - (1 - p0) / 2) < 0.005
+    assert abs(float(np.mean(t == -1)) - (1 - p0) / 2) < 0.005
+
+
+# ---------------------------------------------------------------- pack
+
+def _decode_bytes(row_bytes, k):
+    """Independent decoder: read each weight's two bits one by one."""
+    out = []
+    for kk in range(k):
+        g, r = divmod(kk, 16)
+        j, i = divmod(r, 4)
+        byte = row_bytes[4 * g + i]
+        code = (byte >> (2 * j)) & 3
+        assert code != 3
+        out.append(code - 1)
+    return out
+
+
+def pin_pack_roundtrip(o):
+    rng = np.random.default_rng(17)
+    t = rng.integers(-1, 2, size=(5, 96)).astype(np.int8)
+    t[2] = 0
+    p = o.pack_ternary(t)
+    assert p.shape == (5, 24) and p.dtype == np.uint8
+    for n in range(5):
+        assert _decode_bytes(p[n].tolist(), 96) == t[n].tolist()
+    assert p[2].tolist() == [0x55] * 24
+
+
+# ---------------------------------------------------------------- act-quant
+
+def _quant_scalar_row(row):
+    a = max(abs(float(v)) for v in row)
+    m = max(a, F32_EPS)
+    s = f32(127.0 / m)                       # one binary32 division
+    out = []
+    for v in row:
+        p = f32(float(v) * s)                # exact binary64 product, rounded once
+        out.append(max(-127, min(127, round(p))))
+    return out, a
+
+
+def pin_quant_act_independent(o):
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((6, 4096)).astype(np.float32)
+    x[1] = rng.standard_t(4, 4096).astype(np.float32)
+    x[2] = 0.0
+    x[3] *= np.float32(1e-4)
+    # make ties: x * s = k + 0.5 exactly when absmax = 127
+    x[4, :8] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -126.5, 126.5]
+    x[4, 8:] = rng.uniform(-100, 100, 4088).astype(np.float32)
+    q, a, rs = o.quant_act(x)
+    for r in range(x.shape[0]):
+        ref, ar = _quant_scalar_row(x[r])
+        assert q[r].tolist() == ref
+        assert float(a[r]) == ar
+        assert int(rs[r]) == sum(ref)
+
+
+def pin_quant_act_order_sensitive(o):
+    """A case where 127/m is rounded before the product matters: the product
+    x * RN32(127/m) and RN32(x*127)/m round to opposite sides of a half."""
+    # absmax 15.317623 (0x417514FC) and x = 1.2664177 (0x3FA219FA):
+    # x * RN32(127/m) = 10.5 exactly -> 10, while RN32(x*127)/m = 10.500001 -> 11;
+    # absmax 12.734374 (0x414BBFFF), x = -2.25609 (0xC01063C7): -22.500002 -> -23
+    # against -22.5 -> -22.
+    bits = np.array([[0x417514FC, 0x3FA219FA, 0, 0],
+                     [0xC14BBFFF, 0xC01063C7, 0x3F800000, 0]], np.uint32)
+    x = np.tile(bits.view(np.float32), (1, 4))
+    q, _, _ = o.quant_act(x)
+    assert q[0, 1] == 10 and q[1, 1] == -23
+    for r in range(x.shape[0]):
+        ref, _ = _quant_scalar_row(x[r])
+        assert q[r].tolist() == ref
+
+
+def pin_quant_act_invariants(o):
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((16, 256)).astype(np.float32)
+    x[5] = 0.0
+    q, a, _ = o.quant_act(x)
+    for r in range(16):
+        if r == 5:
+            assert not q[r].any() and float(a[r]) == 0.0
+        else:
+            assert int(np.max(np.abs(q[r].astype(np.int32)))) == 127
+    assert int(q.astype(np.int32).min()) >= -127
+    qn, an, _ = o.quant_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(an, a)
+    for k in (-10, 4):
+        qk, _, _ = o.quant_act(x * np.float32(2.0 ** k))
+        assert np.array_equal(qk, q)
+    # one token per row: T rows quantise independently of each other
+    q1, _, _ = o.quant_act(x[3:4])
+    assert np.array_equal(q1[0], q[3])
+
+
+def pin_widen_bf16(o):
+    bits = np.array([[0x3F80, 0xC040, 0x0000, 0x8000, 0x4049, 0x0001]], np.uint16)
+    x = o.widen_bf16(bits)
+    assert x[0, :4].tolist() == [1.0, -3.0, 0.0, -0.0]
+    assert x[0, 4] == np.float32(3.140625)
+    assert x[0, 5] == np.float32(2.0 ** -133)
+
+
+# ---------------------------------------------------------------- contraction
+
+def pin_contract_bruteforce(o):
+    rng = np.random.default_rng(21)
+    k = 5
+    rows = np.array(np.meshgrid(*[[-1, 0, 1]] * k, indexing="ij")).reshape(k, -1).T
+    k16 = 16
+    t = np.zeros((rows.shape[0], k16), np.int8)
+    t[:, :k] = rows
+    t[:, k:] = rng.integers(-1, 2, size=(rows.shape[0], k16 - k))
+    q = rng.integers(-127, 128, size=(3, k16)).astype(np.int8)
+    acc = o.contract(q, t)
+    assert acc.shape == (3, rows.shape[0]) and acc.dtype == np.int32
+    for a in range(3):
+        for n in range(rows.shape[0]):
+            s = 0
+            for kk in range(k16):
+                s += int(t[n, kk]) * int(q[a, kk])
+            assert int(acc[a, n]) == s
+
+
+def pin_contract_invariants(o):
+    rng = np.random.default_rng(22)
+    t = rng.integers(-1, 2, size=(9, 128)).astype(np.int8)
+    t[4] = 0
+    q = rng.integers(-127, 128, size=(7, 128)).astype(np.int8)
+    q[:, :3] = 127
+    acc = o.contract(q, t)
+    assert not acc[:, 4].any()
+    p = rng.permutation(128)
+    assert np.array_equal(o.contract(q[:, p], t[:, p]), acc)
+    assert np.array_equal(o.contract(q, -t), -acc)
+    # a square, non-symmetric t checked against explicit loops
+    ts = rng.integers(-1, 2, size=(16, 16)).astype(np.int8)
+    qs = rng.integers(-127, 128, size=(3, 16)).astype(np.int8)
+    accs = o.contract(qs, ts)
+    for a in range(3):
+        for n in range(16):
+            assert int(accs[a, n]) == sum(int(ts[n, kk]) * int(qs[a, kk]) for kk in range(16))
+    # extremes: all +127 against all +1 gives 127*K
+    full = o.contract(np.full((1, 128), 127, np.int8), np.ones((1, 128), np.int8))
+    assert int(full[0, 0]) == 127 * 128
+
+
+def pin_contract_large_k(o):
+    """K = 2**18: partial sums pass 2**24, where a binary32 accumulator would
+    start to round; the int64 dot product is the independent route."""
+    rng = np.random.default_rng(24)
+    k = 1 << 18
+    q = rng.integers(90, 128, size=(2, k)).astype(np.int8)
+    q[1, ::3] = -127
+    t = rng.integers(0, 2, size=(3, k)).astype(np.int8)
+    t[2] = 1
+    t[2, 7] = 0
+    acc = o.contract(q, t)
+    ref = q.astype(np.int64) @ t.astype(np.int64).T
+    assert np.array_equal(acc.astype(np.int64), ref)
+
+
+# ---------------------------------------------------------------- rescale
+
+def pin_rescale(o):
+    rng = np.random.default_rng(23)
+    acc = rng.integers(-300000, 300000, size=(4, 6)).astype(np.int32)
+    acc[1, 2] = 0
+    gamma = np.float32(0.0159)
+    absmax = np.array([3.5, 0.0, 1e-7, 17.25], np.float32)
+    y = np.asarray(o.rescale(acc, gamma, absmax), np.float64)
+    for t in range(4):
+        m = Fraction(float(max(absmax[t], np.float32(1e-5))))
+        for n in range(6):
+            exact = Fraction(int(acc[t, n])) * Fraction(float(gamma)) * m / 127
+            if exact == 0:
+                assert y[t, n] == 0.0
+            else:
+                assert abs(Fraction(float(y[t, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+    assert y[1, 2] == 0.0
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

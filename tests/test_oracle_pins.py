@@ -1,0 +1,186 @@
+"""The oracle against facts that do not come from itself (CPU only).
+
+``test_pin`` runs every pin of tests/pins.py on the oracle.  ``test_mutant``
+plants one plausible mistake at a time into a copy of the oracle (a dropped
+epsilon, another rounding rule, a swapped bit order, a per-row instead of a
+per-matrix scale, a transposed or truncated contraction, ...) and checks that
+at least one pin fails, so each pin set is shown to be able to see it.
+"""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+
+def _ns(**overrides):
+    d = {k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("__")}
+    d.update(overrides)
+    return types.SimpleNamespace(**d)
+
+
+@pytest.mark.parametrize("pin", pins.PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(oracle)
+
+
+# ------------------------------------------------------------------ mutants
+
+def _per_row_gamma(w):
+    w = np.asarray(w, np.float32)
+    return np.float32(np.mean(np.abs(w), axis=1, dtype=np.float64)[0])
+
+
+def _f32_sum_gamma(w):
+    w = np.asarray(w, np.float32)
+    s = np.float32(0)
+    for v in np.abs(w).ravel():
+        s = np.float32(s + v)
+    return np.float32(s / np.float32(w.size))
+
+
+def _f64_sequential_gamma(w):
+    w = np.asarray(w, np.float32)
+    s = 0.0
+    for v in np.abs(w).ravel().tolist():
+        s += v
+    return np.float32(s / w.size)
+
+
+def _tern_no_eps(w, gamma):
+    u = np.asarray(w, np.float32) / np.float32(gamma)
+    return np.clip(np.rint(u), -1, 1).astype(np.int8)
+
+
+def _half_away(v):
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def _tern_half_away(w, gamma):
+    u = np.asarray(w, np.float32) / (np.float32(gamma) + np.float32(1e-5))
+    return np.clip(_half_away(u), -1, 1).astype(np.int8)
+
+
+def _tern_eps_as_max(w, gamma):
+    u = np.asarray(w, np.float32) / np.maximum(np.float32(gamma), np.float32(1e-5))
+    return np.clip(np.rint(u), -1, 1).astype(np.int8)
+
+
+def _tern_threshold_gamma(w, gamma):
+    # the prose paraphrase "above the mean -> +1" instead of eq. (1)-(2)
+    w = np.asarray(w, np.float32)
+    return ((w > gamma).astype(np.int8) - (w < -gamma).astype(np.int8))
+
+
+def _pack_swapped(t):
+    n, k = t.shape
+    c = (t.astype(np.int64) + 1).astype(np.uint32).reshape(n, k // 16, 4, 4)
+    words = np.zeros((n, k // 16), np.uint32)
+    for j in range(4):
+        for i in range(4):
+            words |= c[:, :, j, i] << np.uint32(2 * i + 8 * j)
+    return words.astype("<u4").view(np.uint8).reshape(n, k // 4)
+
+
+def _pack_twos_complement(t):
+    n, k = t.shape
+    c = (t.astype(np.int64) & 3).astype(np.uint32).reshape(n, k // 16, 4, 4)
+    words = np.zeros((n, k // 16), np.uint32)
+    for j in range(4):
+        for i in range(4):
+            words |= c[:, :, j, i] << np.uint32(8 * i + 2 * j)
+    return words.astype("<u4").view(np.uint8).reshape(n, k // 4)
+
+
+def _make_quant(rounder=np.rint, qb=127, order="scale_first", eps=True, per_token=True):
+    def quant(x):
+        x = np.asarray(x)
+        if x.dtype == np.uint16:
+            x = oracle.widen_bf16(x)
+        x = np.asarray(x, np.float32)
+        a = np.max(np.abs(x), axis=1) if per_token else np.full(x.shape[0], np.max(np.abs(x)), np.float32)
+        m = np.maximum(a, np.float32(1e-5)) if eps else a
+        if order == "scale_first":
+            v = x * (np.float32(qb) / m)[:, None]
+        else:
+            v = (x * np.float32(qb)) / m[:, None]
+        with np.errstate(invalid="ignore"):
+            q = np.clip(rounder(v), -127, 127)
+        if not np.all(np.isfinite(q)):
+            raise FloatingPointError("non-finite q")
+        q = q.astype(np.int8)
+        return q, a.astype(np.float32), q.astype(np.int64).sum(axis=1).astype(np.int32)
+    return quant
+
+
+def _contract_neg(q, t):
+    return -oracle.contract(q, t)
+
+
+def _contract_drop_last(q, t):
+    return oracle.contract(q[:, :-1], t[:, :-1])
+
+
+def _contract_transposed_t(q, t):
+    tt = np.asarray(t)
+    if tt.shape[0] == tt.shape[1]:
+        tt = tt.T
+    return oracle.contract(q, tt)
+
+
+def _contract_f32(q, t):
+    acc = np.asarray(q, np.float32) @ np.asarray(t, np.float32).T
+    return acc.astype(np.int32)
+
+
+def _rescale_gamma_eps(acc, gamma, absmax):
+    return oracle.rescale(acc, np.float32(gamma) + np.float32(1e-5), absmax)
+
+
+def _rescale_128(acc, gamma, absmax):
+    return oracle.rescale(acc, gamma, absmax) * (127.0 / 128.0)
+
+
+def _rescale_no_floor(acc, gamma, absmax):
+    m = np.asarray(absmax, np.float32).astype(np.float64)
+    return np.asarray(acc, np.float64) * np.float64(gamma) * m[:, None] / 127.0
+
+
+MUTANTS = {
+    "gamma_per_row": dict(absmean_gamma=_per_row_gamma),
+    "gamma_f32_running_sum": dict(absmean_gamma=_f32_sum_gamma),
+    "gamma_f64_running_sum": dict(absmean_gamma=_f64_sequential_gamma),
+    "ternarize_no_eps": dict(ternarize=_tern_no_eps),
+    "ternarize_half_away": dict(ternarize=_tern_half_away),
+    "ternarize_eps_as_max": dict(ternarize=_tern_eps_as_max),
+    "ternarize_threshold_gamma": dict(ternarize=_tern_threshold_gamma),
+    "pack_swapped_bits": dict(pack_ternary=_pack_swapped),
+    "pack_twos_complement": dict(pack_ternary=_pack_twos_complement),
+    "quant_half_away": dict(quant_act=_make_quant(rounder=_half_away)),
+    "quant_qb128": dict(quant_act=_make_quant(qb=128)),
+    "quant_product_first": dict(quant_act=_make_quant(order="product_first")),
+    "quant_no_eps": dict(quant_act=_make_quant(eps=False)),
+    "quant_per_tensor": dict(quant_act=_make_quant(per_token=False)),
+    "contract_negated": dict(contract=_contract_neg),
+    "contract_drop_last_k": dict(contract=_contract_drop_last),
+    "contract_transposed": dict(contract=_contract_transposed_t),
+    "contract_f32": dict(contract=_contract_f32),
+    "rescale_gamma_plus_eps": dict(rescale=_rescale_gamma_eps),
+    "rescale_by_128": dict(rescale=_rescale_128),
+    "rescale_no_floor": dict(rescale=_rescale_no_floor),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    o = _ns(**MUTANTS[name])
+    failed = []
+    for pin in pins.PINS:
+        try:
+            pin(o)
+        except Exception:  # an assertion, or the mutant raising on a pin's input
+            failed.append(pin.__name__)
+    assert failed, f"no pin detects the planted mistake {name}"
