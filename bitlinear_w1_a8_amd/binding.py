@@ -1,0 +1,146 @@
+"""ctypes binding of libbitlinear.so (include/bitlinear.h), same names.
+
+Argument marshalling only: tensors are allocated with torch on the caller's
+device, their data pointers and the current HIP stream are passed to the C
+ABI, and a non-OK status raises BitLinearError with the library's message.
+Every step of the forward runs in the library's HIP kernels; there is no
+other code path.  If the library is not built, loading raises ImportError.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitlinear.so")
+
+BL_F32, BL_BF16 = 0, 1
+ALGOS = {"auto": 0, "gemv": 1, "gemm": 2}
+
+_lib = None
+
+_c_i64, _c_sz, _c_vp, _c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+
+# name -> (restype, argtypes), as declared in include/bitlinear.h
+SIGNATURES = {
+    "bitlinear_abi_version": (_c_int, []),
+    "bitlinear_last_error": (ctypes.c_char_p, []),
+    "bitlinear_gemv_max_tokens": (_c_i64, []),
+    "bitlinear_pack_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "bitlinear_pack_weights": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "bitlinear_quant_act": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "bitlinear_forward": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp,
+                                   _c_vp, _c_vp]),
+    "bitlinear_forward_algo": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                        _c_vp, _c_vp, _c_int, _c_vp]),
+}
+
+
+class BitLinearError(RuntimeError):
+    """A non-OK status from libbitlinear; ``status`` holds the code."""
+
+    def __init__(self, status, message):
+        super().__init__(f"libbitlinear status {status}: {message}")
+        self.status = status
+
+
+def load():
+    """Load libbitlinear.so once and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m bitlinear_w1_a8_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def last_error():
+    return load().bitlinear_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise BitLinearError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemv_max_tokens():
+    return int(load().bitlinear_gemv_max_tokens())
+
+
+def pack_weights(w):
+    """Step A0 on the GPU: float32 W[N, K] -> (packed uint8[N, K/4], gamma float32[1])."""
+    lib = load()
+    _need_cuda(w, "w", torch.float32)
+    n, k = w.shape
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    wsb = int(lib.bitlinear_pack_workspace_bytes(n, k))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=w.device)
+    _check(lib.bitlinear_pack_weights(_ptr(w), n, k, _ptr(packed), _ptr(gamma), _ptr(ws), wsb,
+                                      _stream(w.device)))
+    return packed, gamma
+
+
+def quant_act(x, with_rowsum=True):
+    """Step A1 on the GPU: x[T, K] (float32 or bfloat16) -> (xq int8, absmax f32[T], rowsum i32[T] or None)."""
+    lib = load()
+    _need_cuda(x, "x")
+    if x.dtype == torch.float32:
+        dt = BL_F32
+    elif x.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    t, k = x.shape
+    xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
+    absmax = torch.empty(t, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(t, dtype=torch.int32, device=x.device) if with_rowsum else None
+    _check(lib.bitlinear_quant_act(_ptr(x), dt, t, k, _ptr(xq), _ptr(absmax), _ptr(rowsum),
+                                   _stream(x.device)))
+    return xq, absmax, rowsum
+
+
+def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None, acc_out=None):
+    """Steps A2 + A3 on the GPU: -> y float32[T, N] (and acc int32[T, N] if want_acc)."""
+    lib = load()
+    _need_cuda(packed, "packed", torch.uint8)
+    _need_cuda(gamma, "gamma", torch.float32)
+    _need_cuda(xq, "xq", torch.int8)
+    _need_cuda(absmax, "absmax", torch.float32)
+    t, k = xq.shape
+    y = out if out is not None else torch.empty((t, n), dtype=torch.float32, device=xq.device)
+    acc = acc_out
+    if want_acc and acc is None:
+        acc = torch.empty((t, n), dtype=torch.int32, device=xq.device)
+    _check(lib.bitlinear_forward_algo(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
+                                      _ptr(y), _ptr(acc), ALGOS[algo], _stream(xq.device)))
+    return (y, acc) if want_acc else y
+
+
+def bitlinear(x, packed, gamma, n, algo="auto"):
+    """Quantise x and run the forward: y = BitLinear(x) with pre-packed weights."""
+    xq, absmax, _ = quant_act(x, with_rowsum=False)
+    return forward(packed, gamma, xq, absmax, n, algo=algo)

@@ -1,0 +1,121 @@
+// C ABI of libbitlinear (declared in include/bitlinear.h): argument checks on
+// the host, then kernel launches on the caller's stream.
+#include <stdio.h>
+#include <stdarg.h>
+#include <string>
+
+#include "bitlinear.h"
+#include "bl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// T at or below which BL_ALGO_AUTO picks the decode kernel.
+constexpr int64_t kGemvMaxTokens = 64;
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int64_t kMaxN = int64_t(1) << 26;
+constexpr int64_t kMaxNK = int64_t(1) << 38;  // keeps every gamma bucket below 2^62
+constexpr int64_t kMaxTN = int64_t(1) << 36;  // y up to 256 GiB
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_k(const char* fn, int64_t k) {
+  if (k < 16 || k > BITLINEAR_MAX_K || k % 16 != 0)
+    return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 16 in [16, %d]", fn,
+                (long long)k, BITLINEAR_MAX_K);
+  return BL_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(BL_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  g_last_error.clear();
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+int64_t bitlinear_gemv_max_tokens(void) { return kGemvMaxTokens; }
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return bl::kPackWorkspaceBytes;
+}
+
+int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "bitlinear_pack_weights";
+  if (!w || !packed || !gamma || !workspace) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (int rc = check_k(fn, K)) return rc;
+  if (N < 1 || N > kMaxN || N * K > kMaxNK)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 8))
+    return fail(BL_ERR_ALIGN, "%s: w and packed need 16-byte, gamma 4-byte, workspace 8-byte alignment", fn);
+  if (workspace_bytes < bl::kPackWorkspaceBytes)
+    return fail(BL_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                bl::kPackWorkspaceBytes);
+  return launched(fn, bl::launch_pack(w, N, K, packed, gamma,
+                                      static_cast<unsigned long long*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
+                        float* absmax, int32_t* rowsum, void* stream) {
+  const char* fn = "bitlinear_quant_act";
+  if (!x || !xq || !absmax) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (x_dtype != BL_F32 && x_dtype != BL_BF16)
+    return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (int rc = check_k(fn, K)) return rc;
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(absmax, 4) || (rowsum && !aligned(rowsum, 4)))
+    return fail(BL_ERR_ALIGN, "%s: x and xq need 16-byte, absmax and rowsum 4-byte alignment", fn);
+  return launched(fn, bl::launch_quant(x, x_dtype == BL_BF16, T, K, xq, absmax, rowsum,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                           const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                           int32_t* acc, int algo, void* stream) {
+  const char* fn = "bitlinear_forward";
+  if (!packed || !gamma || !xq || !absmax || !y)
+    return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (int rc = check_k(fn, K)) return rc;
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  if (N < 1 || N > kMaxN || T * N > kMaxTN)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      !aligned(y, 4) || (acc && !aligned(acc, 4)))
+    return fail(BL_ERR_ALIGN, "%s: packed and xq need 16-byte, the others 4-byte alignment", fn);
+  if (algo == BL_ALGO_AUTO) algo = T <= kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (algo == BL_ALGO_GEMV)
+    return launched(fn, bl::launch_gemv(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+  if (algo == BL_ALGO_GEMM)
+    return launched(fn, bl::launch_gemm(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+  return fail(BL_ERR_ARG, "%s: unknown algo %d", fn, algo);
+}
+
+int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                      const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                      int32_t* acc, void* stream) {
+  return bitlinear_forward_algo(packed, gamma, xq, absmax, T, N, K, y, acc, BL_ALGO_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal declarations shared by the HIP translation units of libbitlinear.
+// Nothing here is part of the public C ABI (include/bitlinear.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Constants of the forward.  eps is added to gamma before the weight division
+// and floors a token's absmax; activations are clipped to [-127, 127].
+constexpr float kEps = 1e-5f;
+constexpr float kQb = 127.0f;
+
+// Exponent buckets of the exact gamma sum: one uint64 per binary32 exponent.
+constexpr int kGammaBuckets = 256;
+constexpr size_t kPackWorkspaceBytes = kGammaBuckets * sizeof(unsigned long long);
+
+hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                       unsigned long long* buckets, hipStream_t stream);
+
+hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
+                        float* absmax, int32_t* rowsum, hipStream_t stream);
+
+// Decode kernel: handles any T by taking tokens 64 at a time.
+hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                       int32_t* acc, hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                       int32_t* acc, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Codes of weights k = 16g+4j .. 16g+4j+3 of a packed word, one per byte.
+__device__ __forceinline__ uint32_t codes_of(uint32_t word, int j) {
+  return (word >> (2 * j)) & 0x03030303u;
+}
+
+// Binary32 scale applied to a token's exact int32 sum: gamma * m / 127.
+__device__ __forceinline__ float out_scale(float gamma, float absmax) {
+  const float m = fmaxf(absmax, kEps);
+  return (gamma * m) / kQb;
+}
+
+}  // namespace bl

@@ -1,0 +1,168 @@
+/*
+ * bitlinear.h -- C ABI of the BitLinear (W1.58A8) forward on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * BitLinear replaces a bias-free torch.nn.Linear ("BitNet b1.58 2B4T
+ * Technical Report", section 2, architecture; same section of the English
+ * summary "BitNet b1.58 2B4T Technical Report | Summary").  Its forward has
+ * four steps, and this library runs each of them in hand-written HIP kernels:
+ *
+ *   A0  absmean ternarisation of the latent weights to {-1, 0, +1} with one
+ *       scale gamma per matrix, stored at 2 bits per weight
+ *       ("BitNet解读", weight quantisation function, eq. (1)-(3);
+ *        2B4T report section 5.1: four ternary values per 8-bit integer);
+ *   A1  per-token absmax quantisation of the activations to int8
+ *       ("BitNet解读", activation quantisation; 2B4T report section 2);
+ *   A2  the ternary x int8 contraction into exact int32 sums
+ *       ("BitNet解读", computational efficiency: +1 adds, -1 subtracts,
+ *        0 skips);
+ *   A3  the rescale of each sum by gamma times the activation scale
+ *       (bitnet.cpp post on gitcode.csdn.net, section 1.1: a scale factor
+ *        restores the range of the ternary weights).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensor pointers are DEVICE pointers into row-major buffers that the
+ *   caller allocates and owns; outputs are written in place.  The library
+ *   keeps no state between calls and never allocates device memory.
+ * - `stream` is a hipStream_t passed as void*; NULL selects the null stream.
+ *   Every call only enqueues work on `stream`: it never synchronises the host.
+ * - Arguments are validated on the host before any HIP call.  A failed check
+ *   returns its bl_status code and records a message that
+ *   bitlinear_last_error() returns (per thread).  A failed launch returns
+ *   BL_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *   synchronisation.  No C++ exception crosses this interface.
+ * - Inputs must be finite; this is not checked on the device.
+ * - Calls are thread-safe; calls on different streams may run concurrently.
+ *
+ * Numerical contract (the plain reading of the pages, fixed here):
+ * - eps = 1e-5f is added to gamma before the weight division (eq. (1)) and
+ *   floors a token's absmax before the activation division; Qb = 127.
+ * - Every round-to-integer rounds half to even; the weight division, the
+ *   activation scale 127/m and the product x * (127/m) are single IEEE
+ *   binary32 operations.
+ * - gamma is the exact sum of |W| rounded once to binary64, divided by N*K in
+ *   binary64 and rounded to binary32, so it does not depend on any order.
+ * - y = acc * gamma * max(absmax, eps) / 127, computed in binary32 (within
+ *   1e-5 relative of the binary64 value; y is +0 exactly where acc is 0).
+ *
+ * Packed weight layout (the pages fix only "four weights per byte"):
+ *   code c = t + 1 in {0, 1, 2} (3 never occurs).  Row n of the N x K matrix
+ *   occupies K/4 bytes at byte offset n*K/4.  The 16 weights
+ *   k = 16g + 4j + i (j, i in 0..3) of group g form one little-endian 32-bit
+ *   word at row byte offset 4g, weight k in bits [8i + 2j, 8i + 2j + 2).
+ *   Hence (word >> 2j) & 0x03030303 holds the codes of k = 16g+4j .. 16g+4j+3
+ *   in its four bytes, in order.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+/* Largest K accepted: keeps every |acc| <= 127*K below 2^24, so the int32
+ * sum converts to binary32 exactly. */
+#define BITLINEAR_MAX_K 131072
+
+typedef enum {
+  BL_OK = 0,
+  BL_ERR_NULL = 1,      /* a required pointer is NULL */
+  BL_ERR_SHAPE = 2,     /* T, N or K out of range, or K % 16 != 0 */
+  BL_ERR_ALIGN = 3,     /* a pointer lacks the alignment stated below */
+  BL_ERR_DTYPE = 4,     /* unknown activation dtype */
+  BL_ERR_WORKSPACE = 5, /* workspace smaller than bitlinear_pack_workspace_bytes */
+  BL_ERR_HIP = 6,       /* a HIP launch failed; the message names the error */
+  BL_ERR_ARG = 7        /* another invalid argument (e.g. unknown algorithm) */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+
+typedef enum {
+  BL_ALGO_AUTO = 0, /* decode kernel for T <= bitlinear_gemv_max_tokens(), else GEMM */
+  BL_ALGO_GEMV = 1, /* streaming decode kernel, any T (tokens taken 64 at a time) */
+  BL_ALGO_GEMM = 2  /* LDS-tiled int8 MFMA kernel, any T */
+} bl_algo;
+
+/* Version of this interface (BITLINEAR_ABI_VERSION). */
+int bitlinear_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* bitlinear_last_error(void);
+
+/* Largest T that BL_ALGO_AUTO sends to the decode (GEMV) kernel. */
+int64_t bitlinear_gemv_max_tokens(void);
+
+/* Bytes of device workspace that bitlinear_pack_weights needs for an N x K
+ * matrix (a small constant: the exact-sum buckets of gamma). */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/* Step A0: absmean ternarisation and 2-bit packing of one weight matrix.
+ * Follows "BitNet解读", weight quantisation function: gamma = mean |W| over
+ * all N*K entries (eq. (3)), t = RoundClip(W / (gamma + eps), -1, 1)
+ * (eq. (1), (2)); packing follows the 2B4T report, section 5.1 (four ternary
+ * values per 8-bit integer), in the layout stated at the top of this file.
+ *
+ *   w         [N, K] float32 latent weights, row-major, 16-byte aligned.
+ *   N, K      1 <= N <= 2^26, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
+ *   packed    [N, K/4] uint8 output, 16-byte aligned.
+ *   gamma     [1] float32 output (device), 4-byte aligned.
+ *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K)
+ *             bytes, 8-byte aligned; its contents are overwritten.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
+int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                           float* gamma, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Step A1: per-token absmax quantisation of activations to int8.
+ * Follows "BitNet解读", activation quantisation (each token scaled into
+ * [-Qb, Qb], no zero point) and the 2B4T report, section 2 (8-bit, absmax per
+ * token).  Per row t: a = max_k |x[t,k]|, s = 127 / max(a, eps),
+ * xq = clamp(round_half_even(x * s), -127, 127).
+ *
+ *   x        [T, K] activations of dtype x_dtype (BL_F32 or BL_BF16),
+ *            row-major, 16-byte aligned.
+ *   T, K     1 <= T <= 2^24, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
+ *   xq       [T, K] int8 output, 16-byte aligned.
+ *   absmax   [T] float32 output: a itself (not floored), 4-byte aligned.
+ *   rowsum   [T] int32 output sum_k xq[t,k], or NULL to skip it.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_HIP. */
+int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
+                        float* absmax, int32_t* rowsum, void* stream);
+
+/* Steps A2 and A3: y[t, n] = (sum_k t[n,k] * xq[t,k]) * gamma * max(absmax[t], eps) / 127.
+ * The contraction follows "BitNet解读", computational efficiency (ternary
+ * weights turn products into add, subtract or skip) and is exact in int32;
+ * the rescale follows the bitnet.cpp post, section 1.1 (the scale factor).
+ * Dispatches on T (BL_ALGO_AUTO); see bitlinear_forward_algo.
+ *
+ *   packed   [N, K/4] uint8 from bitlinear_pack_weights, 16-byte aligned.
+ *   gamma    [1] float32 (device) from bitlinear_pack_weights.
+ *   xq       [T, K] int8 from bitlinear_quant_act, 16-byte aligned.
+ *   absmax   [T] float32 from bitlinear_quant_act.
+ *   T, N, K  1 <= T <= 2^24, 1 <= N <= 2^26, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
+ *   y        [T, N] float32 output, 4-byte aligned.
+ *   acc      [T, N] int32 output of the exact sums, or NULL to skip it.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                      const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                      int32_t* acc, void* stream);
+
+/* bitlinear_forward with an explicit kernel choice (a bl_algo value); the
+ * results are identical for every choice.  Errors as bitlinear_forward, plus
+ * BL_ERR_ARG for an unknown algo. */
+int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                           const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                           int32_t* acc, int algo, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/bitlinear.h declares, and rejects bad arguments with the documented
+status before making any HIP call (so these run on a CPU-only host).
+
+Every call below fails at least one host-side check; none reaches a launch.
+"""
+
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, BL_ERR_ARG = range(8)
+
+# fake device addresses: never dereferenced, every call using them fails a check
+A16 = 0x7F0000000000
+A_ODD = 0x7F0000000001
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib(built_lib):
+    from bitlinear_w1_a8_amd import binding
+    return binding.load()
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert len(names) == 8
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_header():
+    from bitlinear_w1_a8_amd import binding
+    assert sorted(binding.SIGNATURES) == header_functions()
+
+
+def test_constants(lib):
+    assert lib.bitlinear_abi_version() == 1
+    assert lib.bitlinear_gemv_max_tokens() == 64
+    assert lib.bitlinear_pack_workspace_bytes(2560, 2560) == 2048
+    assert lib.bitlinear_pack_workspace_bytes(28672, 8192) == 2048
+
+
+def _err(lib):
+    return lib.bitlinear_last_error().decode()
+
+
+def test_pack_errors(lib):
+    f = lib.bitlinear_pack_weights
+    assert f(None, 16, 64, A16, A16, A16, 4096, None) == BL_ERR_NULL
+    assert "NULL" in _err(lib)
+    assert f(A16, 16, 40, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert "K=40" in _err(lib)
+    assert f(A16, 16, 0, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A16, 16, 131072 + 16, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A16, 0, 64, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A16, (1 << 26) + 1, 64, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A_ODD, 16, 64, A16, A16, A16, 4096, None) == BL_ERR_ALIGN
+    assert f(A16, 16, 64, A16 + 8, A16, A16, 4096, None) == BL_ERR_ALIGN
+    assert f(A16, 16, 64, A16, A16, A16 + 4, 4096, None) == BL_ERR_ALIGN
+    assert f(A16, 16, 64, A16, A16, A16, 2047, None) == BL_ERR_WORKSPACE
+    assert "2048" in _err(lib)
+
+
+def test_quant_errors(lib):
+    f = lib.bitlinear_quant_act
+    assert f(A16, 1, 4, 64, None, A16, None, None) == BL_ERR_NULL
+    assert f(A16, 1, 4, 64, A16, None, None, None) == BL_ERR_NULL
+    assert f(A16, 2, 4, 64, A16, A16, None, None) == BL_ERR_DTYPE
+    assert f(A16, -1, 4, 64, A16, A16, None, None) == BL_ERR_DTYPE
+    assert f(A16, 1, 4, 63, A16, A16, None, None) == BL_ERR_SHAPE
+    assert f(A16, 1, 0, 64, A16, A16, None, None) == BL_ERR_SHAPE
+    assert f(A16, 1, (1 << 24) + 1, 64, A16, A16, None, None) == BL_ERR_SHAPE
+    assert f(A16 + 8, 1, 4, 64, A16, A16, None, None) == BL_ERR_ALIGN
+    assert f(A16, 1, 4, 64, A16 + 1, A16, None, None) == BL_ERR_ALIGN
+    assert f(A16, 1, 4, 64, A16, A16 + 2, None, None) == BL_ERR_ALIGN
+    assert f(A16, 1, 4, 64, A16, A16, A16 + 2, None) == BL_ERR_ALIGN
+
+
+def test_forward_errors(lib):
+    f = lib.bitlinear_forward_algo
+    good = (A16, A16, A16, A16)
+    assert f(None, A16, A16, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_NULL
+    assert f(*good, 1, 16, 64, None, None, 0, None) == BL_ERR_NULL
+    assert f(*good, 1, 16, 48 + 1, A16, None, 0, None) == BL_ERR_SHAPE
+    assert f(*good, 0, 16, 64, A16, None, 0, None) == BL_ERR_SHAPE
+    assert f(*good, 1, 0, 64, A16, None, 0, None) == BL_ERR_SHAPE
+    assert f(*good, 1 << 20, 1 << 20, 64, A16, None, 0, None) == BL_ERR_SHAPE
+    assert f(A16 + 4, A16, A16, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
+    assert f(A16, A16, A16 + 8, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
+    assert f(*good, 1, 16, 64, A16 + 2, None, 0, None) == BL_ERR_ALIGN
+    assert f(*good, 1, 16, 64, A16, A16 + 1, 0, None) == BL_ERR_ALIGN
+    assert f(*good, 1, 16, 64, A16, None, 3, None) == BL_ERR_ARG
+    assert f(*good, 1, 16, 64, A16, None, -1, None) == BL_ERR_ARG
+    assert lib.bitlinear_forward(None, A16, A16, A16, 1, 16, 64, A16, None, None) == BL_ERR_NULL
+
+
+def test_last_error_is_per_thread(lib):
+    assert lib.bitlinear_quant_act(None, 1, 4, 64, A16, A16, None, None) == BL_ERR_NULL
+    seen = {}
+
+    def other():
+        seen["before"] = _err(lib)
+        lib.bitlinear_quant_act(A16, 7, 4, 64, A16, A16, None, None)
+        seen["after"] = _err(lib)
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["before"] == ""
+    assert "x_dtype 7" in seen["after"]
+    assert "NULL" in _err(lib)
+
+
+def test_binding_raises(built_lib):
+    from bitlinear_w1_a8_amd import binding
+    with pytest.raises(binding.BitLinearError) as ei:
+        binding._check(BL_ERR_SHAPE)
+    assert ei.value.status == BL_ERR_SHAPE

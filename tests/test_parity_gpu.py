@@ -1,0 +1,293 @@
+"""Parity of the HIP path with the CPU oracle (needs an MI355X).
+
+Every test feeds the same seeded inputs to both sides and compares element
+by element: packed bytes, gamma bits, int8 activations, absmax bits, row sums
+and int32 sums must be equal; float32 outputs must be within 1e-5 relative of
+the oracle's binary64 values, and exactly +0 wherever the sum is 0.  Test ids
+name the shapes, so a failing or faulting case is named by `pytest -v`.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bitlinear_w1_a8_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+Y_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def bl(built_lib):
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from bitlinear_w1_a8_amd import binding
+    binding.load()
+    return binding
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ checks
+
+def check_pack(bl, w):
+    packed_ref, gamma_ref = oracle.pack_weights(w)
+    packed, gamma = bl.pack_weights(dev(w))
+    g = host(gamma)
+    assert g.view(np.uint32)[0] == np.float32(gamma_ref).view(np.uint32), (g[0], gamma_ref)
+    p = host(packed)
+    bad = int(np.count_nonzero(p != packed_ref))
+    assert bad == 0, f"{bad} of {p.size} packed bytes differ"
+    return packed, gamma, packed_ref, gamma_ref
+
+
+def check_quant(bl, x, dtype):
+    if dtype == "bf16":
+        bits = wl.bf16_bits(x)
+        q_ref, a_ref, rs_ref = oracle.quant_act(bits)
+        xin = dev_bf16(bits)
+    else:
+        q_ref, a_ref, rs_ref = oracle.quant_act(x)
+        xin = dev(x)
+    xq, absmax, rowsum = bl.quant_act(xin)
+    q = host(xq)
+    bad = int(np.count_nonzero(q != q_ref))
+    assert bad == 0, f"{bad} of {q.size} int8 activations differ"
+    assert np.array_equal(host(absmax).view(np.uint32), a_ref.view(np.uint32))
+    assert np.array_equal(host(rowsum), rs_ref)
+    return xq, absmax, q_ref, a_ref
+
+
+def check_y(y, acc_ref, gamma, absmax_ref):
+    y_ref = oracle.rescale(acc_ref, gamma, absmax_ref)
+    zero = acc_ref == 0
+    assert np.all(y[zero] == 0.0) and not np.any(np.signbit(y[zero]))
+    nz = ~zero
+    if np.any(nz):
+        rel = np.abs(y[nz].astype(np.float64) - y_ref[nz]) / np.abs(y_ref[nz])
+        assert float(rel.max()) <= Y_RTOL, f"max relative error {rel.max():.3g}"
+
+
+def check_forward(bl, packed_dev, gamma_dev, xq_dev, absmax_dev, t_ref, q_ref, gamma_ref,
+                  absmax_ref, algo):
+    n = t_ref.shape[0]
+    y, acc = bl.forward(packed_dev, gamma_dev, xq_dev, absmax_dev, n, algo=algo, want_acc=True)
+    acc_ref = oracle.contract(q_ref, t_ref)
+    a = host(acc)
+    bad = int(np.count_nonzero(a != acc_ref))
+    assert bad == 0, f"{bad} of {a.size} int32 sums differ ({algo})"
+    check_y(host(y), acc_ref, gamma_ref, absmax_ref)
+    return a
+
+
+# ------------------------------------------------------------------ step A0
+
+PACK_SHAPES = [(1, 16), (2, 32), (3, 48), (16, 64), (17, 272), (33, 96), (512, 256),
+               (640, 2560), (2560, 2560), (6912, 2560), (2560, 6912)]
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES, ids=[f"N{n}_K{k}" for n, k in PACK_SHAPES])
+def test_pack_random(bl, n, k):
+    check_pack(bl, wl.latent_weights(n, k, 0.02, 7000 + n + k))
+
+
+def _tie_matrix():
+    """Weights with W/(gamma+eps) exactly +-0.5 (round to 0) and +-0.5 ulp
+    around it, at a fixed point of gamma."""
+    base = np.full((16, 64), 0.5, np.float32)
+    d = np.float32(0.5)
+    for _ in range(6):
+        w = base.copy()
+        half = np.float32(0.5) * d
+        w[0, :8] = [half, -half, np.nextafter(half, np.float32(1)), -np.nextafter(half, np.float32(1)),
+                    np.nextafter(half, np.float32(0)), half, half, -half]
+        w[1, :4] = [np.float32(1.5) * d, np.float32(-1.5) * d, np.float32(2.5) * d, 0.0]
+        g = oracle.absmean_gamma(w)
+        d_new = np.float32(g) + np.float32(1e-5)
+        if d_new == d:
+            break
+        d = d_new
+    u = w[0, :2] / (np.float32(oracle.absmean_gamma(w)) + np.float32(1e-5))
+    assert np.all(np.abs(u) == 0.5)
+    return w
+
+
+def _awkward_matrix():
+    rng = np.random.default_rng(77)
+    mant = rng.random((64, 96)) + 0.5
+    expo = rng.integers(-140, 60, size=(64, 96))
+    w = (mant * np.exp2(expo.astype(np.float64))).astype(np.float32)
+    w *= np.where(rng.random((64, 96)) < 0.5, -1, 1).astype(np.float32)
+    w[rng.random((64, 96)) < 0.1] = 0.0
+    return w
+
+
+SPECIAL = {
+    "all_zero": lambda: np.zeros((32, 64), np.float32),
+    "constant": lambda: np.full((8, 128), np.float32(-0.0123), np.float32),
+    "ties": _tie_matrix,
+    "awkward_exponents": _awkward_matrix,
+    "one_row_zero": lambda: np.where(np.arange(64)[:, None] == 5, 0.0,
+                                     wl.latent_weights(64, 256, 0.02, 5)).astype(np.float32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPECIAL))
+def test_pack_special(bl, name):
+    _, _, packed_ref, _ = check_pack(bl, SPECIAL[name]())
+    if name == "all_zero":
+        assert np.all(packed_ref == 0x55)
+
+
+# ------------------------------------------------------------------ step A1
+
+QUANT_SHAPES = [(1, 16), (4, 256), (7, 48), (3, 2560), (2, 6912), (1, 28672), (65, 8192),
+                (300, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("t,k", QUANT_SHAPES, ids=[f"T{t}_K{k}" for t, k in QUANT_SHAPES])
+def test_quant_random(bl, t, k, dtype):
+    x = wl.activations_student_t(t, k, 4, 9000 + t + k)
+    check_quant(bl, x, dtype)
+
+
+def test_quant_wide_f32(bl):
+    # more 16-byte vectors than one pass holds in registers: re-read path
+    x = wl.activations_normal(2, 65536, 31, 0.01, 8.0)
+    check_quant(bl, x, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_special_rows(bl, dtype):
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((8, 256)).astype(np.float32)
+    x[0] = 0.0                                            # all-zero token
+    x[1, :8] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -126.5, 126.5]  # exact ties
+    x[1, 8:] = 0.25
+    x[2] *= np.float32(1e-30)                             # tiny values
+    x[3] *= np.float32(1e30)                              # huge values
+    x[4, :] = np.float32(-3.0)                            # constant negative row
+    x[5, :] = np.float32(1e-39)                           # subnormal row
+    x[6, 3] = np.float32(1e4)                             # one outlier
+    check_quant(bl, x, dtype)
+
+
+# ------------------------------------------------------------------ steps A2 + A3
+
+FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (16, 33, 320),
+              (17, 100, 256), (33, 64, 128), (64, 200, 1024), (65, 130, 192), (130, 257, 272),
+              (1, 2560, 2560), (8, 640, 2560), (1, 100, 6912), (5, 37, 28672)]
+
+
+def _forward_inputs(t, n, k, seed, zero_rows=True):
+    rng = np.random.default_rng(seed)
+    tern = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    if zero_rows and n > 2:
+        tern[n // 2] = 0
+    x = wl.activations_student_t(t, k, 4, seed + 1)
+    if t > 2:
+        x[t // 2] = 0.0
+    q, absmax, _ = oracle.quant_act(x)
+    gamma = np.float32(0.0173)
+    return tern, q, absmax, gamma
+
+
+@pytest.mark.parametrize("algo", ["gemv", "gemm"])
+@pytest.mark.parametrize("t,n,k", FWD_SHAPES, ids=[f"T{t}_N{n}_K{k}" for t, n, k in FWD_SHAPES])
+def test_forward_shapes(bl, t, n, k, algo):
+    tern, q, absmax, gamma = _forward_inputs(t, n, k, 100 * t + n + k)
+    check_forward(bl, dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q), dev(absmax),
+                  tern, q, gamma, absmax, algo)
+
+
+def test_forward_extremes(bl):
+    """All q = +-127 against all-ones rows: the largest sums the contraction makes."""
+    t, n, k = 3, 48, 4096
+    tern = np.ones((n, k), np.int8)
+    tern[1::2] = -1
+    tern[5] = 0
+    q = np.full((t, k), 127, np.int8)
+    q[1] = -127
+    q[2, ::2] = -127
+    absmax = np.array([5.0, 0.25, 1e-7], np.float32)
+    gamma = np.float32(3.0)
+    for algo in ("gemv", "gemm"):
+        a = check_forward(bl, dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q),
+                          dev(absmax), tern, q, gamma, absmax, algo)
+        assert a[0, 0] == 127 * k
+
+
+def test_forward_deterministic_and_kernels_agree(bl):
+    t, n, k = 32, 1000, 2560
+    tern, q, absmax, gamma = _forward_inputs(t, n, k, 55)
+    args = (dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q), dev(absmax), n)
+    runs = [bl.forward(*args, algo=a, want_acc=True) for a in ("gemv", "gemv", "gemm", "gemm")]
+    ys = [host(y) for y, _ in runs]
+    accs = [host(a) for _, a in runs]
+    for i in range(1, 4):
+        assert np.array_equal(accs[i], accs[0])
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+    assert np.array_equal(ys[2].view(np.uint32), ys[3].view(np.uint32))
+
+
+def test_forward_on_side_stream(bl):
+    t, n, k = 4, 300, 512
+    tern, q, absmax, gamma = _forward_inputs(t, n, k, 66)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        args = (dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q), dev(absmax))
+        y, acc = bl.forward(*args, n, want_acc=True)
+    s.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), oracle.contract(q, tern))
+
+
+def test_bitlinear_end_to_end(bl):
+    w = wl.latent_weights(96, 320, 0.02, 3)
+    x = wl.activations_normal(5, 320, 4)
+    packed, gamma = bl.pack_weights(dev(w))
+    y = host(bl.bitlinear(dev(x), packed, gamma, 96))
+    y_ref, acc_ref, _, gamma_ref = oracle.forward(w, x)
+    _, a_ref, _ = oracle.quant_act(x)
+    check_y(y, acc_ref, gamma_ref, a_ref)
+
+
+# ------------------------------------------------------------------ the five workloads, full size
+
+def _workload_cases():
+    cases = []
+    for idx, w in sorted(wl.WORKLOADS.items()):
+        for mi, m in enumerate(w.matrices):
+            cases.append(pytest.param(idx, mi, id=f"w{idx}_{w.name}_{m.name}_K{m.k}_N{m.n}"))
+    return cases
+
+
+@pytest.mark.parametrize("widx,mi", _workload_cases())
+def test_workload_full_size(bl, widx, mi):
+    w = wl.WORKLOADS[widx]
+    m = w.matrices[mi]
+    weights = w.weights(mi)
+    packed, gamma, packed_ref, gamma_ref = check_pack(bl, weights)
+    tern = oracle.ternarize(weights, gamma_ref)
+    del weights
+    for t in w.tokens:
+        x = w.activations(mi, t)
+        xq, absmax, q_ref, a_ref = check_quant(bl, x, w.x_dtype)
+        algos = ["auto"] + (["gemv", "gemm"] if widx == 3 else [])
+        for algo in algos:
+            check_forward(bl, packed, gamma, xq, absmax, tern, q_ref, gamma_ref, a_ref, algo)
+    if widx in (2, 5):
+        # the ternary zero fraction of Gaussian weights, about 31%
+        assert abs(float(np.mean(tern == 0)) - 0.3101) < 0.005
