@@ -1,0 +1,353 @@
+"""Throughput of the BitLinear (W1.58A8) forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the per-token hot path over one 2B-class decoder layer
+at T = 1: for each of its seven projections (q, k, v, o: 2560->2560/640;
+gate, up: 2560->6912; down: 6912->2560) the bf16 activation is quantised to
+int8 (act-quant kernel) and contracted with the 2-bit packed ternary weights
+(decode GEMV kernel, rescale fused).  Weights are packed once at set-up
+(step A0 is an offline conversion) and then copied to L distinct layer sets
+(> 1 GB in total, four times the 256 MB MALL), and consecutive steps rotate
+through them, so every step streams its weights from HBM.  The timed steps
+replay a HIP graph of L consecutive steps.
+
+The JSON line reports algorithmic GB/s of the whole step (value), the decode
+GEMV kernel against the HBM roofline, the CPU oracle timed on a bounded
+sample, and, as extra context, the prefill GEMM (T = 2048) in int8 TOP/s.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOP/s
+ROT_BYTES = 1.1e9               # packed weights rotated through per pass
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--warmup", type=int, default=256)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extra", action="store_true", help="skip the prefill GEMM context run")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="counter runs: two eager passes over the layer sets plus the copy "
+                        "calibration, no timing and no JSON")
+    return p.parse_args()
+
+
+def gemv_bytes(t, n, k):
+    """Algorithmic bytes of one forward launch: packed W, int8 x, absmax, gamma, fp32 y."""
+    return n * k // 4 + t * k + 4 * t + 4 + 4 * t * n
+
+
+def quant_bytes(t, k, in_bytes=2):
+    """Algorithmic bytes of one act-quant launch: x in, int8 x, absmax, rowsum out."""
+    return in_bytes * t * k + t * k + 8 * t
+
+
+def kernel_src_hash(name):
+    path = os.path.join(ROOT, "bitlinear_w1_a8_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(kernel_file, key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only
+    while the kernel source still hashes to what was profiled."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_src_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Calls:
+    """Direct C-ABI calls with pre-built pointer arguments (no per-call torch work)."""
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    def quant(self, x, xq, absmax, t, k, stream):
+        rc = self.lib.bitlinear_quant_act(x, 1, t, k, xq, absmax, None, stream)
+        if rc:
+            raise RuntimeError(self.lib.bitlinear_last_error().decode())
+
+    def forward(self, packed, gamma, xq, absmax, t, n, k, y, algo, stream):
+        rc = self.lib.bitlinear_forward_algo(packed, gamma, xq, absmax, t, n, k, y, None, algo,
+                                             stream)
+        if rc:
+            raise RuntimeError(self.lib.bitlinear_last_error().decode())
+
+
+def ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def decode_setup(torch, binding, wl, dev):
+    """Seeded weights and activations of the 2B decode layer, packed on the GPU."""
+    wk = wl.WORKLOADS[2]
+    mats = []
+    pack_ms = []
+    for mi, m in enumerate(wk.matrices):
+        w = torch.from_numpy(wk.weights(mi)).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        packed, gamma = binding.pack_weights(w)
+        torch.cuda.synchronize()
+        pack_ms.append((time.perf_counter() - t0) * 1e3)
+        del w
+        bits = wl.bf16_bits(wk.activations(mi, 1))
+        x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        mats.append(dict(m=m, packed=packed, gamma=gamma, x=x,
+                         xq=torch.empty((1, m.k), dtype=torch.int8, device=dev),
+                         absmax=torch.empty(1, dtype=torch.float32, device=dev),
+                         y=torch.empty((1, m.n), dtype=torch.float32, device=dev)))
+    layer_bytes = sum(d["packed"].numel() for d in mats)
+    n_sets = int(np.ceil(ROT_BYTES / layer_bytes))
+    sets = [[d["packed"] for d in mats]]
+    for _ in range(n_sets - 1):
+        sets.append([d["packed"].clone() for d in mats])
+    torch.cuda.synchronize()
+    return mats, sets, pack_ms
+
+
+def capture(torch, fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn(stream)  # one eager pass before capture
+    stream.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        fn(stream)
+    return g
+
+
+def time_graph(torch, g, reps, warm, stream):
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)  # ms
+
+
+def cpu_baseline(oracle, wl, budget_s=12.0):
+    """The oracle as it stands (quant_act, contract, rescale) on the same
+    decode layer at T = 1; the sample is as many whole layers as fit the
+    budget, at least one."""
+    wk = wl.WORKLOADS[2]
+    tern, xs, gammas = [], [], []
+    for mi, m in enumerate(wk.matrices):
+        w = wk.weights(mi)
+        g = oracle.absmean_gamma(w)
+        tern.append(oracle.ternarize(w, g))
+        gammas.append(g)
+        xs.append(wl.bf16_bits(wk.activations(mi, 1)))
+    layers = 0
+    t0 = time.perf_counter()
+    while True:
+        for mi in range(len(wk.matrices)):
+            q, a, _ = oracle.quant_act(xs[mi])
+            acc = oracle.contract(q, tern[mi])
+            oracle.rescale(acc, gammas[mi], a)
+        layers += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or layers >= 200:
+            break
+    step_bytes = sum(gemv_bytes(1, m.n, m.k) + quant_bytes(1, m.k) for m in wk.matrices)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl absent: report the affinity set
+        cores = len(os.sched_getaffinity(0))
+    return {"value": step_bytes * layers / el / 1e9, "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{layers} decode layers (7 projections, T=1, act-quant + contract + "
+                      f"rescale) in {el:.1f} s; weights ternarised beforehand"}
+
+
+def prefill_extra(torch, binding, wl, dev, stream):
+    """Context: prefill GEMM (T = 2048) on both 2B shapes, TOP/s of the GEMM
+    kernel alone and of act-quant + GEMM."""
+    wk = wl.WORKLOADS[4]
+    lib = binding.load()
+    calls = Calls(lib)
+    out = {}
+    for mi, m in enumerate(wk.matrices):
+        t = 2048
+        packed, gamma = binding.pack_weights(torch.from_numpy(wk.weights(mi)).to(dev))
+        bits = wl.bf16_bits(wk.activations(mi, t))
+        x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        xq = torch.empty((t, m.k), dtype=torch.int8, device=dev)
+        absmax = torch.empty(t, dtype=torch.float32, device=dev)
+        y = torch.empty((t, m.n), dtype=torch.float32, device=dev)
+        P = [ptr(v) for v in (packed, gamma, xq, absmax, y, x)]
+
+        def gemm_only(s, P=P, m=m):
+            h = ctypes.c_void_p(s.cuda_stream)
+            calls.forward(P[0], P[1], P[2], P[3], t, m.n, m.k, P[4], 2, h)
+
+        def both(s, P=P, m=m):
+            h = ctypes.c_void_p(s.cuda_stream)
+            calls.quant(P[5], P[2], P[3], t, m.k, h)
+            calls.forward(P[0], P[1], P[2], P[3], t, m.n, m.k, P[4], 2, h)
+
+        reps = 50
+        g1 = capture(torch, gemm_only, stream)
+        ms1 = time_graph(torch, g1, reps, 5, stream) / reps
+        g2 = capture(torch, both, stream)
+        ms2 = time_graph(torch, g2, reps, 5, stream) / reps
+        ops = 2.0 * t * m.n * m.k
+        out[f"{m.k}->{m.n}"] = {
+            "gemm_us": round(ms1 * 1e3, 2), "gemm_tops": round(ops / ms1 / 1e9, 1),
+            "gemm_frac_of_int8_peak": round(ops / ms1 / 1e9 / INT8_PEAK_TOPS, 4),
+            "quant_plus_gemm_us": round(ms2 * 1e3, 2),
+            "quant_plus_gemm_tops": round(ops / ms2 / 1e9, 1)}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the forward's sharding is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bitlinear_w1_a8_amd import binding, workloads as wl
+
+    if not os.path.exists(binding.LIB_PATH):
+        from bitlinear_w1_a8_amd import build
+        build.build(verbose=False)
+    lib = binding.load()
+    calls = Calls(lib)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    mats, sets, pack_ms = decode_setup(torch, binding, wl, dev)
+    n_sets = len(sets)
+    mp = [dict(x=ptr(d["x"]), xq=ptr(d["xq"]), absmax=ptr(d["absmax"]), y=ptr(d["y"]),
+               gamma=ptr(d["gamma"]), n=d["m"].n, k=d["m"].k) for d in mats]
+    set_ptrs = [[ptr(p) for p in s] for s in sets]
+
+    def steps(s, with_quant=True, with_gemv=True):
+        h = ctypes.c_void_p(s.cuda_stream)
+        for sp in set_ptrs:                      # one step per layer set
+            for mi, d in enumerate(mp):
+                if with_quant:
+                    calls.quant(d["x"], d["xq"], d["absmax"], 1, d["k"], h)
+                if with_gemv:
+                    calls.forward(sp[mi], d["gamma"], d["xq"], d["absmax"], 1, d["n"], d["k"],
+                                  d["y"], 1, h)
+
+    if args.profile_pass:
+        for _ in range(2):
+            steps(stream)
+        stream.synchronize()
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print("profile pass done", flush=True)
+        return
+
+    step_bytes = sum(gemv_bytes(1, d["n"], d["k"]) + quant_bytes(1, d["k"]) for d in mp)
+    gemv_launch_bytes = sum(gemv_bytes(1, d["n"], d["k"]) for d in mp) / len(mp)
+
+    reps = max(1, args.steps // n_sets)
+    warm = max(1, args.warmup // n_sets)
+    k_steps = reps * n_sets
+
+    # timed region: whole steps (act-quant + GEMV for all seven projections)
+    g_all = capture(torch, lambda s: steps(s), stream)
+    ms = time_graph(torch, g_all, reps, warm, stream)
+    ms_per_step = ms / k_steps
+
+    # the dominant kernel alone: average duration of one decode-GEMV launch
+    g_gemv = capture(torch, lambda s: steps(s, with_quant=False), stream)
+    ms_g = time_graph(torch, g_gemv, reps, warm, stream)
+    gemv_us = ms_g * 1e3 / (k_steps * len(mp))
+    g_quant = capture(torch, lambda s: steps(s, with_gemv=False), stream)
+    ms_q = time_graph(torch, g_quant, reps, warm, stream)
+    quant_us = ms_q * 1e3 / (k_steps * len(mp))
+
+    # the same steps launched one by one on the stream, without a graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eager_reps = max(1, reps // 4)
+    for _ in range(eager_reps):
+        steps(stream)
+    stream.synchronize()
+    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / (eager_reps * n_sets)
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    achieved = gemv_launch_bytes / (gemv_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": committed_traffic("gemv.hip", "decode_gemv_2b_t1"),
+                "kernel": "k_gemv (decode GEMV, T=1)",
+                "avg_launch_us": round(gemv_us, 3),
+                "algorithmic_bytes_per_launch": int(gemv_launch_bytes)}
+
+    extra = {"eager_ms_per_step": round(eager_ms_per_step, 4),
+             "act_quant_avg_launch_us": round(quant_us, 3),
+             "layer_sets_rotated": n_sets,
+             "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
+             "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]}
+    if not args.no_extra:
+        extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        cpu = cpu_baseline(oracle, wl)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    rec = {"metric": "BitLinear decode GEMV HBM GB/s (% peak) + prefill GEMM int8 TOPS (% MFMA peak)",
+           "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": k_steps,
+           "warmup": warm * n_sets, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+           "data": "synthetic",
+           "config": {"workload": "decode_2b_t1_layer: T=1, bf16 x, 7 projections "
+                                  "(2560->2560, 2560->640 x2, 2560->2560, 2560->6912 x2, "
+                                  "6912->2560), act-quant + GEMV each, weights rotated cold",
+                      "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
+                      "step_bytes": int(step_bytes)},
+           "roofline": roofline, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
