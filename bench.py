@@ -235,8 +235,8 @@ def prefill_extra(torch, binding, wl, dev, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the forward's sharding is a design note, not code)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(sharding the forward across GPUs is a design note, not code)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -24,8 +24,8 @@ Sources (the pages this follows, by title and section):
 * bitnet.cpp post (gitcode.csdn.net), section 1.1: the ternary weights come
   with a scale factor that restores the value range.
 
-Readings taken where the pages are silent (each one is also listed, with its
-reason, in the design notes at the repository root):
+Readings taken where the pages are silent (no page prints these values, so
+they are pinned by the readings themselves, not by a printed number):
 
 * epsilon = 1e-5 in float32, added to gamma as eq. (1) prints it;
 * Qb = 127, symmetric clip to [-127, 127];
