@@ -28,9 +28,9 @@ namespace bl {
 namespace {
 
 constexpr int kGemvTokens = 64;   // tokens per launch (4 MFMA column tiles)
-constexpr int kMaxWaves = 8;
+constexpr int kGemvStage = 8;     // 16-byte activation vectors staged per thread
 
-template <int VEC, int RT, int NTT>
+template <int VEC, int RT, int NTT, int U>
 __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packed,
                                               const float* __restrict__ gamma,
                                               const int8_t* __restrict__ xq,
@@ -69,48 +69,58 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) qs[tt] = 0;
 
-  for (int c = wave; c < nchunks; c += nwaves) {
-    const int wi = c * 4 * VEC + qg * VEC;          // first packed word of this lane
-    const bool kvalid = wi < K16;                   // VEC divides K16 when VEC > 1
-    uint32_t wv[RT][VEC];
+  // Each pass: a wave takes U consecutive chunks and issues all their loads
+  // before the first MFMA, so U * 1 KiB per row tile is in flight per wave.
+  for (int c0 = wave * U; c0 < nchunks; c0 += nwaves * U) {
+    uint32_t wv[U][RT][VEC];
+    uint32_t xv[U][NTT][4 * VEC];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if constexpr (VEC == 4) {
-        const uint4 u =
-            kvalid ? *reinterpret_cast<const uint4*>(wrow[rt] + wi) : make_uint4(0, 0, 0, 0);
-        wv[rt][0] = u.x; wv[rt][1] = u.y; wv[rt][2] = u.z; wv[rt][3] = u.w;
-      } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) wv[rt][v] = kvalid ? wrow[rt][wi + v] : 0u;
-      }
-    }
-    uint32_t xv[NTT][4 * VEC];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-      const bool ok = kvalid && tvalid[tt];
-      const uint4* src = reinterpret_cast<const uint4*>(xrow[tt] + (int64_t)wi * 16);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const uint4 u = ok ? src[v] : make_uint4(0, 0, 0, 0);
-        xv[tt][4 * v + 0] = u.x; xv[tt][4 * v + 1] = u.y;
-        xv[tt][4 * v + 2] = u.z; xv[tt][4 * v + 3] = u.w;
-      }
-#pragma unroll
-      for (int d = 0; d < 4 * VEC; ++d)
-        qs[tt] = __builtin_amdgcn_sdot4((int)xv[tt][d], 0x01010101, qs[tt], false);
-    }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
+    for (int u = 0; u < U; ++u) {
+      const int wi = (c0 + u) * 4 * VEC + qg * VEC;   // first packed word of this lane
+      const bool kvalid = wi < K16;                   // VEC divides K16 when VEC > 1
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint32_t w = wv[rt][v];
-        const v4i a = {(int)codes_of(w, 0), (int)codes_of(w, 1), (int)codes_of(w, 2),
-                       (int)codes_of(w, 3)};
+        if constexpr (VEC == 4) {
+          const uint4 w4 =
+              kvalid ? *reinterpret_cast<const uint4*>(wrow[rt] + wi) : make_uint4(0, 0, 0, 0);
+          wv[u][rt][0] = w4.x; wv[u][rt][1] = w4.y; wv[u][rt][2] = w4.z; wv[u][rt][3] = w4.w;
+        } else {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          const v4i b = {(int)xv[tt][4 * v + 0], (int)xv[tt][4 * v + 1], (int)xv[tt][4 * v + 2],
-                         (int)xv[tt][4 * v + 3]};
-          acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rt][tt], 0, 0, 0);
+          for (int v = 0; v < VEC; ++v) wv[u][rt][v] = kvalid ? wrow[rt][wi + v] : 0u;
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        const bool ok = kvalid && tvalid[tt];
+        const uint4* src = reinterpret_cast<const uint4*>(xrow[tt] + (int64_t)wi * 16);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const uint4 x4 = ok ? src[v] : make_uint4(0, 0, 0, 0);
+          xv[u][tt][4 * v + 0] = x4.x; xv[u][tt][4 * v + 1] = x4.y;
+          xv[u][tt][4 * v + 2] = x4.z; xv[u][tt][4 * v + 3] = x4.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int d = 0; d < 4 * VEC; ++d)
+          qs[tt] = __builtin_amdgcn_sdot4((int)xv[u][tt][d], 0x01010101, qs[tt], false);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint32_t w = wv[u][rt][v];
+          const v4i a = {(int)codes_of(w, 0), (int)codes_of(w, 1), (int)codes_of(w, 2),
+                         (int)codes_of(w, 3)};
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) {
+            const v4i b = {(int)xv[u][tt][4 * v + 0], (int)xv[u][tt][4 * v + 1],
+                           (int)xv[u][tt][4 * v + 2], (int)xv[u][tt][4 * v + 3]};
+            acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rt][tt], 0, 0, 0);
+          }
         }
       }
     }
@@ -155,17 +165,193 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
   }
 }
 
-template <int VEC, int RT, int NTT>
+// Software-pipelined variant for T <= 16 and K % 256 == 0 (the decode case).
+//
+// Per chunk (256 k of a 16-row tile) a lane holds four packed words w_v.
+// Instead of shifting every 2-bit field down, three of the four fields are
+// only masked: w & 0x03030303, w & 0x0C0C0C0C and w & 0x30303030 hold c,
+// 4c and 16c in each byte (all still non-negative int8), and only the top
+// field needs a shift.  Slice j of the four words forms one MFMA operand, and
+// each scale accumulates separately; the exact sums are divided by 4 and 16
+// once at the end (they are exact multiples).  The activation bytes are laid
+// out in LDS so that the matching B operand of slice j is one 16-byte read:
+// within every 64-byte group the 4x4 dword matrix (word v, slice j) is
+// stored transposed.  The token's sum of q over K, which removes the code
+// offset (c = t + 1), is taken once while staging.
+//
+// Each wave walks its chunks with P loads in flight: the load of chunk i+P
+// is issued as soon as chunk i is consumed.
+template <int P>
+__global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__ packed,
+                                                    const float* __restrict__ gamma,
+                                                    const int8_t* __restrict__ xq,
+                                                    const float* __restrict__ absmax, int T,
+                                                    int N, int K, float* __restrict__ y,
+                                                    int32_t* __restrict__ acc_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qg = lane >> 4, r = lane & 15;
+  const int K16 = K >> 4;
+  const int nchunks = K16 >> 4;                     // 16 words (256 k) per chunk
+  const int n0 = blockIdx.x * 16;
+  // LDS: [256 B zeros][T x (K + 16) activation bytes, transposed per 64 B]
+  //      [T row sums][partials].  The 16-byte pad per token spreads the
+  //      tokens of one B-operand read over different banks.
+  const int xs = (K >> 2) + 4;                      // token stride in dwords
+  uint32_t* zero = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* xl = zero + 64;
+  int* rsum = reinterpret_cast<int*>(xl + T * xs);
+  int* red = rsum + 16;
+
+  int n = n0 + r;
+  n = n < N ? n : N - 1;
+  const uint4* wrow = reinterpret_cast<const uint4*>(packed + (int64_t)n * K16) + qg;
+  const int my = (nchunks - wave + nwaves - 1) / nwaves;   // chunks of this wave (>= 1)
+  auto chunk_of = [&](int i) { return wave + (i < my ? i : my - 1) * nwaves; };
+
+  // Issue order matters: vector loads retire in order, so anything waited on
+  // before the main loop (the activations) is issued before the weight
+  // prefetch, which then stays in flight through the staging and the barrier.
+  constexpr int kStage = kGemvStage;
+  const int per_tok = K >> 4, nvec = T * per_tok;
+  const uint4* src = reinterpret_cast<const uint4*>(xq);
+  uint4 sv[kStage];
+#pragma unroll
+  for (int m = 0; m < kStage; ++m) {
+    const int i = threadIdx.x + m * blockDim.x;
+    sv[m] = src[i < nvec ? i : nvec - 1];
+  }
+  // the epilogue's scalars, fetched early so their latency hides under the loop
+  const float g = gamma[0];
+  const float am = absmax[threadIdx.x < 16 * T ? (threadIdx.x >> 4) : 0];
+
+  uint4 buf[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) buf[j] = wrow[(size_t)chunk_of(j) * 4];
+
+  if (threadIdx.x < 64) zero[threadIdx.x] = 0u;
+  if (threadIdx.x < 16) rsum[threadIdx.x] = 0;
+  // Vector i (16 bytes) is word v = i & 3 of its 64-byte group; its dword
+  // (v, j) is stored at position (j, v) of the group.
+  auto stage_store = [&](int i, const uint4& v) {
+    const int t = i / per_tok, iv = i - t * per_tok;
+    uint32_t* gp = xl + t * xs + (iv >> 2) * 16 + (iv & 3);
+    gp[0] = v.x; gp[4] = v.y; gp[8] = v.z; gp[12] = v.w;
+  };
+#pragma unroll
+  for (int m = 0; m < kStage; ++m) {
+    const int i = threadIdx.x + m * blockDim.x;
+    if (i < nvec) stage_store(i, sv[m]);
+  }
+  // (the host guarantees nvec <= kStage * blockDim: one round covers it)
+  __syncthreads();
+
+  // B operand address: lanes of tokens past T read the zero block (stride 0)
+  const uint4* xb = reinterpret_cast<const uint4*>(r < T ? xl + r * xs + qg * 16 : zero);
+  const int xstride = r < T ? 16 : 0;              // uint4 per chunk
+
+  v4i a1 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0}, a16 = {0, 0, 0, 0};
+  struct Slices { v4i s0, s1, s2, s3; };
+  auto unpack = [](const uint4& w4) {
+    Slices q;
+    q.s0 = v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u),
+               (int)(w4.z & 0x03030303u), (int)(w4.w & 0x03030303u)};
+    q.s1 = v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu),
+               (int)(w4.z & 0x0C0C0C0Cu), (int)(w4.w & 0x0C0C0C0Cu)};
+    q.s2 = v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u),
+               (int)(w4.z & 0x30303030u), (int)(w4.w & 0x30303030u)};
+    q.s3 = v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
+               (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)};
+    return q;
+  };
+  auto mma = [&](const Slices& q, int c) {
+    const uint4* xc = xb + c * xstride;
+    const uint4 b0 = xc[0], b1 = xc[1], b2 = xc[2], b3 = xc[3];
+    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        q.s0, v4i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w}, a1, 0, 0, 0);
+    a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        q.s1, v4i{(int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w}, a4, 0, 0, 0);
+    a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        q.s2, v4i{(int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w}, a16, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        q.s3, v4i{(int)b3.x, (int)b3.y, (int)b3.z, (int)b3.w}, a1, 0, 0, 0);
+  };
+
+  int i0 = 0;
+  for (; i0 + P <= my; i0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = i0 + j;
+      // consume buf[j] first, then refill the same registers: no copies, and
+      // the wait before the masks is only for this one load (P-1 stay in flight)
+      const Slices q = unpack(buf[j]);
+      buf[j] = wrow[(size_t)chunk_of(i + P) * 4];
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q, wave + i * nwaves);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j)   // the last my % P chunks are already in buf[0..]
+    if (i0 + j < my) mma(unpack(buf[j]), wave + (i0 + j) * nwaves);
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    red[(wave * 4 + v) * 64 + lane] = a1[v] + (a4[v] >> 2) + (a16[v] >> 4);
+
+  // sum of q per token (removes the code offset), read back from LDS
+  for (int t = 0; t < T; ++t) {
+    const uint4* xt = reinterpret_cast<const uint4*>(xl + t * xs);
+    int part = 0;
+    for (int i = threadIdx.x; i < (K >> 4); i += blockDim.x) {
+      const uint4 v = xt[i];
+      part = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, part, false);
+      part = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, part, false);
+      part = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, part, false);
+      part = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, part, false);
+    }
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    part += __shfl_xor(part, 8);
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (lane == 0) atomicAdd(&rsum[t], part);
+  }
+  __syncthreads();
+  // 16 * T <= 256 outputs and blockDim >= 64: thread idx < 16 * T owns one
+  for (int idx = threadIdx.x; idx < 16 * T; idx += blockDim.x) {
+    const int i = idx & 15, tl = idx >> 4;
+    const int nn = n0 + i;
+    if (nn >= N) continue;
+    const int slot = i & 3, ln = (i >> 2) * 16 + tl;
+    int sum = -rsum[tl];
+    for (int wv = 0; wv < nwaves; ++wv) sum += red[(wv * 4 + slot) * 64 + ln];
+    const int64_t o = (int64_t)tl * N + nn;
+    if (acc_out) acc_out[o] = sum;
+    y[o] = (float)sum * out_scale(g, idx == (int)threadIdx.x ? am : absmax[tl]);
+  }
+}
+
+// Launch-shape tunables (compile-time so variants can be built and compared).
+#ifndef BL_GEMV_U
+#define BL_GEMV_U 4          // chunks whose loads a wave issues together
+#endif
+#ifndef BL_GEMV_MAXW
+#define BL_GEMV_MAXW 8       // most waves per block (they split K)
+#endif
+
+template <int VEC, int RT, int NTT, int U>
 void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
          int t, int n, int k, float* y, int32_t* acc, hipStream_t stream) {
   const int k16 = k / 16;
   const int nchunks = (k16 + 4 * VEC - 1) / (4 * VEC);
-  int nw = nchunks / 2;                 // at least two chunks per wave where possible
+  int nw = (nchunks + U - 1) / U;       // one pass of U chunks per wave where possible
   if (nw < 1) nw = 1;
-  if (nw > kMaxWaves) nw = kMaxWaves;
+  if (nw > BL_GEMV_MAXW) nw = BL_GEMV_MAXW;
   const int grid = (n + 16 * RT - 1) / (16 * RT);
   const size_t lds = (size_t)nw * RT * NTT * 4 * 64 * sizeof(int);
-  k_gemv<VEC, RT, NTT><<<grid, nw * 64, lds, stream>>>(
+  k_gemv<VEC, RT, NTT, U><<<grid, nw * 64, lds, stream>>>(
       reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc);
 }
 
@@ -174,18 +360,72 @@ void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
                 const float* absmax, int t, int n, int k, float* y, int32_t* acc,
                 hipStream_t stream) {
   if (t <= 16)
-    run<VEC, 1, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   else if (t <= 32)
-    run<VEC, 2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    run<VEC, 2, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                    stream);
   else
-    run<VEC, 2, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    run<VEC, 2, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
 }
 
 }  // namespace
 
+#ifndef BL_GEMV_PIPE_P
+#define BL_GEMV_PIPE_P 6          // chunks in flight per wave in the pipelined kernel
+#endif
+#ifndef BL_GEMV_PIPE_WAVES
+#define BL_GEMV_PIPE_WAVES 2048   // total waves aimed for (about 8 per CU)
+#endif
+#ifndef BL_GEMV_PIPE_MINCPW
+#define BL_GEMV_PIPE_MINCPW 4     // fewest chunks per wave when splitting K
+#endif
+#ifndef BL_GEMV_PIPE_XLDS
+#define BL_GEMV_PIPE_XLDS 32768  // largest T*K staged in LDS
+#endif
+
+// Waves per block of the pipelined kernel.  Large grids do best with few,
+// long-running waves (each streams many chunks); small grids need K split over
+// more waves to have enough loads in flight.  Aim for about
+// BL_GEMV_PIPE_WAVES waves in total with at least BL_GEMV_PIPE_MINCPW chunks
+// each, and enough threads to stage T*K bytes in one round.
+int pipe_waves(int64_t t, int64_t n, int64_t k) {
+  const int nchunks = (int)(k / 256);
+  const int64_t blocks = (n + 15) / 16;
+  int nw = (int)((BL_GEMV_PIPE_WAVES + blocks - 1) / blocks);
+  int cap = nchunks / BL_GEMV_PIPE_MINCPW;
+  if (cap < 1) cap = 1;
+  if (nw > cap) nw = cap;
+  const int64_t vecs = t * k / 16;
+  const int need = (int)((vecs + 64 * kGemvStage - 1) / (64 * kGemvStage));
+  if (nw < need) nw = need;
+  if (nw > nchunks) nw = nchunks;
+  return nw;
+}
+
+bool pipe_ok(int64_t t, int64_t n, int64_t k, const void* packed, const void* xq) {
+  if (!(t <= 16 && (k % 256) == 0 && t * k <= BL_GEMV_PIPE_XLDS &&
+        (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
+        (reinterpret_cast<uintptr_t>(xq) % 16) == 0))
+    return false;
+  const int nw = pipe_waves(t, n, k);
+  return nw <= 16 && t * k / 16 <= (int64_t)nw * 64 * kGemvStage;
+}
+
+void run_pipe(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
+              int t, int n, int k, float* y, int32_t* acc, hipStream_t stream) {
+  const int nw = pipe_waves(t, n, k);
+  const size_t lds = 256 + (size_t)t * (k + 16) + 16 * sizeof(int) + (size_t)nw * 4 * 64 * sizeof(int);
+  k_gemv_pipe<BL_GEMV_PIPE_P><<<(n + 15) / 16, nw * 64, lds, stream>>>(
+      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc);
+}
+
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
+  if (pipe_ok(t, n, k, packed, xq)) {
+    run_pipe(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, stream);
+    return hipGetLastError();
+  }
   const bool vec4 = (k % 64) == 0 && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
   for (int64_t t0 = 0; t0 < t; t0 += kGemvTokens) {

@@ -189,7 +189,10 @@ def test_quant_special_rows(bl, dtype):
 
 FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (16, 33, 320),
               (17, 100, 256), (33, 64, 128), (64, 200, 1024), (65, 130, 192), (130, 257, 272),
-              (1, 2560, 2560), (8, 640, 2560), (1, 100, 6912), (5, 37, 28672)]
+              (1, 2560, 2560), (8, 640, 2560), (1, 100, 6912), (5, 37, 28672),
+              # decode kernel edges: ragged N, T = 16 at the staging limit,
+              # many waves per block, one chunk per wave
+              (3, 37, 512), (16, 50, 2048), (2, 17, 8192), (1, 3, 256), (1, 1000, 28672)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
