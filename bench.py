@@ -5,12 +5,16 @@
 A step is one pass of the per-token hot path over one 2B-class decoder layer
 at T = 1: for each of its seven projections (q, k, v, o: 2560->2560/640;
 gate, up: 2560->6912; down: 6912->2560) the bf16 activation is quantised to
-int8 (act-quant kernel) and contracted with the 2-bit packed ternary weights
-(decode GEMV kernel, rescale fused).  Weights are packed once at set-up
-(step A0 is an offline conversion) and then copied to L distinct layer sets
-(> 1 GB in total, four times the 256 MB MALL), and consecutive steps rotate
-through them, so every step streams its weights from HBM.  The timed steps
-replay a HIP graph of L consecutive steps.
+int8 and contracted with the 2-bit packed ternary weights, then rescaled.
+The projections run as four launches in the order a decoder layer needs
+them -- [q, k, v], [o], [gate, up], [down] -- each one call of
+bitlinear_linear_grouped (act-quant fused into the decode GEMV kernel).
+Weights are packed once at set-up (step A0 is an offline conversion) and then
+copied to L distinct layer sets (> 1 GB in total, four times the 256 MB MALL),
+and consecutive steps rotate through them, so every step streams its weights
+from HBM.  The timed steps replay a HIP graph of L consecutive steps.  The
+same layer as 14 separate launches (act-quant, then forward, per projection)
+is reported beside it.
 
 The JSON line reports algorithmic GB/s of the whole step (value), the decode
 GEMV kernel against the HBM roofline, the CPU oracle timed on a bounded
@@ -46,9 +50,15 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--profile-pass", action="store_true",
-                   help="counter runs: two eager passes over the layer sets plus the copy "
-                        "calibration, no timing and no JSON")
+                   help="counter runs: two eager passes of the fused steps over the layer "
+                        "sets plus the copy calibration, no timing and no JSON")
     return p.parse_args()
+
+
+def fused_bytes(t, n, k, in_bytes=2):
+    """Algorithmic bytes of one problem of a fused launch: packed W, raw x and
+    gamma in; fp32 y, int8 x and absmax out."""
+    return n * k // 4 + in_bytes * t * k + 4 + 4 * t * n + t * k + 4 * t
 
 
 def gemv_bytes(t, n, k):
@@ -95,6 +105,11 @@ class Calls:
     def forward(self, packed, gamma, xq, absmax, t, n, k, y, algo, stream):
         rc = self.lib.bitlinear_forward_algo(packed, gamma, xq, absmax, t, n, k, y, None, algo,
                                              stream)
+        if rc:
+            raise RuntimeError(self.lib.bitlinear_last_error().decode())
+
+    def grouped(self, descs, t, stream):
+        rc = self.lib.bitlinear_linear_grouped(descs, len(descs), t, 1, stream)
         if rc:
             raise RuntimeError(self.lib.bitlinear_last_error().decode())
 
@@ -180,7 +195,7 @@ def cpu_baseline(oracle, wl, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or layers >= 200:
             break
-    step_bytes = sum(gemv_bytes(1, m.n, m.k) + quant_bytes(1, m.k) for m in wk.matrices)
+    step_bytes = sum(fused_bytes(1, m.n, m.k) for m in wk.matrices)
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -257,6 +272,7 @@ def main():
     set_ptrs = [[ptr(p) for p in s] for s in sets]
 
     def steps(s, with_quant=True, with_gemv=True):
+        """The layer as 14 launches: act-quant then forward per projection."""
         h = ctypes.c_void_p(s.cuda_stream)
         for sp in set_ptrs:                      # one step per layer set
             for mi, d in enumerate(mp):
@@ -266,9 +282,33 @@ def main():
                     calls.forward(sp[mi], d["gamma"], d["xq"], d["absmax"], 1, d["n"], d["k"],
                                   d["y"], 1, h)
 
+    # The layer's dependency order: q, k, v share their input; o needs the
+    # attention output; gate, up share their input; down needs their product.
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    group_descs = []
+    for sp in set_ptrs:
+        per_set = []
+        for grp in groups:
+            arr = (binding.BlLinear * len(grp))()
+            for gi, mi in enumerate(grp):
+                d = mats[mi]
+                arr[gi] = binding.BlLinear(d["x"].data_ptr(), sp[mi].value,
+                                           d["gamma"].data_ptr(), d["m"].n, d["m"].k,
+                                           d["y"].data_ptr(), d["xq"].data_ptr(),
+                                           d["absmax"].data_ptr(), None)
+            per_set.append(arr)
+        group_descs.append(per_set)
+
+    def fused_steps(s):
+        """The layer as four fused launches in dependency order."""
+        h = ctypes.c_void_p(s.cuda_stream)
+        for per_set in group_descs:
+            for arr in per_set:
+                calls.grouped(arr, 1, h)
+
     if args.profile_pass:
         for _ in range(2):
-            steps(stream)
+            fused_steps(stream)
         stream.synchronize()
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -277,19 +317,24 @@ def main():
         print("profile pass done", flush=True)
         return
 
-    step_bytes = sum(gemv_bytes(1, d["n"], d["k"]) + quant_bytes(1, d["k"]) for d in mp)
+    step_bytes = sum(fused_bytes(1, d["n"], d["k"]) for d in mp)
+    fused_launch_bytes = step_bytes / len(groups)
+    unfused_step_bytes = sum(gemv_bytes(1, d["n"], d["k"]) + quant_bytes(1, d["k"]) for d in mp)
     gemv_launch_bytes = sum(gemv_bytes(1, d["n"], d["k"]) for d in mp) / len(mp)
 
     reps = max(1, args.steps // n_sets)
     warm = max(1, args.warmup // n_sets)
     k_steps = reps * n_sets
 
-    # timed region: whole steps (act-quant + GEMV for all seven projections)
-    g_all = capture(torch, lambda s: steps(s), stream)
-    ms = time_graph(torch, g_all, reps, warm, stream)
+    # timed region: whole steps, four fused launches each
+    g_fused = capture(torch, fused_steps, stream)
+    ms = time_graph(torch, g_fused, reps, warm, stream)
     ms_per_step = ms / k_steps
+    fused_us = ms * 1e3 / (k_steps * len(groups))
 
-    # the dominant kernel alone: average duration of one decode-GEMV launch
+    # the same layer as 14 separate launches, and its kernels alone
+    g_all = capture(torch, lambda s: steps(s), stream)
+    ms_unfused = time_graph(torch, g_all, reps, warm, stream)
     g_gemv = capture(torch, lambda s: steps(s, with_quant=False), stream)
     ms_g = time_graph(torch, g_gemv, reps, warm, stream)
     gemv_us = ms_g * 1e3 / (k_steps * len(mp))
@@ -297,12 +342,12 @@ def main():
     ms_q = time_graph(torch, g_quant, reps, warm, stream)
     quant_us = ms_q * 1e3 / (k_steps * len(mp))
 
-    # the same steps launched one by one on the stream, without a graph
+    # the fused steps launched one by one on the stream, without a graph
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     eager_reps = max(1, reps // 4)
     for _ in range(eager_reps):
-        steps(stream)
+        fused_steps(stream)
     stream.synchronize()
     eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / (eager_reps * n_sets)
 
@@ -313,15 +358,19 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    achieved = gemv_launch_bytes / (gemv_us * 1e-6) / 1e9
+    achieved = fused_launch_bytes / (fused_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": committed_traffic("gemv.hip", "decode_gemv_2b_t1"),
-                "kernel": "k_gemv (decode GEMV, T=1)",
-                "avg_launch_us": round(gemv_us, 3),
-                "algorithmic_bytes_per_launch": int(gemv_launch_bytes)}
+                "traffic": committed_traffic("gemv.hip", "decode_fused_2b_t1"),
+                "kernel": "k_gemv_pipe (act-quant fused into the decode GEMV), T=1",
+                "avg_launch_us": round(fused_us, 3),
+                "algorithmic_bytes_per_launch": int(fused_launch_bytes)}
 
     extra = {"eager_ms_per_step": round(eager_ms_per_step, 4),
+             "unfused_ms_per_step": round(ms_unfused / k_steps, 5),
+             "unfused_gb_s": round(unfused_step_bytes / (ms_unfused / k_steps * 1e-3) / 1e9, 2),
+             "gemv_avg_launch_us": round(gemv_us, 3),
+             "gemv_gb_s": round(gemv_launch_bytes / (gemv_us * 1e-6) / 1e9, 1),
              "act_quant_avg_launch_us": round(quant_us, 3),
              "layer_sets_rotated": n_sets,
              "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
@@ -341,8 +390,9 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
            "data": "synthetic",
            "config": {"workload": "decode_2b_t1_layer: T=1, bf16 x, 7 projections "
-                                  "(2560->2560, 2560->640 x2, 2560->2560, 2560->6912 x2, "
-                                  "6912->2560), act-quant + GEMV each, weights rotated cold",
+                                  "(q 2560->2560, k/v 2560->640, o 2560->2560, gate/up "
+                                  "2560->6912, down 6912->2560) as 4 fused launches "
+                                  "[qkv][o][gate,up][down], weights rotated cold",
                       "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
                       "step_bytes": int(step_bytes)},
            "roofline": roofline, "cpu_baseline": cpu, "extra": extra}

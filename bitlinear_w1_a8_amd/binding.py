@@ -37,6 +37,16 @@ SIGNATURES = {
 }
 
 
+class BlLinear(ctypes.Structure):
+    """struct bl_linear of include/bitlinear.h."""
+    _fields_ = [("x", _c_vp), ("packed", _c_vp), ("gamma", _c_vp), ("N", _c_i64),
+                ("K", _c_i64), ("y", _c_vp), ("xq", _c_vp), ("absmax", _c_vp), ("acc", _c_vp)]
+
+
+SIGNATURES["bitlinear_linear_grouped"] = (_c_int, [ctypes.POINTER(BlLinear), _c_int, _c_i64,
+                                                   _c_int, _c_vp])
+
+
 class BitLinearError(RuntimeError):
     """A non-OK status from libbitlinear; ``status`` holds the code."""
 
@@ -144,3 +154,36 @@ def bitlinear(x, packed, gamma, n, algo="auto"):
     """Quantise x and run the forward: y = BitLinear(x) with pre-packed weights."""
     xq, absmax, _ = quant_act(x, with_rowsum=False)
     return forward(packed, gamma, xq, absmax, n, algo=algo)
+
+
+def linear_grouped(xs, weights, want_acc=False):
+    """Steps A1-A3 for several independent problems in one call.
+
+    xs: list of activations [T, K_i] (one dtype, float32 or bfloat16, same T);
+    weights: list of (packed, gamma) from pack_weights.  Returns a list of
+    (y, xq, absmax, acc-or-None) per problem.
+    """
+    lib = load()
+    if not xs or len(xs) != len(weights):
+        raise ValueError("need one (packed, gamma) per activation tensor")
+    dt = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}.get(xs[0].dtype)
+    if dt is None:
+        raise TypeError(f"x must be float32 or bfloat16, got {xs[0].dtype}")
+    t = xs[0].shape[0]
+    outs, descs = [], (BlLinear * len(xs))()
+    for i, (x, (packed, gamma)) in enumerate(zip(xs, weights)):
+        _need_cuda(x, "x", xs[0].dtype)
+        _need_cuda(packed, "packed", torch.uint8)
+        _need_cuda(gamma, "gamma", torch.float32)
+        k = x.shape[1]
+        n = packed.shape[0]
+        y = torch.empty((t, n), dtype=torch.float32, device=x.device)
+        xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
+        absmax = torch.empty(t, dtype=torch.float32, device=x.device)
+        acc = torch.empty((t, n), dtype=torch.int32, device=x.device) if want_acc else None
+        descs[i] = BlLinear(x.data_ptr(), packed.data_ptr(), gamma.data_ptr(), n, k,
+                            y.data_ptr(), xq.data_ptr(), absmax.data_ptr(),
+                            acc.data_ptr() if acc is not None else None)
+        outs.append((y, xq, absmax, acc))
+    _check(lib.bitlinear_linear_grouped(descs, len(xs), t, dt, _stream(xs[0].device)))
+    return outs

@@ -112,6 +112,31 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
   return fail(BL_ERR_ARG, "%s: unknown algo %d", fn, algo);
 }
 
+int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
+                             void* stream) {
+  const char* fn = "bitlinear_linear_grouped";
+  if (!problems) return fail(BL_ERR_NULL, "%s: NULL problems array", fn);
+  if (count < 1 || count > 8) return fail(BL_ERR_ARG, "%s: count=%d must be in [1, 8]", fn, count);
+  if (x_dtype != BL_F32 && x_dtype != BL_BF16)
+    return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  for (int i = 0; i < count; ++i) {
+    const bl_linear& q = problems[i];
+    if (!q.x || !q.packed || !q.gamma || !q.y || !q.xq || !q.absmax)
+      return fail(BL_ERR_NULL, "%s: problem %d: NULL pointer argument", fn, i);
+    if (int rc = check_k(fn, q.K)) return rc;
+    if (q.N < 1 || q.N > kMaxN || T * q.N > kMaxTN)
+      return fail(BL_ERR_SHAPE, "%s: problem %d: N=%lld out of range", fn, i, (long long)q.N);
+    if (!aligned(q.x, 16) || !aligned(q.packed, 16) || !aligned(q.xq, 16) ||
+        !aligned(q.gamma, 4) || !aligned(q.y, 4) || !aligned(q.absmax, 4) ||
+        (q.acc && !aligned(q.acc, 4)))
+      return fail(BL_ERR_ALIGN, "%s: problem %d: x, packed and xq need 16-byte, the others "
+                  "4-byte alignment", fn, i);
+  }
+  return launched(fn, bl::launch_linear_group(problems, count, T, x_dtype == BL_BF16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
                       const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
                       int32_t* acc, void* stream) {

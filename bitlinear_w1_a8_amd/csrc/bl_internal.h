@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bitlinear.h"
+
 namespace bl {
 
 // Constants of the forward.  eps is added to gamma before the weight division
@@ -26,6 +28,10 @@ hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* x
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream);
+
+// Steps A1-A3 for a group of problems (bitlinear_linear_grouped).
+hipError_t launch_linear_group(const struct bl_linear* probs, int count, int64_t t, int bf16,
+                               hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,

@@ -1,112 +1,188 @@
 // Steps A2 + A3 for many tokens (prefill): a dense int8 contraction on the
-// matrix cores.  Ternary weight tiles are expanded to int8 in LDS, as the
-// 2B4T report (section 5.1) describes for its GPU kernel (packed in HBM,
-// unpacked on chip, multiplied with 8-bit activations), and the result is
-// rescaled in the epilogue.
+// matrix cores, rescaled in the epilogue.
 //
-// Tile: BM tokens x BN weight rows per block, K in steps of BK.  Per K step
-// the block copies the int8 activation tile to LDS and expands the packed
-// weight tile to signed int8 in LDS: (word >> 2j) & 0x03030303 isolates four
-// codes c in {0,1,2}, and one byte-permute through the table {-1, 0, +1}
-// turns them into t = c - 1.  Waves run v_mfma_i32_32x32x32_i8 with
-// A = activations (rows = tokens) and B = weights (columns = output rows), so
-// each lane's 16 results share one output column and a store of one register
-// across the wave covers 32 consecutive outputs of a token.
+// The 2B4T report (section 5.1) keeps four ternary weights per byte in HBM,
+// moves them on chip, unpacks them and multiplies with 8-bit activations.
+// Here the int8 activations go through LDS (they are reused by every wave of
+// the block), while the packed weights go straight from memory into
+// registers: a lane loads 16 bytes (four packed words, 64 weights of one
+// output row) per K step and expands them in registers,
+//   codes = (word >> 2j) & 0x03030303,  t = byte-permute({-1,0,+1}, codes),
+// two or three VALU operations per four weights, into MFMA B operands.
+//
+// v_mfma_i32_32x32x32_i8: A = 32 tokens x 32 k (from LDS), B = 32 k x 32
+// output rows.  Within one MFMA the pairing of k with (lane half, byte) is
+// free as long as A and B agree; this kernel gives lane half h of K-step s the
+// 16 k of packed word 4h + s (relative to the 128-wide K tile), so the four
+// words a lane needs over a K tile are contiguous in memory.
+//
+// Block: 2 x 2 waves, each owning WMF x WNF tiles of 32 x 32 outputs; K in
+// steps of 128 with the activation tile double-buffered in LDS and the next
+// tile's loads in flight during the current tile's MFMAs.  Tiles are ordered
+// so that consecutive tiles of one XCD share activation rows in its L2.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kPad = 16;                 // bytes of padding per LDS row
-constexpr int kLd = BK + kPad;
+constexpr int BK = 128;
+constexpr int kLd = BK + 16;                  // LDS row stride (bytes): spreads banks
 constexpr uint32_t kTernTable = 0x000100FFu;  // bytes {0xFF, 0x00, 0x01, 0x00}
 
 __device__ __forceinline__ uint32_t signed_codes(uint32_t word, int j) {
   return __builtin_amdgcn_perm(kTernTable, kTernTable, codes_of(word, j));
 }
 
+template <int WMF, int WNF>
 __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ packed,
                                                    const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ xq,
                                                    const float* __restrict__ absmax, int T,
                                                    int N, int K, float* __restrict__ y,
                                                    int32_t* __restrict__ acc_out) {
-  __shared__ __align__(16) int8_t As[BM * kLd];
-  __shared__ __align__(16) int8_t Bs[BN * kLd];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int BM = 2 * 32 * WMF, BN = 2 * 32 * WNF;
+  constexpr int kAVec = BM * BK / 16 / kThreads;   // 16-byte A vectors per thread per tile
+  extern __shared__ __align__(16) unsigned char smem[];
+  int8_t* As = reinterpret_cast<int8_t*>(smem);    // [2][BM][kLd]
+  float* scale = reinterpret_cast<float*>(smem + 2 * BM * kLd);  // [BM]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int ntn = (N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * BN;
   const int K16 = K >> 4;
 
-  v16i acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a
+  // contiguous, M-major range of tiles.
+  const int ntn = (N + BN - 1) / BN, ntm = (T + BM - 1) / BM;
+  const int tiles = ntn * ntm;
+  int tile = blockIdx.x;
+  if (tiles >= 8 && (tiles % 8) == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    // activations: BM rows x BK bytes, 16 bytes per thread per step
+  // per-token output scale, once per block
+  {
+    const float g = gamma[0];
+    for (int r = tid; r < BM; r += kThreads) {
+      const int tok = m0 + r;
+      scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
+    }
+  }
+
+  // activation tile loader: thread handles kAVec 16-byte vectors
+  auto load_a = [&](int k0, uint4 (&v)[kAVec]) {
 #pragma unroll
-    for (int u = 0; u < (BM * BK / 16) / kThreads; ++u) {
+    for (int u = 0; u < kAVec; ++u) {
       const int id = tid + u * kThreads;
       const int row = id / (BK / 16), c16 = id % (BK / 16);
       const int tok = m0 + row, kk = k0 + c16 * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tok < T && kk < K) v = *reinterpret_cast<const uint4*>(xq + (int64_t)tok * K + kk);
-      *reinterpret_cast<uint4*>(As + row * kLd + c16 * 16) = v;
+      v[u] = (tok < T && kk < K) ? *reinterpret_cast<const uint4*>(xq + (int64_t)tok * K + kk)
+                                 : make_uint4(0, 0, 0, 0);
     }
-    // weights: BN rows x BK/16 packed words, expanded to 16 signed bytes each
+  };
+  auto store_a = [&](int buf, const uint4 (&v)[kAVec]) {
 #pragma unroll
-    for (int u = 0; u < (BN * BK / 16) / kThreads; ++u) {
+    for (int u = 0; u < kAVec; ++u) {
       const int id = tid + u * kThreads;
-      const int row = id / (BK / 16), wj = id % (BK / 16);
-      const int n = n0 + row, wi = (k0 >> 4) + wj;
-      uint32_t w = 0;
-      if (n < N && wi < K16) w = packed[(int64_t)n * K16 + wi];
-      const uint4 e = make_uint4(signed_codes(w, 0), signed_codes(w, 1), signed_codes(w, 2),
-                                 signed_codes(w, 3));
-      *reinterpret_cast<uint4*>(Bs + row * kLd + wj * 16) = e;
+      const int row = id / (BK / 16), c16 = id % (BK / 16);
+      *reinterpret_cast<uint4*>(As + (buf * BM + row) * kLd + c16 * 16) = v[u];
     }
-    __syncthreads();
+  };
+  // weight words: lane (row l%32 of fragment j, half h = l/32) loads words
+  // 4h .. 4h+3 of the K tile; rows past N read row N-1 (outputs discarded)
+  const uint32_t* brow[WNF];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int kb = ks * 32 + (lane >> 5) * 16;
-      v4i a[2], b[2];
+  for (int j = 0; j < WNF; ++j) {
+    int n = n0 + wn * 32 * WNF + j * 32 + (lane & 31);
+    n = n < N ? n : N - 1;
+    brow[j] = packed + (int64_t)n * K16 + 4 * (lane >> 5);
+  }
+  auto load_b = [&](int k0, uint4 (&w)[WNF]) {
+    const int wi = k0 >> 4;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 t = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 32 + (lane & 31)) * kLd + kb);
+    for (int j = 0; j < WNF; ++j) {
+      // words wi+4h .. wi+4h+3 exist when K16 - wi >= 8; a K tail (K % 128)
+      // reads word by word and zero-fills (the activations there are zero)
+      if ((K16 & 3) == 0 && wi + 8 <= K16) {      // 16-byte aligned and in range
+        w[j] = *reinterpret_cast<const uint4*>(brow[j] + wi);
+      } else {
+        const int h4 = 4 * (lane >> 5);
+        uint32_t t[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t[s] = (wi + h4 + s < K16) ? brow[j][wi + s] : 0u;
+        w[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+    }
+  };
+
+  v16i acc[WMF][WNF];
+#pragma unroll
+  for (int i = 0; i < WMF; ++i)
+#pragma unroll
+    for (int j = 0; j < WNF; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  uint4 av[kAVec];
+  uint4 bw[WNF], bw_next[WNF];
+  load_a(0, av);
+  load_b(0, bw);
+  store_a(0, av);
+  __syncthreads();
+
+  const int ntiles_k = (K + BK - 1) / BK;
+  for (int kt = 0; kt < ntiles_k; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < ntiles_k;
+    // next tile's loads: activations first (waited on before the barrier),
+    // then weights (consumed one iteration later)
+    if (more) {
+      load_a((kt + 1) * BK, av);
+      load_b((kt + 1) * BK, bw_next);
+    }
+    const int8_t* At = As + (cur * BM + wm * 32 * WMF + (lane & 31)) * kLd + 64 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i a[WMF], b[WNF];
+#pragma unroll
+      for (int i = 0; i < WMF; ++i) {
+        const uint4 t = *reinterpret_cast<const uint4*>(At + i * 32 * kLd + 16 * s);
         a[i] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 t = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + j * 32 + (lane & 31)) * kLd + kb);
-        b[j] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+      for (int j = 0; j < WNF; ++j) {
+        const uint32_t w = s == 0 ? bw[j].x : s == 1 ? bw[j].y : s == 2 ? bw[j].z : bw[j].w;
+        b[j] = v4i{(int)signed_codes(w, 0), (int)signed_codes(w, 1), (int)signed_codes(w, 2),
+                   (int)signed_codes(w, 3)};
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WMF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < WNF; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      store_a(cur ^ 1, av);
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) bw[j] = bw_next[j];
     }
     __syncthreads();
   }
 
-  const float g = gamma[0];
+  // epilogue: lane holds column (l % 32) of each fragment and rows
+  // 8*(v/4) + 4*(l/32) + v%4; a register across the wave stores 32
+  // consecutive outputs of two tokens
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < WMF; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int tok = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int r = wm * 32 * WMF + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int tok = m0 + r;
       if (tok >= T) continue;
-      const float sc = out_scale(g, absmax[tok]);
+      const float sc = scale[r];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      for (int j = 0; j < WNF; ++j) {
+        const int n = n0 + wn * 32 * WNF + j * 32 + (lane & 31);
         if (n >= N) continue;
         const int64_t o = (int64_t)tok * N + n;
         const int s = acc[i][j][v];
@@ -117,16 +193,248 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-direct variant (K % 128 == 0): both operands move global -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging), double-buffered, one barrier per
+// 128-wide K step.  The instruction writes 64 lanes x 16 bytes contiguously,
+// so the layout is chosen through the source addresses:
+//   activations: 1 KiB = 8 rows x 128 bytes; row r's 16-byte slot p holds
+//     logical slot p ^ ((r >> 1) & 7), spreading one MFMA read (32 rows, same
+//     column) over the banks;
+//   packed weights: 1 KiB = 32 rows x 32 bytes (8 words = 128 k), row-major.
+// Each wave reads its four weight words per fragment with one 16-byte LDS
+// read and expands them in registers, as in the kernel above.
+// s_waitcnt vmcnt(N) with the other counters left alone (N < 16)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // lgkmcnt 15, expcnt 7, vmcnt N
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+// One static LDS object per pipeline stage: the compiler can then tell that
+// the loads landing in one stage do not alias reads of another, and does not
+// drain every outstanding load before each LDS read.
+template <int WAVES_M, int WMF, int WNF, int STAGES>
+__global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restrict__ packed,
+                                                       const float* __restrict__ gamma,
+                                                       const int8_t* __restrict__ xq,
+                                                       const float* __restrict__ absmax, int T,
+                                                       int N, int K, float* __restrict__ y,
+                                                       int32_t* __restrict__ acc_out) {
+  static_assert(STAGES == 3, "the unrolled step sequence below assumes three stages");
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
+  constexpr int kABuf = BM * BK, kBBuf = BN * (BK / 4);   // bytes per stage
+  constexpr int kAChunks = BM / 8 / 4, kBChunks = BN / 32 / 4;  // 1 KiB loads per wave
+  static_assert(kBChunks >= 1, "BN must be a multiple of 128");
+  __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf], A2[kABuf];
+  __shared__ __align__(16) unsigned char B0[kBBuf], B1[kBBuf], B2[kBBuf];
+  __shared__ float scale[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int K16 = K >> 4;
+
+  const int ntn = (N + BN - 1) / BN, ntm = (T + BM - 1) / BM;
+  const int tiles = ntn * ntm;
+  int tile = blockIdx.x;
+  if (tiles >= 8 && (tiles % 8) == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+
+  // per-token output scale first: its loads retire before the pipeline starts
+  {
+    const float g = gamma[0];
+    for (int r = tid; r < BM; r += kThreads) {
+      const int tok = m0 + r;
+      scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
+    }
+  }
+
+  // 32-bit offsets from the uniform bases (the host keeps T*K and N*K/16
+  // below 2^31), so each load is a scalar base plus one VGPR offset
+  uint32_t aoff[kAChunks];
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    const int c = wave * kAChunks + i;
+    const int r = 8 * c + (lane >> 3);
+    const int slot = (lane & 7) ^ ((r >> 1) & 7);
+    int tok = m0 + r;
+    tok = tok < T ? tok : T - 1;
+    aoff[i] = (uint32_t)tok * (uint32_t)K + 16u * slot;
+  }
+  uint32_t boff[kBChunks];
+#pragma unroll
+  for (int i = 0; i < kBChunks; ++i) {
+    const int c = wave * kBChunks + i;
+    int n = n0 + 32 * c + (lane >> 1);
+    n = n < N ? n : N - 1;
+    boff[i] = (uint32_t)n * (uint32_t)K16 + 4u * (lane & 1);
+  }
+  auto issue = [&](int kt, unsigned char* As, unsigned char* Bs) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(xq + (aoff[i] + k0)),
+                                       (lds_ptr_t)(As + (wave * kAChunks + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> 4))),
+                                       (lds_ptr_t)(Bs + (wave * kBChunks + i) * 1024), 16, 0, 0);
+  };
+
+  v16i acc[WMF][WNF];
+#pragma unroll
+  for (int i = 0; i < WMF; ++i)
+#pragma unroll
+    for (int j = 0; j < WNF; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  const int nk = K / BK;
+  constexpr int kLoads = kAChunks + kBChunks;     // this wave's loads per tile
+  static_assert(kLoads < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
+  issue(0, A0, B0);
+  issue(nk > 1 ? 1 : 0, A1, B1);                  // (a harmless repeat when nk == 1)
+  wait_vm<kLoads>();                              // tile 0 landed, tile 1 in flight
+  __syncthreads();
+
+  const int h = lane >> 5, m = lane & 31;
+  const int aswz = (m >> 1) & 7;
+  // one K step on stage (As, Bs); refill stage (An, Bn) with tile kt + 2
+  auto step = [&](int kt, const unsigned char* As, const unsigned char* Bs, unsigned char* An,
+                  unsigned char* Bn) {
+    const bool refill = kt + 2 < nk;
+    if (refill) issue(kt + 2, An, Bn);
+    const unsigned char* At = As + (wm * 32 * WMF + m) * BK;
+    const unsigned char* Bt = Bs + (wn * 32 * WNF + m) * (BK / 4) + 16 * h;
+    uint4 bw[WNF];
+#pragma unroll
+    for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * (BK / 4));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = 16 * ((4 * h + s) ^ aswz);
+      v4i a[WMF];
+#pragma unroll
+      for (int i = 0; i < WMF; ++i) {
+        const uint4 t = *reinterpret_cast<const uint4*>(At + i * 32 * BK + off);
+        a[i] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+      }
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) {
+        // expand one weight fragment right before its MFMAs (few live registers)
+        const uint32_t w = s == 0 ? bw[j].x : s == 1 ? bw[j].y : s == 2 ? bw[j].z : bw[j].w;
+        const v4i b = {(int)signed_codes(w, 0), (int)signed_codes(w, 1),
+                       (int)signed_codes(w, 2), (int)signed_codes(w, 3)};
+#pragma unroll
+        for (int i = 0; i < WMF; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep K steps apart: bounds live registers
+    }
+    // Tile kt+1 must have landed: this wave's loads by the wait, everyone's
+    // by the barrier.  A plain s_barrier, not __syncthreads(): the latter's
+    // release fence would also wait for the refill issued above.  The only
+    // LDS writes in the loop are these loads, which the wait covers.
+    if (refill) wait_vm<kLoads>();
+    else wait_vm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nk; kt += 3) {
+    step(kt, A0, B0, A2, B2);
+    if (kt + 1 < nk) step(kt + 1, A1, B1, A0, B0);
+    if (kt + 2 < nk) step(kt + 2, A2, B2, A1, B1);
+  }
+
+#pragma unroll
+  for (int i = 0; i < WMF; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 32 * WMF + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+      const int tok = m0 + r;
+      if (tok >= T) continue;
+      const float sc = scale[r];
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) {
+        const int n = n0 + wn * 32 * WNF + j * 32 + m;
+        if (n >= N) continue;
+        const int64_t o = (int64_t)tok * N + n;
+        const int sv = acc[i][j][v];
+        if (acc_out) acc_out[o] = sv;
+        y[o] = (float)sv * sc;
+      }
+    }
+  }
+}
+
+template <int WAVES_M, int WMF, int WNF, int STAGES>
+hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                   const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
+                   hipStream_t stream) {
+  constexpr int BM = WAVES_M * 32 * WMF, BN = (4 / WAVES_M) * 32 * WNF;
+  const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
+  auto kern = k_gemm_lds<WAVES_M, WMF, WNF, STAGES>;
+  kern<<<dim3((unsigned)tiles), kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed),
+                                                         gamma, xq, absmax, (int)t, (int)n,
+                                                         (int)k, y, acc);
+  return hipGetLastError();
+}
+
+template <int WMF, int WNF>
+hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
+               int64_t t, int64_t n, int64_t k, float* y, int32_t* acc, hipStream_t stream) {
+  constexpr int BM = 64 * WMF, BN = 64 * WNF;
+  const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
+  const size_t lds = 2 * (size_t)BM * kLd + BM * sizeof(float);
+  auto kern = k_gemm<WMF, WNF>;
+  static bool lds_set = false;  // once per process (idempotent if raced)
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  kern<<<dim3((unsigned)tiles), kThreads, lds, stream>>>(reinterpret_cast<const uint32_t*>(packed),
+                                                         gamma, xq, absmax, (int)t, (int)n,
+                                                         (int)k, y, acc);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+#ifndef BL_GEMM_BIG_MIN_TILES
+#define BL_GEMM_BIG_MIN_TILES 384   // use 256 x 128 tiles when at least this many exist
+#endif
+
+#ifndef BL_GEMM_LDS_MIN_TILES
+#define BL_GEMM_LDS_MIN_TILES 128   // LDS-direct tiles from this many tiles on
+#endif
+#ifndef BL_GEMM_STAGES
+#define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
+#endif
+#ifndef BL_GEMM_WAVES_M
+#define BL_GEMM_WAVES_M 1           // 1: 128 x 512 block tiles; 2: 256 x 256
+#endif
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
-  const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  const dim3 grid((unsigned)tiles);
-  k_gemm<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed), gamma, xq,
-                                        absmax, (int)t, (int)n, (int)k, y, acc);
-  return hipGetLastError();
+  constexpr int kLdsBM = BL_GEMM_WAVES_M * 128, kLdsBN = (4 / BL_GEMM_WAVES_M) * 128;
+  const int64_t lds_tiles = ((n + kLdsBN - 1) / kLdsBN) * ((t + kLdsBM - 1) / kLdsBM);
+  if (k % BK == 0 && lds_tiles >= BL_GEMM_LDS_MIN_TILES && t * k < (int64_t(1) << 31) &&
+      n * (k / 16) < (int64_t(1) << 31))
+    return run_lds<BL_GEMM_WAVES_M, 4, 4, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y,
+                                                          acc, stream);
+  const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
+  if (big >= BL_GEMM_BIG_MIN_TILES)
+    return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+  return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
 }
 
 }  // namespace bl

@@ -22,6 +22,7 @@
 // Work split: a block owns 16*RT weight rows; its waves split K into chunks of
 // 64*VEC k; partial 16x16 tiles are summed through LDS; the epilogue
 // multiplies by gamma * max(absmax, eps) / 127.
+#include "bitlinear.h"
 #include "bl_internal.h"
 
 namespace bl {
@@ -177,36 +178,95 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
 // out in LDS so that the matching B operand of slice j is one 16-byte read:
 // within every 64-byte group the 4x4 dword matrix (word v, slice j) is
 // stored transposed.  The token's sum of q over K, which removes the code
-// offset (c = t + 1), is taken once while staging.
+// offset (c = t + 1), is taken once per block.
 //
 // Each wave walks its chunks with P loads in flight: the load of chunk i+P
 // is issued as soon as chunk i is consumed.
-template <int P>
-__global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__ packed,
-                                                    const float* __restrict__ gamma,
-                                                    const int8_t* __restrict__ xq,
-                                                    const float* __restrict__ absmax, int T,
-                                                    int N, int K, float* __restrict__ y,
-                                                    int32_t* __restrict__ acc_out) {
+//
+// One launch serves a group of independent problems (blocks are dealt out
+// problem by problem).  MODE selects the activation input: kInt8 reads the
+// int8 activations and absmax of a separate act-quant step; kBf16 / kF32
+// read raw activations and quantise them in the block (step A1 fused): every
+// block derives the token absmax itself, scales, rounds half to even and
+// clips exactly as the act-quant kernel does, and the problem's first block
+// also stores the int8 activations and absmax.
+enum PipeMode { kInt8 = 0, kBf16 = 1, kF32 = 2 };
+
+struct PipeProblem {
+  const uint32_t* packed;
+  const float* gamma;
+  const void* x;          // int8 activations (kInt8) or raw bf16 / f32
+  const float* absmax;    // kInt8: per-token absmax from act-quant
+  float* y;
+  int32_t* acc;           // optional exact sums
+  int8_t* xq_out;         // fused modes: quantised activations out (first block)
+  float* absmax_out;      // fused modes: absmax out (first block)
+  int N, K, block0;
+};
+constexpr int kMaxGroup = 8;
+struct PipeGroup {
+  PipeProblem p[kMaxGroup];
+  int count, T;
+};
+
+// DPP row reductions (16 lanes), then the four rows through readlane.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// element e of a raw 16-byte activation vector, widened exactly to binary32
+template <int MODE>
+__device__ __forceinline__ float raw_elem(const uint4& v, int e) {
+  if constexpr (MODE == kBf16) {
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+  }
+}
+
+template <int P, int MODE>
+__global__ __launch_bounds__(1024) void k_gemv_pipe(const PipeGroup grp) {
   extern __shared__ __align__(16) unsigned char smem[];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < grp.count && (int)blockIdx.x >= grp.p[i].block0) pi = i;
+  const PipeProblem& pr = grp.p[pi];
+  const int T = grp.T, N = pr.N, K = pr.K;
+
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qg = lane >> 4, r = lane & 15;
   const int K16 = K >> 4;
   const int nchunks = K16 >> 4;                     // 16 words (256 k) per chunk
-  const int n0 = blockIdx.x * 16;
+  const int n0 = ((int)blockIdx.x - pr.block0) * 16;
   // LDS: [256 B zeros][T x (K + 16) activation bytes, transposed per 64 B]
-  //      [T row sums][partials].  The 16-byte pad per token spreads the
-  //      tokens of one B-operand read over different banks.
+  //      [16 row sums][16 absmax bits][partials].  The 16-byte pad per token
+  //      spreads the tokens of one B-operand read over different banks.
   const int xs = (K >> 2) + 4;                      // token stride in dwords
   uint32_t* zero = reinterpret_cast<uint32_t*>(smem);
   uint32_t* xl = zero + 64;
   int* rsum = reinterpret_cast<int*>(xl + T * xs);
-  int* red = rsum + 16;
+  int* amax = rsum + 16;
+  int* red = amax + 16;
 
   int n = n0 + r;
   n = n < N ? n : N - 1;
-  const uint4* wrow = reinterpret_cast<const uint4*>(packed + (int64_t)n * K16) + qg;
+  const uint4* wrow = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
   const int my = (nchunks - wave + nwaves - 1) / nwaves;   // chunks of this wave (>= 1)
   auto chunk_of = [&](int i) { return wave + (i < my ? i : my - 1) * nwaves; };
 
@@ -214,8 +274,9 @@ __global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__
   // before the main loop (the activations) is issued before the weight
   // prefetch, which then stays in flight through the staging and the barrier.
   constexpr int kStage = kGemvStage;
-  const int per_tok = K >> 4, nvec = T * per_tok;
-  const uint4* src = reinterpret_cast<const uint4*>(xq);
+  constexpr int E = MODE == kInt8 ? 16 : MODE == kBf16 ? 8 : 4;  // elements per 16 bytes
+  const int per_tok = K / E, nvec = T * per_tok;
+  const uint4* src = reinterpret_cast<const uint4*>(pr.x);
   uint4 sv[kStage];
 #pragma unroll
   for (int m = 0; m < kStage; ++m) {
@@ -223,28 +284,114 @@ __global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__
     sv[m] = src[i < nvec ? i : nvec - 1];
   }
   // the epilogue's scalars, fetched early so their latency hides under the loop
-  const float g = gamma[0];
-  const float am = absmax[threadIdx.x < 16 * T ? (threadIdx.x >> 4) : 0];
+  const float g = pr.gamma[0];
+  float am = 0.0f;
+  if constexpr (MODE == kInt8) am = pr.absmax[threadIdx.x < 16 * T ? (threadIdx.x >> 4) : 0];
 
   uint4 buf[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) buf[j] = wrow[(size_t)chunk_of(j) * 4];
 
   if (threadIdx.x < 64) zero[threadIdx.x] = 0u;
-  if (threadIdx.x < 16) rsum[threadIdx.x] = 0;
-  // Vector i (16 bytes) is word v = i & 3 of its 64-byte group; its dword
-  // (v, j) is stored at position (j, v) of the group.
-  auto stage_store = [&](int i, const uint4& v) {
-    const int t = i / per_tok, iv = i - t * per_tok;
-    uint32_t* gp = xl + t * xs + (iv >> 2) * 16 + (iv & 3);
-    gp[0] = v.x; gp[4] = v.y; gp[8] = v.z; gp[12] = v.w;
+  if (threadIdx.x < 32) rsum[threadIdx.x] = 0;      // row sums and absmax bits
+  // 16 int8 activations = word v = iv & 3 of a 64-byte group; dword (v, j)
+  // of the group is stored at position (j, v).
+  auto xq_dword = [&](int t, int iv, int j) -> uint32_t* {
+    return xl + t * xs + (iv >> 2) * 16 + (iv & 3) + 4 * j;
   };
+  if constexpr (MODE == kInt8) {
 #pragma unroll
-  for (int m = 0; m < kStage; ++m) {
-    const int i = threadIdx.x + m * blockDim.x;
-    if (i < nvec) stage_store(i, sv[m]);
+    for (int m = 0; m < kStage; ++m) {
+      const int i = threadIdx.x + m * blockDim.x;
+      if (i < nvec) {
+        const int t = i / per_tok, iv = i - t * per_tok;
+        *xq_dword(t, iv, 0) = sv[m].x; *xq_dword(t, iv, 1) = sv[m].y;
+        *xq_dword(t, iv, 2) = sv[m].z; *xq_dword(t, iv, 3) = sv[m].w;
+      }
+    }
+    // (the host guarantees nvec <= kStage * blockDim: one round covers it)
+  } else {
+    // Step A1 in the block: absmax per token (T <= 4) ...
+    int tmax[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int i = threadIdx.x + m * blockDim.x;
+      if (i < nvec) {
+        const int t = i / per_tok;
+        int mx = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          mx = max(mx, (int)(__float_as_uint(raw_elem<MODE>(sv[m], e)) & 0x7fffffffu));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          if (t == tt) tmax[tt] = max(tmax[tt], mx);
+      }
+    }
+    __syncthreads();                                // amax cleared
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt < T) {
+        const int wm = wave_max_nonneg(tmax[tt]);   // non-negative bit patterns order as values
+        if (lane == 0) atomicMax(&amax[tt], wm);
+      }
+    }
+    __syncthreads();
+    // ... then scale, round half to even, clip, and lay out as int8
+    float sc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      sc[tt] = tt < T ? kQb / fmaxf(__uint_as_float((uint32_t)amax[tt]), kEps) : 0.0f;
+    int tsum[4] = {0, 0, 0, 0};
+    const bool first = n0 == 0;
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int i = threadIdx.x + m * blockDim.x;
+      if (i < nvec) {
+        const int t = i / per_tok, ie = i - t * per_tok;   // vector index within the token
+        float s = sc[0];
+#pragma unroll
+        for (int tt = 1; tt < 4; ++tt)
+          if (t == tt) s = sc[tt];
+        uint32_t d[E / 4];
+        int part = 0;
+#pragma unroll
+        for (int w = 0; w < E / 4; ++w) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float v = raw_elem<MODE>(sv[m], 4 * w + b) * s;   // one binary32 product
+            const int q = (int)fminf(fmaxf(rintf(v), -kQb), kQb);
+            part += q;
+            word |= (uint32_t)(q & 0xff) << (8 * b);
+          }
+          d[w] = word;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          if (t == tt) tsum[tt] += part;
+        // E elements start at k = ie * E: int8 vector iv, first dword j0
+        const int k0 = ie * E, iv = k0 >> 4, j0 = (k0 & 15) >> 2;
+#pragma unroll
+        for (int w = 0; w < E / 4; ++w) *xq_dword(t, iv, j0 + w) = d[w];
+        if (first && pr.xq_out) {
+          int8_t* dst = pr.xq_out + (int64_t)t * K + k0;
+          if constexpr (E == 8)
+            *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[E / 4 - 1]);
+          else
+            *reinterpret_cast<uint32_t*>(dst) = d[0];
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt < T) {
+        const int ws = wave_sum_i(tsum[tt]);
+        if (lane == 0) atomicAdd(&rsum[tt], ws);
+      }
+    }
+    if (first && pr.absmax_out && threadIdx.x < T)
+      pr.absmax_out[threadIdx.x] = __uint_as_float((uint32_t)amax[threadIdx.x]);
   }
-  // (the host guarantees nvec <= kStage * blockDim: one round covers it)
   __syncthreads();
 
   // B operand address: lanes of tokens past T read the zero block (stride 0)
@@ -299,24 +446,21 @@ __global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__
   for (int v = 0; v < 4; ++v)
     red[(wave * 4 + v) * 64 + lane] = a1[v] + (a4[v] >> 2) + (a16[v] >> 4);
 
-  // sum of q per token (removes the code offset), read back from LDS
-  for (int t = 0; t < T; ++t) {
-    const uint4* xt = reinterpret_cast<const uint4*>(xl + t * xs);
-    int part = 0;
-    for (int i = threadIdx.x; i < (K >> 4); i += blockDim.x) {
-      const uint4 v = xt[i];
-      part = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, part, false);
-      part = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, part, false);
-      part = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, part, false);
-      part = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, part, false);
+  if constexpr (MODE == kInt8) {
+    // sum of q per token (removes the code offset), read back from LDS
+    for (int t = 0; t < T; ++t) {
+      const uint4* xt = reinterpret_cast<const uint4*>(xl + t * xs);
+      int part = 0;
+      for (int i = threadIdx.x; i < (K >> 4); i += blockDim.x) {
+        const uint4 v = xt[i];
+        part = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, part, false);
+        part = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, part, false);
+        part = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, part, false);
+        part = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, part, false);
+      }
+      part = wave_sum_i(part);
+      if (lane == 0) atomicAdd(&rsum[t], part);
     }
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
-    part += __shfl_xor(part, 8);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (lane == 0) atomicAdd(&rsum[t], part);
   }
   __syncthreads();
   // 16 * T <= 256 outputs and blockDim >= 64: thread idx < 16 * T owns one
@@ -328,8 +472,11 @@ __global__ __launch_bounds__(1024) void k_gemv_pipe(const uint32_t* __restrict__
     int sum = -rsum[tl];
     for (int wv = 0; wv < nwaves; ++wv) sum += red[(wv * 4 + slot) * 64 + ln];
     const int64_t o = (int64_t)tl * N + nn;
-    if (acc_out) acc_out[o] = sum;
-    y[o] = (float)sum * out_scale(g, idx == (int)threadIdx.x ? am : absmax[tl]);
+    if (pr.acc) pr.acc[o] = sum;
+    float a_t;
+    if constexpr (MODE == kInt8) a_t = idx == (int)threadIdx.x ? am : pr.absmax[tl];
+    else a_t = __uint_as_float((uint32_t)amax[tl]);
+    pr.y[o] = (float)sum * out_scale(g, a_t);
   }
 }
 
@@ -387,36 +534,98 @@ void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
 // long-running waves (each streams many chunks); small grids need K split over
 // more waves to have enough loads in flight.  Aim for about
 // BL_GEMV_PIPE_WAVES waves in total with at least BL_GEMV_PIPE_MINCPW chunks
-// each, and enough threads to stage T*K bytes in one round.
-int pipe_waves(int64_t t, int64_t n, int64_t k) {
+// each, and enough threads to stage the activations in one round
+// (elems_per_vec elements per 16-byte vector).
+int pipe_waves(int64_t t, int64_t blocks, int64_t k, int elems_per_vec) {
   const int nchunks = (int)(k / 256);
-  const int64_t blocks = (n + 15) / 16;
   int nw = (int)((BL_GEMV_PIPE_WAVES + blocks - 1) / blocks);
   int cap = nchunks / BL_GEMV_PIPE_MINCPW;
   if (cap < 1) cap = 1;
   if (nw > cap) nw = cap;
-  const int64_t vecs = t * k / 16;
+  const int64_t vecs = t * k / elems_per_vec;
   const int need = (int)((vecs + 64 * kGemvStage - 1) / (64 * kGemvStage));
   if (nw < need) nw = need;
   if (nw > nchunks) nw = nchunks;
   return nw;
 }
 
+bool pipe_shape_ok(int64_t t, int64_t k, int elems_per_vec, int max_t) {
+  if (!(t <= max_t && (k % 256) == 0 && t * k <= BL_GEMV_PIPE_XLDS)) return false;
+  const int nw = pipe_waves(t, 1, k, elems_per_vec);  // the fewest-waves case bounds staging
+  return nw <= 16 && t * k / elems_per_vec <= (int64_t)16 * 64 * kGemvStage;
+}
+
 bool pipe_ok(int64_t t, int64_t n, int64_t k, const void* packed, const void* xq) {
-  if (!(t <= 16 && (k % 256) == 0 && t * k <= BL_GEMV_PIPE_XLDS &&
-        (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
-        (reinterpret_cast<uintptr_t>(xq) % 16) == 0))
-    return false;
-  const int nw = pipe_waves(t, n, k);
-  return nw <= 16 && t * k / 16 <= (int64_t)nw * 64 * kGemvStage;
+  (void)n;
+  return pipe_shape_ok(t, k, 16, 16) && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
+         (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
+}
+
+size_t pipe_lds(int64_t t, int64_t k, int nw) {
+  return 256 + (size_t)t * (k + 16) + 32 * sizeof(int) + (size_t)nw * 4 * 64 * sizeof(int);
+}
+
+template <int MODE>
+hipError_t run_pipe_group(const PipeGroup& grp, int blocks, int nw, size_t lds,
+                          hipStream_t stream) {
+  k_gemv_pipe<BL_GEMV_PIPE_P, MODE><<<blocks, nw * 64, lds, stream>>>(grp);
+  return hipGetLastError();
 }
 
 void run_pipe(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
               int t, int n, int k, float* y, int32_t* acc, hipStream_t stream) {
-  const int nw = pipe_waves(t, n, k);
-  const size_t lds = 256 + (size_t)t * (k + 16) + 16 * sizeof(int) + (size_t)nw * 4 * 64 * sizeof(int);
-  k_gemv_pipe<BL_GEMV_PIPE_P><<<(n + 15) / 16, nw * 64, lds, stream>>>(
-      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc);
+  PipeGroup grp = {};
+  grp.count = 1;
+  grp.T = t;
+  grp.p[0] = PipeProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
+                         nullptr, nullptr, n, k, 0};
+  const int blocks = (n + 15) / 16;
+  int nw = pipe_waves(t, blocks, k, 16);
+  if (nw * 64 * kGemvStage < (int64_t)t * k / 16) nw = (int)((t * k / 16 + 64 * kGemvStage - 1) / (64 * kGemvStage));
+  run_pipe_group<kInt8>(grp, blocks, nw, pipe_lds(t, k, nw), stream);
+}
+
+hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int bf16,
+                               hipStream_t stream) {
+  const int E = bf16 ? 8 : 4;
+  bool fused = count <= kMaxGroup;
+  for (int i = 0; fused && i < count; ++i) {
+    fused = pipe_shape_ok(t, probs[i].K, E, 4) &&
+            (reinterpret_cast<uintptr_t>(probs[i].x) % 16) == 0 &&
+            (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
+  }
+  if (!fused) {  // act-quant then forward, problem by problem
+    for (int i = 0; i < count; ++i) {
+      const bl_linear& q = probs[i];
+      hipError_t e = launch_quant(q.x, bf16, t, q.K, q.xq, q.absmax, nullptr, stream);
+      if (e != hipSuccess) return e;
+      e = launch_gemv(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  PipeGroup grp = {};
+  grp.count = count;
+  grp.T = (int)t;
+  int blocks = 0;
+  int64_t kmax = 0;
+  for (int i = 0; i < count; ++i) {
+    const bl_linear& q = probs[i];
+    grp.p[i] = PipeProblem{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr,
+                           q.y, q.acc, q.xq, q.absmax, (int)q.N, (int)q.K, blocks};
+    blocks += (int)((q.N + 15) / 16);
+    if (q.K > kmax) kmax = q.K;
+  }
+  // one block shape for the group: waves for the widest K, staging for every K
+  int nw = pipe_waves(t, blocks, kmax, E);
+  for (int i = 0; i < count; ++i) {
+    const int need = (int)((t * probs[i].K / E + 64 * kGemvStage - 1) / (64 * kGemvStage));
+    if (nw < need) nw = need;
+  }
+  if (nw > 16) nw = 16;
+  const size_t lds = pipe_lds(t, kmax, nw);
+  return bf16 ? run_pipe_group<kBf16>(grp, blocks, nw, lds, stream)
+              : run_pipe_group<kF32>(grp, blocks, nw, lds, stream);
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,

@@ -161,6 +161,35 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
                            const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
                            int32_t* acc, int algo, void* stream);
 
+/* One problem of bitlinear_linear_grouped: a whole BitLinear forward. */
+typedef struct bl_linear {
+  const void* x;          /* [T, K] activations, dtype of the call, 16-byte aligned */
+  const uint8_t* packed;  /* [N, K/4] from bitlinear_pack_weights, 16-byte aligned */
+  const float* gamma;     /* [1] from bitlinear_pack_weights */
+  int64_t N, K;           /* 1 <= N <= 2^26, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0 */
+  float* y;               /* [T, N] output, 4-byte aligned */
+  int8_t* xq;             /* [T, K] int8 activations (written), 16-byte aligned */
+  float* absmax;          /* [T] token absmax (written) */
+  int32_t* acc;           /* [T, N] exact int32 sums, or NULL */
+} bl_linear;
+
+/* Steps A1-A3 for `count` (1..8) independent BitLinear problems that share T
+ * and the activation dtype: the same results as bitlinear_quant_act followed
+ * by bitlinear_forward on each problem (same operations, same rounding), for
+ * callers that run several projections of one layer back to back (e.g. the
+ * query/key/value or gate/up projections of a decoder layer).  For decode
+ * shapes (T <= 4, K % 256 == 0, T*K <= 32768) one kernel does all of it:
+ * each block quantises the activations it needs in LDS, then streams its
+ * weight rows; otherwise the steps run per problem.
+ *
+ *   problems  HOST array of `count` descriptors (read during the call only).
+ *   T         1 <= T <= 2^24 tokens, the same for every problem.
+ *   x_dtype   BL_F32 or BL_BF16.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_ARG
+ * (count out of range), BL_ERR_HIP. */
+int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

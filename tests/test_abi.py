@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for name in names:
         assert hasattr(lib, name), name
 
@@ -130,3 +130,24 @@ def test_binding_raises(built_lib):
     with pytest.raises(binding.BitLinearError) as ei:
         binding._check(BL_ERR_SHAPE)
     assert ei.value.status == BL_ERR_SHAPE
+
+
+def test_linear_grouped_errors(lib):
+    from bitlinear_w1_a8_amd.binding import BlLinear
+    f = lib.bitlinear_linear_grouped
+    good = BlLinear(A16, A16, A16, 32, 256, A16, A16, A16, None)
+    arr = (BlLinear * 9)(*([good] * 9))
+    assert f(None, 1, 1, 1, None) == BL_ERR_NULL
+    assert f(arr, 0, 1, 1, None) == BL_ERR_ARG
+    assert f(arr, 9, 1, 1, None) == BL_ERR_ARG
+    assert f(arr, 2, 1, 3, None) == BL_ERR_DTYPE
+    assert f(arr, 2, 0, 1, None) == BL_ERR_SHAPE
+    bad = (BlLinear * 2)(good, BlLinear(A16, A16, A16, 32, 256, A16, None, A16, None))
+    assert f(bad, 2, 1, 1, None) == BL_ERR_NULL
+    assert "problem 1" in _err(lib)
+    bad = (BlLinear * 2)(good, BlLinear(A16, A16, A16, 32, 250, A16, A16, A16, None))
+    assert f(bad, 2, 1, 1, None) == BL_ERR_SHAPE
+    bad = (BlLinear * 2)(good, BlLinear(A16 + 2, A16, A16, 32, 256, A16, A16, A16, None))
+    assert f(bad, 2, 1, 1, None) == BL_ERR_ALIGN
+    bad = (BlLinear * 1)(BlLinear(A16, A16, A16, 0, 256, A16, A16, A16, None))
+    assert f(bad, 1, 1, 1, None) == BL_ERR_SHAPE

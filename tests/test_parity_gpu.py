@@ -294,3 +294,48 @@ def test_workload_full_size(bl, widx, mi):
     if widx in (2, 5):
         # the ternary zero fraction of Gaussian weights, about 31%
         assert abs(float(np.mean(tern == 0)) - 0.3101) < 0.005
+
+
+# ------------------------------------------------------------------ grouped A1-A3
+
+GROUPS = {
+    "layer_qkv_t1_bf16": (1, "bf16", [(2560, 2560), (2560, 640), (2560, 640)]),
+    "layer_gateup_t1_bf16": (1, "bf16", [(2560, 6912), (2560, 6912)]),
+    "layer_down_t1_bf16": (1, "bf16", [(6912, 2560)]),
+    "t4_f32_ragged": (4, "f32", [(256, 37), (512, 100), (768, 1)]),
+    "t3_bf16_mixed_k": (3, "bf16", [(2048, 50), (256, 17)]),
+    "t2_k28672": (2, "bf16", [(28672, 64)]),
+    "eight_problems": (2, "bf16", [(256 * (i + 1), 16 * (i + 1) + 3) for i in range(8)]),
+    "fallback_t8": (8, "bf16", [(2560, 200), (512, 33)]),
+    "fallback_k_not_256": (2, "f32", [(48, 20), (256, 16)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPS))
+def test_linear_grouped(bl, name):
+    t, dtype, shapes = GROUPS[name]
+    xs, ws, refs = [], [], []
+    for i, (k, n) in enumerate(shapes):
+        w = wl.latent_weights(n, k, 0.02, 500 + 7 * i + k)
+        x = wl.activations_student_t(t, k, 4, 600 + 7 * i + k)
+        if t > 2:
+            x[1] = 0.0                                  # an all-zero token
+        packed, gamma, _, gamma_ref = check_pack(bl, w)
+        tern = oracle.ternarize(w, gamma_ref)
+        if dtype == "bf16":
+            bits = wl.bf16_bits(x)
+            xs.append(dev_bf16(bits))
+            q_ref, a_ref, _ = oracle.quant_act(bits)
+        else:
+            xs.append(dev(x))
+            q_ref, a_ref, _ = oracle.quant_act(x)
+        ws.append((packed, gamma))
+        refs.append((tern, q_ref, a_ref, gamma_ref))
+    outs = bl.linear_grouped(xs, ws, want_acc=True)
+    for (y, xq, absmax, acc), (tern, q_ref, a_ref, gamma_ref) in zip(outs, refs):
+        assert np.array_equal(host(xq), q_ref)
+        assert np.array_equal(host(absmax).view(np.uint32), a_ref.view(np.uint32))
+        acc_ref = oracle.contract(q_ref, tern)
+        a = host(acc)
+        assert int(np.count_nonzero(a != acc_ref)) == 0
+        check_y(host(y), acc_ref, gamma_ref, a_ref)
