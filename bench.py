@@ -362,7 +362,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": committed_traffic("gemv.hip", "decode_fused_2b_t1"),
-                "kernel": "k_gemv_pipe (act-quant fused into the decode GEMV), T=1",
+                "kernel": "k_gemv_dec (act-quant fused into the decode GEMV), T=1",
                 "avg_launch_us": round(fused_us, 3),
                 "algorithmic_bytes_per_launch": int(fused_launch_bytes)}
 

@@ -20,6 +20,8 @@
 // steps of 128 with the activation tile double-buffered in LDS and the next
 // tile's loads in flight during the current tile's MFMAs.  Tiles are ordered
 // so that consecutive tiles of one XCD share activation rows in its L2.
+#include <type_traits>
+
 #include "bl_internal.h"
 
 namespace bl {
@@ -207,32 +209,64 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ 
 // s_waitcnt vmcnt(N) with the other counters left alone (N < 16)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // lgkmcnt 15, expcnt 7, vmcnt N
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // vmcnt N (bits 3:0 and 15:14), expcnt 7, lgkmcnt 15: only loads are waited on
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
-// One static LDS object per pipeline stage: the compiler can then tell that
-// the loads landing in one stage do not alias reads of another, and does not
-// drain every outstanding load before each LDS read.
-template <int WAVES_M, int WMF, int WNF, int STAGES>
-__global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restrict__ packed,
-                                                       const float* __restrict__ gamma,
-                                                       const int8_t* __restrict__ xq,
-                                                       const float* __restrict__ absmax, int T,
-                                                       int N, int K, float* __restrict__ y,
-                                                       int32_t* __restrict__ acc_out) {
-  static_assert(STAGES == 3, "the unrolled step sequence below assumes three stages");
-  constexpr int WAVES_N = 4 / WAVES_M;
+// Each stage is its own static LDS object and every step below names its
+// stages at compile time, so the compiler can tell that the loads landing in
+// one stage do not alias reads of another and does not drain every
+// outstanding load before each LDS read (one array indexed by stage is not
+// enough for that).
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
+                                                         const float* __restrict__ gamma,
+                                                         const int8_t* __restrict__ xq,
+                                                         const float* __restrict__ absmax,
+                                                         int T, int N, int K,
+                                                         float* __restrict__ y,
+                                                         int32_t* __restrict__ acc_out) {
+  static_assert(STAGES == 3 || STAGES == 4, "three or four stages");
+  constexpr int NT = WAVES * 64;
+  constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
   constexpr int kABuf = BM * BK, kBBuf = BN * (BK / 4);   // bytes per stage
-  constexpr int kAChunks = BM / 8 / 4, kBChunks = BN / 32 / 4;  // 1 KiB loads per wave
-  static_assert(kBChunks >= 1, "BN must be a multiple of 128");
+  constexpr int kAChunks = BM / 8 / WAVES, kBChunks = BN / 32 / WAVES;  // 1 KiB loads per wave
+  static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the wave count");
   __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf], A2[kABuf];
+  __shared__ __align__(16) unsigned char A3[STAGES > 3 ? kABuf : 16];
   __shared__ __align__(16) unsigned char B0[kBBuf], B1[kBBuf], B2[kBBuf];
+  __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
+  auto abuf = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return A0;
+    else if constexpr (S == 1) return A1;
+    else if constexpr (S == 2) return A2;
+    else return A3;
+  };
+  auto bbuf = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return B0;
+    else if constexpr (S == 1) return B1;
+    else if constexpr (S == 2) return B2;
+    else return B3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restric
   // per-token output scale first: its loads retire before the pipeline starts
   {
     const float g = gamma[0];
-    for (int r = tid; r < BM; r += kThreads) {
+    for (int r = tid; r < BM; r += NT) {
       const int tok = m0 + r;
       scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
     }
@@ -296,22 +330,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restric
 
   const int nk = K / BK;
   constexpr int kLoads = kAChunks + kBChunks;     // this wave's loads per tile
-  static_assert(kLoads < 16, "vmcnt immediate");
+  static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
-  issue(0, A0, B0);
-  issue(nk > 1 ? 1 : 0, A1, B1);                  // (a harmless repeat when nk == 1)
-  wait_vm<kLoads>();                              // tile 0 landed, tile 1 in flight
-  __syncthreads();
+  // prologue: tiles 0 .. STAGES-2 (repeats of the last tile when K is short)
+  issue(0, abuf(I0{}), bbuf(I0{}));
+  issue(nk > 1 ? 1 : 0, abuf(I1{}), bbuf(I1{}));
+  if constexpr (STAGES == 4) issue(nk > 2 ? 2 : nk - 1, abuf(I2{}), bbuf(I2{}));
+  // tile 0 landed (the rest stays in flight) and the scale writes are done;
+  // a fence-free barrier, as a fence would wait for every load
+  wait_vm_lgkm0<kLoads * (STAGES - 2)>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 
   const int h = lane >> 5, m = lane & 31;
   const int aswz = (m >> 1) & 7;
-  // one K step on stage (As, Bs); refill stage (An, Bn) with tile kt + 2
-  auto step = [&](int kt, const unsigned char* As, const unsigned char* Bs, unsigned char* An,
-                  unsigned char* Bn) {
-    const bool refill = kt + 2 < nk;
-    if (refill) issue(kt + 2, An, Bn);
-    const unsigned char* At = As + (wm * 32 * WMF + m) * BK;
-    const unsigned char* Bt = Bs + (wn * 32 * WNF + m) * (BK / 4) + 16 * h;
+  // One K step on stage S; refill stage (S + STAGES - 1) % STAGES, which the
+  // previous step finished reading, with tile kt + STAGES - 1.
+  auto step = [&](auto stage_c, int kt) {
+    constexpr int S = decltype(stage_c)::value;
+    using R = std::integral_constant<int, (S + STAGES - 1) % STAGES>;
+    // unconditional (no branch, so no join where the compiler would drain
+    // every load): past the end it re-fetches the last tile into a stage that
+    // is never read again
+    issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, abuf(R{}), bbuf(R{}));
+    const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
+    const unsigned char* Bt = bbuf(stage_c) + (wn * 32 * WNF + m) * (BK / 4) + 16 * h;
     uint4 bw[WNF];
 #pragma unroll
     for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * (BK / 4));
@@ -340,17 +384,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restric
     // by the barrier.  A plain s_barrier, not __syncthreads(): the latter's
     // release fence would also wait for the refill issued above.  The only
     // LDS writes in the loop are these loads, which the wait covers.
-    if (refill) wait_vm<kLoads>();
-    else wait_vm<0>();
+    wait_vm<kLoads * (STAGES - 2)>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < nk; kt += 3) {
-    step(kt, A0, B0, A2, B2);
-    if (kt + 1 < nk) step(kt + 1, A1, B1, A0, B0);
-    if (kt + 2 < nk) step(kt + 2, A2, B2, A1, B1);
+  // whole stage cycles without conditionals (branch joins make the compiler
+  // drain every outstanding load), then the remaining steps
+  int kt = 0;
+  for (; kt + STAGES <= nk; kt += STAGES) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    step(I2{}, kt + 2);
+    if constexpr (STAGES == 4) step(I3{}, kt + 3);
   }
+  if (kt < nk) step(I0{}, kt);
+  if (kt + 1 < nk) step(I1{}, kt + 1);
+  if constexpr (STAGES == 4)
+    if (kt + 2 < nk) step(I2{}, kt + 2);
+  wait_vm<0>();   // no load may land in LDS after the block has finished
 
 #pragma unroll
   for (int i = 0; i < WMF; ++i) {
@@ -373,14 +425,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(const uint32_t* __restric
   }
 }
 
-template <int WAVES_M, int WMF, int WNF, int STAGES>
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES>
 hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
                    hipStream_t stream) {
-  constexpr int BM = WAVES_M * 32 * WMF, BN = (4 / WAVES_M) * 32 * WNF;
+  constexpr int BM = WAVES_M * 32 * WMF, BN = (WAVES / WAVES_M) * 32 * WNF;
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  auto kern = k_gemm_lds<WAVES_M, WMF, WNF, STAGES>;
-  kern<<<dim3((unsigned)tiles), kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed),
+  auto kern = k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES>;
+  kern<<<dim3((unsigned)tiles), WAVES * 64, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed),
                                                          gamma, xq, absmax, (int)t, (int)n,
                                                          (int)k, y, acc);
   return hipGetLastError();
@@ -418,19 +470,29 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_STAGES
 #define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
 #endif
+#ifndef BL_GEMM_WAVES
+#define BL_GEMM_WAVES 8             // waves per block of the LDS-direct kernel
+#endif
 #ifndef BL_GEMM_WAVES_M
-#define BL_GEMM_WAVES_M 1           // 1: 128 x 512 block tiles; 2: 256 x 256
+#define BL_GEMM_WAVES_M 1           // waves along M (the rest along N)
+#endif
+#ifndef BL_GEMM_WMF
+#define BL_GEMM_WMF 4               // 32-row fragments per wave
+#endif
+#ifndef BL_GEMM_WNF
+#define BL_GEMM_WNF 2               // 32-column fragments per wave
 #endif
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
-  constexpr int kLdsBM = BL_GEMM_WAVES_M * 128, kLdsBN = (4 / BL_GEMM_WAVES_M) * 128;
+  constexpr int kLdsBM = BL_GEMM_WAVES_M * 32 * BL_GEMM_WMF;
+  constexpr int kLdsBN = (BL_GEMM_WAVES / BL_GEMM_WAVES_M) * 32 * BL_GEMM_WNF;
   const int64_t lds_tiles = ((n + kLdsBN - 1) / kLdsBN) * ((t + kLdsBM - 1) / kLdsBM);
   if (k % BK == 0 && lds_tiles >= BL_GEMM_LDS_MIN_TILES && t * k < (int64_t(1) << 31) &&
       n * (k / 16) < (int64_t(1) << 31))
-    return run_lds<BL_GEMM_WAVES_M, 4, 4, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y,
-                                                          acc, stream);
+    return run_lds<BL_GEMM_WAVES, BL_GEMM_WAVES_M, BL_GEMM_WMF, BL_GEMM_WNF, BL_GEMM_STAGES>(
+        packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
   if (big >= BL_GEMM_BIG_MIN_TILES)
     return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);

@@ -29,7 +29,6 @@ namespace bl {
 namespace {
 
 constexpr int kGemvTokens = 64;   // tokens per launch (4 MFMA column tiles)
-constexpr int kGemvStage = 8;     // 16-byte activation vectors staged per thread
 
 template <int VEC, int RT, int NTT, int U>
 __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packed,
@@ -166,48 +165,58 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
   }
 }
 
-// Software-pipelined variant for T <= 16 and K % 256 == 0 (the decode case).
+// Decode kernel for T <= 16 and K % 256 == 0 (T <= 4 with step A1 fused).
 //
-// Per chunk (256 k of a 16-row tile) a lane holds four packed words w_v.
-// Instead of shifting every 2-bit field down, three of the four fields are
-// only masked: w & 0x03030303, w & 0x0C0C0C0C and w & 0x30303030 hold c,
-// 4c and 16c in each byte (all still non-negative int8), and only the top
-// field needs a shift.  Slice j of the four words forms one MFMA operand, and
-// each scale accumulates separately; the exact sums are divided by 4 and 16
-// once at the end (they are exact multiples).  The activation bytes are laid
-// out in LDS so that the matching B operand of slice j is one 16-byte read:
-// within every 64-byte group the 4x4 dword matrix (word v, slice j) is
-// stored transposed.  The token's sum of q over K, which removes the code
-// offset (c = t + 1), is taken once per block.
+// Unpacking: per chunk (256 k of a 16-row tile) a lane holds four packed
+// words.  Three of the four 2-bit fields are only masked: w & 0x03030303,
+// w & 0x0C0C0C0C and w & 0x30303030 hold c, 4c and 16c in each byte (all
+// non-negative int8), and only the top field needs a shift.  Slice j of the
+// four words is one MFMA operand; each scale accumulates separately and the
+// exact sums are divided by 4 and 16 at the end (they are exact multiples).
+// The B operand that matches slice j is dword j of each of the four 16-byte
+// activation vectors that cover the lane's 64 k.
 //
-// Each wave walks its chunks with P loads in flight: the load of chunk i+P
-// is issued as soon as chunk i is consumed.
-//
-// One launch serves a group of independent problems (blocks are dealt out
-// problem by problem).  MODE selects the activation input: kInt8 reads the
-// int8 activations and absmax of a separate act-quant step; kBf16 / kF32
-// read raw activations and quantise them in the block (step A1 fused): every
-// block derives the token absmax itself, scales, rounds half to even and
-// clips exactly as the act-quant kernel does, and the problem's first block
-// also stores the int8 activations and absmax.
-enum PipeMode { kInt8 = 0, kBf16 = 1, kF32 = 2 };
+// A decode launch moves a few MB, so its time is mostly latency:
+//  - a block's problem is blockIdx.y, known before the first load, and all
+//    arguments arrive in one batch;
+//  - the activations go from global memory straight into LDS (no registers
+//    held while the weights are in flight), issued before the weights;
+//  - wave w owns a contiguous run of at most CPW chunks of its 16 rows and
+//    issues all of their loads at once: one memory round trip per wave;
+//  - the block barriers wait for LDS traffic only, so the weight loads stay
+//    in flight while the activations land (and, with step A1 fused, while
+//    they are quantised: every block derives the token absmax itself,
+//    scales, rounds half to even and clips exactly as the act-quant kernel
+//    does, and block 0 of each problem stores the int8 activations and
+//    absmax);
+//  - each wave removes the code offset (c = t + 1) of its own k run with the
+//    sum of q over that run, computed while its loads are in flight; the
+//    waves add their partial tiles in LDS and the last one to finish writes
+//    the block's outputs.
+enum DecMode { kInt8 = 0, kBf16 = 1, kF32 = 2 };
 
-struct PipeProblem {
+struct DecProblem {
   const uint32_t* packed;
   const float* gamma;
   const void* x;          // int8 activations (kInt8) or raw bf16 / f32
   const float* absmax;    // kInt8: per-token absmax from act-quant
   float* y;
   int32_t* acc;           // optional exact sums
-  int8_t* xq_out;         // fused modes: quantised activations out (first block)
-  float* absmax_out;      // fused modes: absmax out (first block)
-  int N, K, block0;
+  int8_t* xq_out;         // fused modes: quantised activations out (block 0)
+  float* absmax_out;      // fused modes: absmax out (block 0)
+  int N, K;
+  int per;                // chunks per wave: ceil((K / 256) / nw) <= CPW
 };
 constexpr int kMaxGroup = 8;
-struct PipeGroup {
-  PipeProblem p[kMaxGroup];
-  int count, T;
+struct DecGroup {
+  DecProblem p[kMaxGroup];
+  int T, nw;              // tokens; waves per block (the block has 64 * nw threads)
 };
+
+// LDS header of the decode kernel: 64 zero bytes, the 16 x 16 int32 tile
+// (token-major), the finishing counter and 16 absmax bit patterns.
+constexpr int kDecHead = 64 + 256 * 4 + 4 + 16 * 4 + 12;   // padded to 16 bytes
+static_assert(kDecHead % 16 == 0, "LDS header alignment");
 
 // DPP row reductions (16 lanes), then the four rows through readlane.
 __device__ __forceinline__ int wave_max_nonneg(int v) {
@@ -227,6 +236,27 @@ __device__ __forceinline__ int wave_sum_i(int v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// Block barrier for LDS traffic only.  __syncthreads() also orders global
+// memory, and on this target loads and stores share one counter, so it would
+// wait for every weight load in flight.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_sync() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));   // lgkmcnt, expcnt: no wait
+}
+
+typedef __attribute__((address_space(3))) void* dec_lds_t;
+typedef __attribute__((address_space(1))) void* dec_glb_t;
+
 // element e of a raw 16-byte activation vector, widened exactly to binary32
 template <int MODE>
 __device__ __forceinline__ float raw_elem(const uint4& v, int e) {
@@ -238,245 +268,270 @@ __device__ __forceinline__ float raw_elem(const uint4& v, int e) {
   }
 }
 
-template <int P, int MODE>
-__global__ __launch_bounds__(1024) void k_gemv_pipe(const PipeGroup grp) {
+template <int CPW, int MODE, bool ONE>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kInt8 ? 8 : 6))) void k_gemv_dec(const DecGroup grp) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < grp.count && (int)blockIdx.x >= grp.p[i].block0) pi = i;
-  const PipeProblem& pr = grp.p[pi];
-  const int T = grp.T, N = pr.N, K = pr.K;
+  const DecProblem pr = grp.p[blockIdx.y];
+  const int T = ONE ? 1 : grp.T, nwaves = grp.nw;
+  // Every argument in one batch of scalar loads: without this the compiler
+  // fetches them in dependent rounds around the early exit below.
+  __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
+                   "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
+                   "s"(pr.per), "s"(T), "s"(nwaves));
+  const int N = pr.N, K = pr.K, per = pr.per;
+  const int n0 = (int)blockIdx.x * 16;
+  if (n0 >= N) return;                              // the grid spans the widest problem
 
-  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nthreads = nwaves * 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qg = lane >> 4, r = lane & 15;
   const int K16 = K >> 4;
-  const int nchunks = K16 >> 4;                     // 16 words (256 k) per chunk
-  const int n0 = ((int)blockIdx.x - pr.block0) * 16;
-  // LDS: [256 B zeros][T x (K + 16) activation bytes, transposed per 64 B]
-  //      [16 row sums][16 absmax bits][partials].  The 16-byte pad per token
-  //      spreads the tokens of one B-operand read over different banks.
-  const int xs = (K >> 2) + 4;                      // token stride in dwords
-  uint32_t* zero = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* xl = zero + 64;
-  int* rsum = reinterpret_cast<int*>(xl + T * xs);
-  int* amax = rsum + 16;
-  int* red = amax + 16;
+  const int nchunks = K >> 8;                       // 16 words (256 k) per chunk
+  const int c0 = wave * per;
+  const int cnt = min(per, nchunks - c0);           // <= 0 when K is narrower than the block
+
+  // LDS: [header][T x (K + 16) int8 activations, row-major; the 16-byte pad
+  //      per token spreads the tokens of one B-operand read over the banks]
+  //      [fused modes: the raw activations, T x K]
+  const int tstride = K + 16;
+  int* zero = reinterpret_cast<int*>(smem);                    // 16 ints of zeros
+  int* tile = zero + 16;                                       // [token][row]
+  int* counter = tile + 256;
+  int* amax = counter + 1;
+  unsigned char* xs8 = smem + kDecHead;
+  unsigned char* raw = xs8 + T * tstride;
 
   int n = n0 + r;
-  n = n < N ? n : N - 1;
+  n = n < N ? n : N - 1;                            // rows past N are computed, never stored
   const uint4* wrow = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
-  const int my = (nchunks - wave + nwaves - 1) / nwaves;   // chunks of this wave (>= 1)
-  auto chunk_of = [&](int i) { return wave + (i < my ? i : my - 1) * nwaves; };
 
-  // Issue order matters: vector loads retire in order, so anything waited on
-  // before the main loop (the activations) is issued before the weight
-  // prefetch, which then stays in flight through the staging and the barrier.
-  constexpr int kStage = kGemvStage;
-  constexpr int E = MODE == kInt8 ? 16 : MODE == kBf16 ? 8 : 4;  // elements per 16 bytes
-  const int per_tok = K / E, nvec = T * per_tok;
-  const uint4* src = reinterpret_cast<const uint4*>(pr.x);
-  uint4 sv[kStage];
-#pragma unroll
-  for (int m = 0; m < kStage; ++m) {
-    const int i = threadIdx.x + m * blockDim.x;
-    sv[m] = src[i < nvec ? i : nvec - 1];
-  }
-  // the epilogue's scalars, fetched early so their latency hides under the loop
-  const float g = pr.gamma[0];
+  // Issue order matters: vector memory operations retire in order, so what
+  // is waited on first goes first.  The token absmax (int8 input) ...
   float am = 0.0f;
-  if constexpr (MODE == kInt8) am = pr.absmax[threadIdx.x < 16 * T ? (threadIdx.x >> 4) : 0];
-
-  uint4 buf[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) buf[j] = wrow[(size_t)chunk_of(j) * 4];
-
-  if (threadIdx.x < 64) zero[threadIdx.x] = 0u;
-  if (threadIdx.x < 32) rsum[threadIdx.x] = 0;      // row sums and absmax bits
-  // 16 int8 activations = word v = iv & 3 of a 64-byte group; dword (v, j)
-  // of the group is stored at position (j, v).
-  auto xq_dword = [&](int t, int iv, int j) -> uint32_t* {
-    return xl + t * xs + (iv >> 2) * 16 + (iv & 3) + 4 * j;
-  };
+  if constexpr (MODE == kInt8) am = pr.absmax[min(lane >> 4, T - 1)];
+  // ... then the activations, straight into LDS (lane l's 16 bytes land at
+  // the wave's base + 16 l): int8 input, this wave's own k run; raw input
+  // (step A1 fused), the whole rows, shared by the block ...
+  const int run0 = c0 * 256, runb = cnt > 0 ? cnt * 256 : 0;   // this wave's k run
   if constexpr (MODE == kInt8) {
-#pragma unroll
-    for (int m = 0; m < kStage; ++m) {
-      const int i = threadIdx.x + m * blockDim.x;
-      if (i < nvec) {
-        const int t = i / per_tok, iv = i - t * per_tok;
-        *xq_dword(t, iv, 0) = sv[m].x; *xq_dword(t, iv, 1) = sv[m].y;
-        *xq_dword(t, iv, 2) = sv[m].z; *xq_dword(t, iv, 3) = sv[m].w;
-      }
-    }
-    // (the host guarantees nvec <= kStage * blockDim: one round covers it)
+    const int8_t* x8 = static_cast<const int8_t*>(pr.x);
+    for (int t = 0; t < T; ++t)
+      for (int base = 0; base < runb; base += 1024)
+        if (base + 16 * lane < runb)
+          __builtin_amdgcn_global_load_lds(
+              (dec_glb_t)(x8 + (int64_t)t * K + run0 + base + 16 * lane),
+              (dec_lds_t)(xs8 + t * tstride + run0 + base), 16, 0, 0);
   } else {
-    // Step A1 in the block: absmax per token (T <= 4) ...
-    int tmax[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < kStage; ++m) {
-      const int i = threadIdx.x + m * blockDim.x;
-      if (i < nvec) {
-        const int t = i / per_tok;
-        int mx = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          mx = max(mx, (int)(__float_as_uint(raw_elem<MODE>(sv[m], e)) & 0x7fffffffu));
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          if (t == tt) tmax[tt] = max(tmax[tt], mx);
-      }
-    }
-    __syncthreads();                                // amax cleared
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt < T) {
-        const int wm = wave_max_nonneg(tmax[tt]);   // non-negative bit patterns order as values
-        if (lane == 0) atomicMax(&amax[tt], wm);
-      }
-    }
-    __syncthreads();
-    // ... then scale, round half to even, clip, and lay out as int8
-    float sc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      sc[tt] = tt < T ? kQb / fmaxf(__uint_as_float((uint32_t)amax[tt]), kEps) : 0.0f;
-    int tsum[4] = {0, 0, 0, 0};
-    const bool first = n0 == 0;
-#pragma unroll
-    for (int m = 0; m < kStage; ++m) {
-      const int i = threadIdx.x + m * blockDim.x;
-      if (i < nvec) {
-        const int t = i / per_tok, ie = i - t * per_tok;   // vector index within the token
-        float s = sc[0];
-#pragma unroll
-        for (int tt = 1; tt < 4; ++tt)
-          if (t == tt) s = sc[tt];
-        uint32_t d[E / 4];
-        int part = 0;
-#pragma unroll
-        for (int w = 0; w < E / 4; ++w) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float v = raw_elem<MODE>(sv[m], 4 * w + b) * s;   // one binary32 product
-            const int q = (int)fminf(fmaxf(rintf(v), -kQb), kQb);
-            part += q;
-            word |= (uint32_t)(q & 0xff) << (8 * b);
-          }
-          d[w] = word;
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          if (t == tt) tsum[tt] += part;
-        // E elements start at k = ie * E: int8 vector iv, first dword j0
-        const int k0 = ie * E, iv = k0 >> 4, j0 = (k0 & 15) >> 2;
-#pragma unroll
-        for (int w = 0; w < E / 4; ++w) *xq_dword(t, iv, j0 + w) = d[w];
-        if (first && pr.xq_out) {
-          int8_t* dst = pr.xq_out + (int64_t)t * K + k0;
-          if constexpr (E == 8)
-            *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[E / 4 - 1]);
-          else
-            *reinterpret_cast<uint32_t*>(dst) = d[0];
-        }
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt < T) {
-        const int ws = wave_sum_i(tsum[tt]);
-        if (lane == 0) atomicAdd(&rsum[tt], ws);
-      }
-    }
-    if (first && pr.absmax_out && threadIdx.x < T)
-      pr.absmax_out[threadIdx.x] = __uint_as_float((uint32_t)amax[threadIdx.x]);
+    const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
+    const int nvec = T * K / (MODE == kBf16 ? 8 : 4);
+    for (int base = wave * 64; base < nvec; base += nthreads)
+      if (base + lane < nvec)
+        __builtin_amdgcn_global_load_lds((dec_glb_t)(xr + 16 * (base + lane)),
+                                         (dec_lds_t)(raw + 16 * base), 16, 0, 0);
   }
-  __syncthreads();
-
-  // B operand address: lanes of tokens past T read the zero block (stride 0)
-  const uint4* xb = reinterpret_cast<const uint4*>(r < T ? xl + r * xs + qg * 16 : zero);
-  const int xstride = r < T ? 16 : 0;              // uint4 per chunk
-
-  v4i a1 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0}, a16 = {0, 0, 0, 0};
-  struct Slices { v4i s0, s1, s2, s3; };
-  auto unpack = [](const uint4& w4) {
-    Slices q;
-    q.s0 = v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u),
-               (int)(w4.z & 0x03030303u), (int)(w4.w & 0x03030303u)};
-    q.s1 = v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu),
-               (int)(w4.z & 0x0C0C0C0Cu), (int)(w4.w & 0x0C0C0C0Cu)};
-    q.s2 = v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u),
-               (int)(w4.z & 0x30303030u), (int)(w4.w & 0x30303030u)};
-    q.s3 = v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
-               (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)};
-    return q;
-  };
-  auto mma = [&](const Slices& q, int c) {
-    const uint4* xc = xb + c * xstride;
-    const uint4 b0 = xc[0], b1 = xc[1], b2 = xc[2], b3 = xc[3];
-    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        q.s0, v4i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w}, a1, 0, 0, 0);
-    a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        q.s1, v4i{(int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w}, a4, 0, 0, 0);
-    a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        q.s2, v4i{(int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w}, a16, 0, 0, 0);
-    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        q.s3, v4i{(int)b3.x, (int)b3.y, (int)b3.z, (int)b3.w}, a1, 0, 0, 0);
-  };
-
-  int i0 = 0;
-  for (; i0 + P <= my; i0 += P) {
+  const float g = pr.gamma[0];
+  // ... and last every weight chunk of this wave; slots past cnt repeat the
+  // row's last chunk and meet a zero B operand below.
+  uint4 buf[CPW];
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int i = i0 + j;
-      // consume buf[j] first, then refill the same registers: no copies, and
-      // the wait before the masks is only for this one load (P-1 stay in flight)
-      const Slices q = unpack(buf[j]);
-      buf[j] = wrow[(size_t)chunk_of(i + P) * 4];
-      __builtin_amdgcn_sched_barrier(0);
-      mma(q, wave + i * nwaves);
-    }
+  for (int i = 0; i < CPW; ++i) {
+    const int c = min(c0 + i, nchunks - 1);
+    buf[i] = wrow[(size_t)c * 4];
   }
-#pragma unroll
-  for (int j = 0; j < P; ++j)   // the last my % P chunks are already in buf[0..]
-    if (i0 + j < my) mma(unpack(buf[j]), wave + (i0 + j) * nwaves);
 
-#pragma unroll
-  for (int v = 0; v < 4; ++v)
-    red[(wave * 4 + v) * 64 + lane] = a1[v] + (a4[v] >> 2) + (a16[v] >> 4);
-
+  for (int i = threadIdx.x; i < 16 + 256 + 1 + 16; i += nthreads) zero[i] = 0;
+  int qsum = 0;     // sum of q over this wave's k run, token of lane l: l & 15
+  float a_t = am;   // absmax of the token whose outputs lane l writes (l >> 4)
   if constexpr (MODE == kInt8) {
-    // sum of q per token (removes the code offset), read back from LDS
+    lds_sync();                                     // header cleared (the waves arrive together)
+    wait_vmem<CPW>();                               // this wave's activation run landed
     for (int t = 0; t < T; ++t) {
-      const uint4* xt = reinterpret_cast<const uint4*>(xl + t * xs);
+      const uint4* xt = reinterpret_cast<const uint4*>(xs8 + t * tstride + run0);
       int part = 0;
-      for (int i = threadIdx.x; i < (K >> 4); i += blockDim.x) {
+      for (int i = lane; i < runb / 16; i += 64) {
         const uint4 v = xt[i];
         part = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, part, false);
         part = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, part, false);
         part = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, part, false);
         part = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, part, false);
       }
-      part = wave_sum_i(part);
-      if (lane == 0) atomicAdd(&rsum[t], part);
+      const int sum = wave_sum_i(part);
+      if (r == t) qsum = sum;
     }
+  } else {
+    // Step A1 in the block.  The absmax of each token (T <= 4) over all of
+    // K, from every wave's share of the raw rows ...
+    wait_vmem<CPW>();                               // this wave's share landed
+    lds_sync();                                     // ... every wave's; header cleared
+    constexpr int E = MODE == kBf16 ? 8 : 4;        // elements per 16 bytes
+    const int per_tok = K / E, nvec = T * per_tok;
+    const uint4* raw4 = reinterpret_cast<const uint4*>(raw);
+    uint32_t tmax[4] = {0, 0, 0, 0};                // magnitude bit patterns
+    for (int i = threadIdx.x; i < nvec; i += nthreads) {
+      const uint4 v = raw4[i];
+      uint32_t mx;
+      if constexpr (MODE == kBf16) {
+        // bf16 magnitudes order as unsigned 16-bit integers: packed max
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        const uint32_t m = 0x7fff7fffu;
+        us2 h = __builtin_elementwise_max(
+            __builtin_bit_cast(us2, v.x & m), __builtin_bit_cast(us2, v.y & m));
+        h = __builtin_elementwise_max(h, __builtin_bit_cast(us2, v.z & m));
+        h = __builtin_elementwise_max(h, __builtin_bit_cast(us2, v.w & m));
+        mx = (uint32_t)max(h.x, h.y) << 16;
+      } else {
+        mx = max(max(v.x & 0x7fffffffu, v.y & 0x7fffffffu), max(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
+      }
+      if constexpr (ONE) {
+        tmax[0] = max(tmax[0], mx);
+      } else {
+        const int t = (i >= per_tok) + (i >= 2 * per_tok) + (i >= 3 * per_tok);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          if (t == tt) tmax[tt] = max(tmax[tt], mx);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < (ONE ? 1 : 4); ++tt) {
+      if (tt < T) {
+        const int wm = wave_max_nonneg((int)tmax[tt]);  // non-negative patterns order as values
+        if (lane == 0) atomicMax(&amax[tt], wm);
+      }
+    }
+    lds_sync();
+    // ... then each wave scales, rounds half to even and clips its own k run
+    // into the int8 rows (read back only by this wave: no barrier), four
+    // activations per lane at a time, summing q on the way.  Block 0 of the
+    // problem also stores the int8 activations and the absmax.
+    float sc[4];
+#pragma unroll
+    for (int tt = 0; tt < (ONE ? 1 : 4); ++tt)
+      sc[tt] = tt < T ? kQb / fmaxf(__uint_as_float((uint32_t)amax[tt]), kEps) : 0.0f;
+    a_t = __uint_as_float((uint32_t)amax[ONE ? 0 : min(lane >> 4, T - 1)]);
+    const bool first = blockIdx.x == 0;
+    const int ru = runb / 4;                        // 4-element units per token in the run
+    int tsum[4] = {0, 0, 0, 0};
+    for (int i = lane; i < T * ru; i += 64) {
+      const int t = ONE ? 0 : (i >= ru) + (i >= 2 * ru) + (i >= 3 * ru);
+      const int k0 = run0 + (i - t * ru) * 4;       // first k of the unit
+      float f[4];
+      if constexpr (MODE == kBf16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(raw + 2 * ((int64_t)t * K + k0));
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(raw + 4 * ((int64_t)t * K + k0));
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+      }
+      float s = sc[0];
+      if constexpr (!ONE) {
+#pragma unroll
+        for (int tt = 1; tt < 4; ++tt)
+          if (t == tt) s = sc[tt];
+      }
+      int q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        q[e] = (int)fminf(fmaxf(rintf(f[e] * s), -kQb), kQb);   // one binary32 product
+      // low bytes of q0..q3 into one word
+      const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x04000c0cu);
+      const uint32_t word = lo | hi;
+      const int part = __builtin_amdgcn_sdot4((int)word, 0x01010101, 0, false);
+      if constexpr (ONE) {
+        tsum[0] += part;
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          if (t == tt) tsum[tt] += part;
+      }
+      *reinterpret_cast<uint32_t*>(xs8 + t * tstride + k0) = word;
+      if (first && pr.xq_out) *reinterpret_cast<uint32_t*>(pr.xq_out + (int64_t)t * K + k0) = word;
+    }
+#pragma unroll
+    for (int tt = 0; tt < (ONE ? 1 : 4); ++tt) {
+      if (tt < T) {
+        const int sum = wave_sum_i(tsum[tt]);
+        if (r == tt) qsum = sum;
+      }
+    }
+    if (first && wave == 0 && pr.absmax_out && lane < T)
+      pr.absmax_out[lane] = __uint_as_float((uint32_t)amax[lane]);
   }
-  __syncthreads();
-  // 16 * T <= 256 outputs and blockDim >= 64: thread idx < 16 * T owns one
-  for (int idx = threadIdx.x; idx < 16 * T; idx += blockDim.x) {
+  // lane l's output scale (token l >> 4); with int8 input it waits for the epilogue
+  float osc = 0.0f;
+  if constexpr (MODE != kInt8) osc = out_scale(g, a_t);
+
+  // B operands of slot i: this token's 64 bytes of chunk c0 + i (four
+  // 16-byte vectors; slice j takes dword j of each), or zeros for tokens past
+  // T and for the repeated slots past cnt
+  const unsigned char* xrow = xs8 + (r < T ? r : 0) * tstride + qg * 64;
+  v4i a1 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0}, a16 = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const uint32_t* xc = (r < T && i < cnt)
+                             ? reinterpret_cast<const uint32_t*>(xrow + (c0 + i) * 256)
+                             : reinterpret_cast<const uint32_t*>(zero);
+    // slice j: dword j of each 16-byte vector (two ds_read2_b32 each)
+    auto xs = [&](int j) { return v4i{(int)xc[j], (int)xc[4 + j], (int)xc[8 + j], (int)xc[12 + j]}; };
+    const uint4 w4 = buf[i];
+    if constexpr (CPW < 8) {
+      // fields masked in place: c, 4c and 16c per byte, three accumulators
+      a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u), (int)(w4.z & 0x03030303u),
+               (int)(w4.w & 0x03030303u)}),
+          xs(0), a1, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu), (int)(w4.z & 0x0C0C0C0Cu),
+               (int)(w4.w & 0x0C0C0C0Cu)}),
+          xs(1), a4, 0, 0, 0);
+      a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u), (int)(w4.z & 0x30303030u),
+               (int)(w4.w & 0x30303030u)}),
+          xs(2), a16, 0, 0, 0);
+    } else {
+      // eight chunks in flight leave no room for three accumulators: every
+      // field is shifted down to c and summed in one
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            (v4i{(int)codes_of(w4.x, j), (int)codes_of(w4.y, j), (int)codes_of(w4.z, j),
+                 (int)codes_of(w4.w, j)}),
+            xs(j), a1, 0, 0, 0);
+    }
+    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        (v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
+             (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)}),
+        xs(3), a1, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // one chunk's operands live at a time
+  }
+
+  // lane (qg, r) holds rows 4qg + v of token column r
+  if (r < T) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      atomicAdd(&tile[r * 16 + 4 * qg + v], a1[v] + (a4[v] >> 2) + (a16[v] >> 4) - qsum);
+  }
+  // The last wave to add its tile writes the block's outputs; the others are
+  // done.  The counter's release/acquire orders the tile adds before it.
+  int ticket = 0;
+  if (lane == 0)
+    ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  ticket = __builtin_amdgcn_readfirstlane(ticket);
+  if (ticket != nwaves - 1) return;
+  for (int idx = lane; idx < 16 * T; idx += 64) {
     const int i = idx & 15, tl = idx >> 4;
     const int nn = n0 + i;
     if (nn >= N) continue;
-    const int slot = i & 3, ln = (i >> 2) * 16 + tl;
-    int sum = -rsum[tl];
-    for (int wv = 0; wv < nwaves; ++wv) sum += red[(wv * 4 + slot) * 64 + ln];
+    const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int64_t o = (int64_t)tl * N + nn;
     if (pr.acc) pr.acc[o] = sum;
-    float a_t;
-    if constexpr (MODE == kInt8) a_t = idx == (int)threadIdx.x ? am : pr.absmax[tl];
-    else a_t = __uint_as_float((uint32_t)amax[tl]);
-    pr.y[o] = (float)sum * out_scale(g, a_t);
+    float sc = MODE == kInt8 ? out_scale(g, am) : osc;
+    if (idx >= 64) {   // T > 4: tokens past lane 63's
+      sc = out_scale(g, MODE == kInt8 ? pr.absmax[tl] : __uint_as_float((uint32_t)amax[tl]));
+    }
+    pr.y[o] = (float)sum * sc;
   }
 }
 
@@ -517,80 +572,108 @@ void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
 
 }  // namespace
 
-#ifndef BL_GEMV_PIPE_P
-#define BL_GEMV_PIPE_P 6          // chunks in flight per wave in the pipelined kernel
+namespace {
+
+#ifndef BL_GEMV_DEC_RESIDENT
+#define BL_GEMV_DEC_RESIDENT 8192   // waves resident at once (8 per SIMD, 1024 SIMDs)
 #endif
-#ifndef BL_GEMV_PIPE_WAVES
-#define BL_GEMV_PIPE_WAVES 2048   // total waves aimed for (about 8 per CU)
+#ifndef BL_GEMV_DEC_MAXW
+#define BL_GEMV_DEC_MAXW 8          // waves per block, unless K needs more (8 chunks each)
 #endif
-#ifndef BL_GEMV_PIPE_MINCPW
-#define BL_GEMV_PIPE_MINCPW 4     // fewest chunks per wave when splitting K
+#ifndef BL_GEMV_DEC_CPW
+#define BL_GEMV_DEC_CPW 2           // chunks per wave aimed for
 #endif
-#ifndef BL_GEMV_PIPE_XLDS
-#define BL_GEMV_PIPE_XLDS 32768  // largest T*K staged in LDS
+#ifndef BL_GEMV_DEC_XLDS
+#define BL_GEMV_DEC_XLDS 32768    // largest T*K of int8 activations staged in LDS
+#endif
+#ifndef BL_GEMV_DEC_RAWLDS
+#define BL_GEMV_DEC_RAWLDS 32768  // largest raw activation bytes (fused act-quant) in LDS
 #endif
 
-// Waves per block of the pipelined kernel.  Large grids do best with few,
-// long-running waves (each streams many chunks); small grids need K split over
-// more waves to have enough loads in flight.  Aim for about
-// BL_GEMV_PIPE_WAVES waves in total with at least BL_GEMV_PIPE_MINCPW chunks
-// each, and enough threads to stage the activations in one round
-// (elems_per_vec elements per 16-byte vector).
-int pipe_waves(int64_t t, int64_t blocks, int64_t k, int elems_per_vec) {
-  const int nchunks = (int)(k / 256);
-  int nw = (int)((BL_GEMV_PIPE_WAVES + blocks - 1) / blocks);
-  int cap = nchunks / BL_GEMV_PIPE_MINCPW;
-  if (cap < 1) cap = 1;
-  if (nw > cap) nw = cap;
-  const int64_t vecs = t * k / elems_per_vec;
-  const int need = (int)((vecs + 64 * kGemvStage - 1) / (64 * kGemvStage));
-  if (nw < need) nw = need;
-  if (nw > nchunks) nw = nchunks;
-  return nw;
+// Launch shape of the decode kernel for a group of `blocks` 16-row tiles
+// whose widest K is kmax: nw waves per block, each owning at most cpw
+// (a template size: 2, 4 or 8) consecutive 256-k chunks.  A block's time is
+// mostly latency plus the work its waves do one after another on the SIMDs,
+// so: about BL_GEMV_DEC_CPW chunks per wave, at most BL_GEMV_DEC_MAXW waves
+// per block and no more waves than fit on the chip at once, but never more
+// than 8 chunks per wave (K <= 32768, 128 chunks, keeps nw <= 16).
+struct DecShape {
+  int nw, cpw;
+};
+DecShape dec_shape(int64_t blocks, int64_t kmax) {
+  const int nchunks = (int)(kmax / 256);
+  int nw = (nchunks + BL_GEMV_DEC_CPW - 1) / BL_GEMV_DEC_CPW;
+  if (nw > BL_GEMV_DEC_MAXW) nw = BL_GEMV_DEC_MAXW;
+  const int64_t fit = BL_GEMV_DEC_RESIDENT / blocks;
+  if (nw > fit) nw = (int)(fit > 1 ? fit : 1);
+  const int least = (nchunks + 7) / 8;
+  if (nw < least) nw = least;
+  const int per = (nchunks + nw - 1) / nw;
+  return DecShape{nw, per <= 2 ? 2 : per <= 4 ? 4 : 8};
 }
 
-bool pipe_shape_ok(int64_t t, int64_t k, int elems_per_vec, int max_t) {
-  if (!(t <= max_t && (k % 256) == 0 && t * k <= BL_GEMV_PIPE_XLDS)) return false;
-  const int nw = pipe_waves(t, 1, k, elems_per_vec);  // the fewest-waves case bounds staging
-  return nw <= 16 && t * k / elems_per_vec <= (int64_t)16 * 64 * kGemvStage;
+// Shapes the decode kernel takes: raw_bytes is 0 for int8 activations, else
+// the size of one raw activation (step A1 fused, at most 4 tokens).
+bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
+  if ((k % 256) != 0 || t * k > BL_GEMV_DEC_XLDS) return false;
+  if (raw_bytes == 0) return t <= 16;
+  return t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
 }
 
-bool pipe_ok(int64_t t, int64_t n, int64_t k, const void* packed, const void* xq) {
-  (void)n;
-  return pipe_shape_ok(t, k, 16, 16) && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
-         (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
+size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes) {
+  return kDecHead + (size_t)t * (kmax + 16) + (size_t)t * kmax * raw_bytes;
 }
 
-size_t pipe_lds(int64_t t, int64_t k, int nw) {
-  return 256 + (size_t)t * (k + 16) + 32 * sizeof(int) + (size_t)nw * 4 * 64 * sizeof(int);
+template <int MODE, bool ONE>
+void launch_dec(const DecGroup& grp, dim3 grid, const DecShape& sh, size_t lds,
+                hipStream_t stream) {
+  if (sh.cpw == 2)
+    k_gemv_dec<2, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
+  else if (sh.cpw == 4)
+    k_gemv_dec<4, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
+  else
+    k_gemv_dec<8, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
 }
 
 template <int MODE>
-hipError_t run_pipe_group(const PipeGroup& grp, int blocks, int nw, size_t lds,
-                          hipStream_t stream) {
-  k_gemv_pipe<BL_GEMV_PIPE_P, MODE><<<blocks, nw * 64, lds, stream>>>(grp);
+hipError_t run_dec(DecGroup& grp, int count, int bx, const DecShape& sh, size_t lds,
+                   hipStream_t stream) {
+  grp.nw = sh.nw;
+  for (int i = 0; i < count; ++i) grp.p[i].per = (grp.p[i].K / 256 + sh.nw - 1) / sh.nw;
+  const dim3 grid((unsigned)bx, (unsigned)count);
+  bool one = false;   // single-token specialisation of the fused prologue
+  if constexpr (MODE != kInt8) one = grp.T == 1;
+  if (one)
+    launch_dec<MODE, MODE != kInt8>(grp, grid, sh, lds, stream);
+  else
+    launch_dec<MODE, false>(grp, grid, sh, lds, stream);
   return hipGetLastError();
 }
 
-void run_pipe(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
-              int t, int n, int k, float* y, int32_t* acc, hipStream_t stream) {
-  PipeGroup grp = {};
-  grp.count = 1;
-  grp.T = t;
-  grp.p[0] = PipeProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
-                         nullptr, nullptr, n, k, 0};
-  const int blocks = (n + 15) / 16;
-  int nw = pipe_waves(t, blocks, k, 16);
-  if (nw * 64 * kGemvStage < (int64_t)t * k / 16) nw = (int)((t * k / 16 + 64 * kGemvStage - 1) / (64 * kGemvStage));
-  run_pipe_group<kInt8>(grp, blocks, nw, pipe_lds(t, k, nw), stream);
+bool dec_ok(int64_t t, int64_t k, const void* packed, const void* xq) {
+  return dec_shape_ok(t, k, 0) && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
+         (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
 }
+
+hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                        const float* absmax, int t, int n, int k, float* y, int32_t* acc,
+                        hipStream_t stream) {
+  DecGroup grp = {};
+  grp.T = t;
+  grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
+                        nullptr, nullptr, n, k, 0};
+  const int blocks = (n + 15) / 16;
+  return run_dec<kInt8>(grp, 1, blocks, dec_shape(blocks, k), dec_lds(t, k, 0), stream);
+}
+
+}  // namespace
 
 hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int bf16,
                                hipStream_t stream) {
-  const int E = bf16 ? 8 : 4;
+  const int rb = bf16 ? 2 : 4;   // bytes per raw activation
   bool fused = count <= kMaxGroup;
   for (int i = 0; fused && i < count; ++i) {
-    fused = pipe_shape_ok(t, probs[i].K, E, 4) &&
+    fused = dec_shape_ok(t, probs[i].K, rb) &&
             (reinterpret_cast<uintptr_t>(probs[i].x) % 16) == 0 &&
             (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
   }
@@ -604,37 +687,30 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
     }
     return hipSuccess;
   }
-  PipeGroup grp = {};
-  grp.count = count;
+  DecGroup grp = {};
   grp.T = (int)t;
-  int blocks = 0;
-  int64_t kmax = 0;
+  int64_t bx = 0, blocks = 0, kmax = 0;
   for (int i = 0; i < count; ++i) {
     const bl_linear& q = probs[i];
-    grp.p[i] = PipeProblem{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr,
-                           q.y, q.acc, q.xq, q.absmax, (int)q.N, (int)q.K, blocks};
-    blocks += (int)((q.N + 15) / 16);
+    grp.p[i] = DecProblem{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr,
+                          q.y, q.acc, q.xq, q.absmax, (int)q.N, (int)q.K, 0};
+    const int64_t b = (q.N + 15) / 16;
+    blocks += b;
+    if (b > bx) bx = b;
     if (q.K > kmax) kmax = q.K;
   }
-  // one block shape for the group: waves for the widest K, staging for every K
-  int nw = pipe_waves(t, blocks, kmax, E);
-  for (int i = 0; i < count; ++i) {
-    const int need = (int)((t * probs[i].K / E + 64 * kGemvStage - 1) / (64 * kGemvStage));
-    if (nw < need) nw = need;
-  }
-  if (nw > 16) nw = 16;
-  const size_t lds = pipe_lds(t, kmax, nw);
-  return bf16 ? run_pipe_group<kBf16>(grp, blocks, nw, lds, stream)
-              : run_pipe_group<kF32>(grp, blocks, nw, lds, stream);
+  // one block shape for the group: sized for the widest K
+  const DecShape sh = dec_shape(blocks, kmax);
+  const size_t lds = dec_lds(t, kmax, rb);
+  return bf16 ? run_dec<kBf16>(grp, count, (int)bx, sh, lds, stream)
+              : run_dec<kF32>(grp, count, (int)bx, sh, lds, stream);
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
-  if (pipe_ok(t, n, k, packed, xq)) {
-    run_pipe(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, stream);
-    return hipGetLastError();
-  }
+  if (dec_ok(t, k, packed, xq))
+    return run_dec_int8(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, stream);
   const bool vec4 = (k % 64) == 0 && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
   for (int64_t t0 = 0; t0 < t; t0 += kGemvTokens) {
