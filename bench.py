@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill GEMM context run")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--fused-only", action="store_true",
+                   help="time only the fused layer steps (a kernel trace of this run holds "
+                        "nothing but the roofline kernel's launches)")
     p.add_argument("--profile-pass", action="store_true",
                    help="counter runs: two eager passes of the fused steps over the layer "
                         "sets plus the copy calibration, no timing and no JSON")
@@ -332,24 +335,32 @@ def main():
     ms_per_step = ms / k_steps
     fused_us = ms * 1e3 / (k_steps * len(groups))
 
-    # the same layer as 14 separate launches, and its kernels alone
-    g_all = capture(torch, lambda s: steps(s), stream)
-    ms_unfused = time_graph(torch, g_all, reps, warm, stream)
-    g_gemv = capture(torch, lambda s: steps(s, with_quant=False), stream)
-    ms_g = time_graph(torch, g_gemv, reps, warm, stream)
-    gemv_us = ms_g * 1e3 / (k_steps * len(mp))
-    g_quant = capture(torch, lambda s: steps(s, with_gemv=False), stream)
-    ms_q = time_graph(torch, g_quant, reps, warm, stream)
-    quant_us = ms_q * 1e3 / (k_steps * len(mp))
+    extra = {}
+    if not args.fused_only:
+        # the same layer as 14 separate launches, and its kernels alone
+        g_all = capture(torch, lambda s: steps(s), stream)
+        ms_unfused = time_graph(torch, g_all, reps, warm, stream)
+        g_gemv = capture(torch, lambda s: steps(s, with_quant=False), stream)
+        ms_g = time_graph(torch, g_gemv, reps, warm, stream)
+        gemv_us = ms_g * 1e3 / (k_steps * len(mp))
+        g_quant = capture(torch, lambda s: steps(s, with_gemv=False), stream)
+        ms_q = time_graph(torch, g_quant, reps, warm, stream)
+        quant_us = ms_q * 1e3 / (k_steps * len(mp))
 
-    # the fused steps launched one by one on the stream, without a graph
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    eager_reps = max(1, reps // 4)
-    for _ in range(eager_reps):
-        fused_steps(stream)
-    stream.synchronize()
-    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / (eager_reps * n_sets)
+        # the fused steps launched one by one on the stream, without a graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eager_reps = max(1, reps // 4)
+        for _ in range(eager_reps):
+            fused_steps(stream)
+        stream.synchronize()
+        eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / (eager_reps * n_sets)
+        extra = {"eager_ms_per_step": round(eager_ms_per_step, 4),
+                 "unfused_ms_per_step": round(ms_unfused / k_steps, 5),
+                 "unfused_gb_s": round(unfused_step_bytes / (ms_unfused / k_steps * 1e-3) / 1e9, 2),
+                 "gemv_avg_launch_us": round(gemv_us, 3),
+                 "gemv_gb_s": round(gemv_launch_bytes / (gemv_us * 1e-6) / 1e9, 1),
+                 "act_quant_avg_launch_us": round(quant_us, 3)}
 
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -366,15 +377,9 @@ def main():
                 "avg_launch_us": round(fused_us, 3),
                 "algorithmic_bytes_per_launch": int(fused_launch_bytes)}
 
-    extra = {"eager_ms_per_step": round(eager_ms_per_step, 4),
-             "unfused_ms_per_step": round(ms_unfused / k_steps, 5),
-             "unfused_gb_s": round(unfused_step_bytes / (ms_unfused / k_steps * 1e-3) / 1e9, 2),
-             "gemv_avg_launch_us": round(gemv_us, 3),
-             "gemv_gb_s": round(gemv_launch_bytes / (gemv_us * 1e-6) / 1e9, 1),
-             "act_quant_avg_launch_us": round(quant_us, 3),
-             "layer_sets_rotated": n_sets,
-             "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
-             "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]}
+    extra.update({"layer_sets_rotated": n_sets,
+                  "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
+                  "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     if not args.no_extra:
         extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
 
