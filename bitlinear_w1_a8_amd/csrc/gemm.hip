@@ -20,6 +20,7 @@
 // steps of 128 with the activation tile double-buffered in LDS and the next
 // tile's loads in flight during the current tile's MFMAs.  Tiles are ordered
 // so that consecutive tiles of one XCD share activation rows in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "bl_internal.h"
@@ -229,24 +230,27 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // one stage do not alias reads of another and does not drain every
 // outstanding load before each LDS read (one array indexed by stage is not
 // enough for that).
-template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES>
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
                                                          const int8_t* __restrict__ xq,
                                                          const float* __restrict__ absmax,
                                                          int T, int N, int K,
                                                          float* __restrict__ y,
-                                                         int32_t* __restrict__ acc_out) {
-  static_assert(STAGES == 3 || STAGES == 4, "three or four stages");
+                                                         int32_t* __restrict__ acc_out,
+                                                         int ksteps, int splits) {
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
   constexpr int kABuf = BM * BK, kBBuf = BN * (BK / 4);   // bytes per stage
   constexpr int kAChunks = BM / 8 / WAVES, kBChunks = BN / 32 / WAVES;  // 1 KiB loads per wave
   static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the wave count");
-  __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf], A2[kABuf];
+  __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf];
+  __shared__ __align__(16) unsigned char A2[STAGES > 2 ? kABuf : 16];
   __shared__ __align__(16) unsigned char A3[STAGES > 3 ? kABuf : 16];
-  __shared__ __align__(16) unsigned char B0[kBBuf], B1[kBBuf], B2[kBBuf];
+  __shared__ __align__(16) unsigned char B0[kBBuf], B1[kBBuf];
+  __shared__ __align__(16) unsigned char B2[STAGES > 2 ? kBBuf : 16];
   __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
   auto abuf = [&](auto st) -> unsigned char* {
@@ -275,9 +279,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 
   const int ntn = (N + BN - 1) / BN, ntm = (T + BM - 1) / BM;
   const int tiles = ntn * ntm;
-  int tile = blockIdx.x;
-  if (tiles >= 8 && (tiles % 8) == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  // work item = (K part, tile); items next to each other share a K part, so
+  // the blocks that run together share activation rows and weight columns
+  const int items = SPLIT ? tiles * splits : tiles;
+  int item = blockIdx.x;
+  if (items >= 8 && (items % 8) == 0) item = (blockIdx.x % 8) * (items / 8) + blockIdx.x / 8;
+  const int part = SPLIT ? item / tiles : 0, tile = item - part * tiles;
   const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+  const uint32_t kbase = (uint32_t)part * (uint32_t)ksteps * BK;   // first k of this part
 
   // per-token output scale first: its loads retire before the pipeline starts
   {
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     boff[i] = (uint32_t)n * (uint32_t)K16 + 4u * (lane & 1);
   }
   auto issue = [&](int kt, unsigned char* As, unsigned char* Bs) {
-    const uint32_t k0 = (uint32_t)kt * BK;
+    const uint32_t k0 = kbase + (uint32_t)kt * BK;
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(xq + (aoff[i] + k0)),
@@ -328,13 +337,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  const int nk = K / BK;
+  const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : K / BK;   // >= 1 (host)
   constexpr int kLoads = kAChunks + kBChunks;     // this wave's loads per tile
   static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
   // prologue: tiles 0 .. STAGES-2 (repeats of the last tile when K is short)
   issue(0, abuf(I0{}), bbuf(I0{}));
-  issue(nk > 1 ? 1 : 0, abuf(I1{}), bbuf(I1{}));
+  if constexpr (STAGES >= 3) issue(nk > 1 ? 1 : 0, abuf(I1{}), bbuf(I1{}));
   if constexpr (STAGES == 4) issue(nk > 2 ? 2 : nk - 1, abuf(I2{}), bbuf(I2{}));
   // tile 0 landed (the rest stays in flight) and the scale writes are done;
   // a fence-free barrier, as a fence would wait for every load
@@ -395,11 +404,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   for (; kt + STAGES <= nk; kt += STAGES) {
     step(I0{}, kt);
     step(I1{}, kt + 1);
-    step(I2{}, kt + 2);
+    if constexpr (STAGES >= 3) step(I2{}, kt + 2);
     if constexpr (STAGES == 4) step(I3{}, kt + 3);
   }
   if (kt < nk) step(I0{}, kt);
-  if (kt + 1 < nk) step(I1{}, kt + 1);
+  if constexpr (STAGES >= 3)
+    if (kt + 1 < nk) step(I1{}, kt + 1);
   if constexpr (STAGES == 4)
     if (kt + 2 < nk) step(I2{}, kt + 2);
   wait_vm<0>();   // no load may land in LDS after the block has finished
@@ -418,23 +428,56 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
         if (n >= N) continue;
         const int64_t o = (int64_t)tok * N + n;
         const int sv = acc[i][j][v];
-        if (acc_out) acc_out[o] = sv;
-        y[o] = (float)sv * sc;
+        if constexpr (SPLIT) {
+          // K split: exact int32 partial sums meet in y (zeroed beforehand,
+          // read as int32 until the finishing pass rescales it in place)
+          atomicAdd(reinterpret_cast<int*>(y) + o, sv);
+        } else {
+          if (acc_out) acc_out[o] = sv;
+          y[o] = (float)sv * sc;
+        }
       }
     }
+  }
+}
+
+// K split, around the kernel above: y is cleared, receives the exact int32
+// partial sums of every K part (integer addition, so the order of the atomic
+// adds does not matter), and is then rescaled in place.
+__global__ __launch_bounds__(256) void k_clear_i32(int* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+// one block per (row, 1024-column block)
+__global__ __launch_bounds__(256) void k_split_finish(float* __restrict__ y,
+                                                      int32_t* __restrict__ acc_out,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ absmax, int N,
+                                                      int col_blocks) {
+  const int t = blockIdx.x / col_blocks, cb = blockIdx.x - t * col_blocks;
+  const float sc = out_scale(gamma[0], absmax[t]);
+  const int64_t row = (int64_t)t * N;
+  for (int c = cb * 1024 + threadIdx.x; c < min(N, cb * 1024 + 1024); c += 256) {
+    const int v = reinterpret_cast<const int*>(y)[row + c];
+    if (acc_out) acc_out[row + c] = v;
+    y[row + c] = (float)v * sc;
   }
 }
 
 template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES>
 hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
-                   hipStream_t stream) {
+                   hipStream_t stream, int splits = 1, int ksteps = 0) {
+  // K parts of ksteps 128-wide steps each (the last may be shorter); the
+  // caller sizes them so that every part has at least one step
+  if (splits == 1) ksteps = (int)(k / BK);
   constexpr int BM = WAVES_M * 32 * WMF, BN = (WAVES / WAVES_M) * 32 * WNF;
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  auto kern = k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES>;
-  kern<<<dim3((unsigned)tiles), WAVES * 64, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed),
-                                                         gamma, xq, absmax, (int)t, (int)n,
-                                                         (int)k, y, acc);
+  auto kern = splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true>
+                         : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false>;
+  kern<<<dim3((unsigned)(tiles * splits)), WAVES * 64, 0, stream>>>(
+      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc,
+      ksteps, splits);
   return hipGetLastError();
 }
 
@@ -467,32 +510,50 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_LDS_MIN_TILES
 #define BL_GEMM_LDS_MIN_TILES 128   // LDS-direct tiles from this many tiles on
 #endif
+#ifndef BL_GEMM_WIDE_MIN_TILES
+#define BL_GEMM_WIDE_MIN_TILES 192  // 128 x 512 tiles when they keep this many CUs busy
+#endif
 #ifndef BL_GEMM_STAGES
 #define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
 #endif
-#ifndef BL_GEMM_WAVES
-#define BL_GEMM_WAVES 8             // waves per block of the LDS-direct kernel
+#ifndef BL_GEMM_SPLIT_ITEMS
+#define BL_GEMM_SPLIT_ITEMS 256     // K split: (part, tile) items aimed for
 #endif
-#ifndef BL_GEMM_WAVES_M
-#define BL_GEMM_WAVES_M 1           // waves along M (the rest along N)
-#endif
-#ifndef BL_GEMM_WMF
-#define BL_GEMM_WMF 4               // 32-row fragments per wave
-#endif
-#ifndef BL_GEMM_WNF
-#define BL_GEMM_WNF 2               // 32-column fragments per wave
+#ifndef BL_GEMM_SPLIT_MIN_OPS
+#define BL_GEMM_SPLIT_MIN_OPS 17179869184.0   // K split only from 2*T*N*K = 2^34 on
 #endif
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
-  constexpr int kLdsBM = BL_GEMM_WAVES_M * 32 * BL_GEMM_WMF;
-  constexpr int kLdsBN = (BL_GEMM_WAVES / BL_GEMM_WAVES_M) * 32 * BL_GEMM_WNF;
-  const int64_t lds_tiles = ((n + kLdsBN - 1) / kLdsBN) * ((t + kLdsBM - 1) / kLdsBM);
-  if (k % BK == 0 && lds_tiles >= BL_GEMM_LDS_MIN_TILES && t * k < (int64_t(1) << 31) &&
-      n * (k / 16) < (int64_t(1) << 31))
-    return run_lds<BL_GEMM_WAVES, BL_GEMM_WAVES_M, BL_GEMM_WMF, BL_GEMM_WNF, BL_GEMM_STAGES>(
-        packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+  // LDS-direct tiles: 8 waves of 128 x 64 (128 x 512) where the grid is wide
+  // enough, else 4 waves (128 x 256), which fill twice as many CUs, else the
+  // 128 x 512 tiles with K split into parts when the problem is large
+  const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
+  const int64_t mt = (t + 127) / 128;
+  const int64_t wide = mt * ((n + 511) / 512), narrow = mt * ((n + 255) / 256);
+  if (lds_ok && wide >= BL_GEMM_WIDE_MIN_TILES)
+    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+  if (lds_ok && narrow >= BL_GEMM_LDS_MIN_TILES)
+    return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+  const int64_t nkt = k / BK;
+  if (lds_ok && nkt >= 8 && 2.0 * (double)t * (double)n * (double)k >= BL_GEMM_SPLIT_MIN_OPS &&
+      t * n < (int64_t(1) << 31)) {
+    int64_t parts = (BL_GEMM_SPLIT_ITEMS + wide - 1) / wide;
+    int64_t steps = (nkt + parts - 1) / parts;
+    if (steps < 4) steps = 4;
+    parts = (nkt + steps - 1) / steps;             // every part has at least one step
+    const int64_t total = t * n;
+    k_clear_i32<<<(unsigned)std::min<int64_t>((total + 255) / 256, 4096), 256, 0, stream>>>(
+        reinterpret_cast<int*>(y), total);
+    hipError_t e = run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                       stream, (int)parts, (int)steps);
+    if (e != hipSuccess) return e;
+    const int col_blocks = (int)((n + 1023) / 1024);
+    k_split_finish<<<(unsigned)(t * col_blocks), 256, 0, stream>>>(y, acc, gamma, absmax, (int)n,
+                                                                   col_blocks);
+    return hipGetLastError();
+  }
   const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
   if (big >= BL_GEMM_BIG_MIN_TILES)
     return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);

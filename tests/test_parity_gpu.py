@@ -192,7 +192,10 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               (1, 2560, 2560), (8, 640, 2560), (1, 100, 6912), (5, 37, 28672),
               # decode kernel edges: ragged N, T = 16 at the staging limit,
               # many waves per block, one chunk per wave
-              (3, 37, 512), (16, 50, 2048), (2, 17, 8192), (1, 3, 256), (1, 1000, 28672)]
+              (3, 37, 512), (16, 50, 2048), (2, 17, 8192), (1, 3, 256), (1, 1000, 28672),
+              # prefill kernel: K split into 38 parts (the last one short) on
+              # ragged T and N; the 128 x 256 tiles; the 128 x 512 tiles
+              (200, 1500, 28672), (1100, 3800, 512), (1500, 8100, 256)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
