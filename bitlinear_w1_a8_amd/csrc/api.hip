@@ -11,8 +11,6 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// T at or below which BL_ALGO_AUTO picks the decode kernel.
-constexpr int64_t kGemvMaxTokens = 64;
 constexpr int64_t kMaxT = int64_t(1) << 24;
 constexpr int64_t kMaxN = int64_t(1) << 26;
 constexpr int64_t kMaxNK = int64_t(1) << 38;  // keeps every gamma bucket below 2^62
@@ -51,7 +49,7 @@ int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
 
 const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
 
-int64_t bitlinear_gemv_max_tokens(void) { return kGemvMaxTokens; }
+int64_t bitlinear_gemv_max_tokens(void) { return bl::kGemvMaxTokens; }
 
 size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
   (void)N;
@@ -103,7 +101,7 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
   if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
       !aligned(y, 4) || (acc && !aligned(acc, 4)))
     return fail(BL_ERR_ALIGN, "%s: packed and xq need 16-byte, the others 4-byte alignment", fn);
-  if (algo == BL_ALGO_AUTO) algo = T <= kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
+  if (algo == BL_ALGO_AUTO) algo = T <= bl::kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (algo == BL_ALGO_GEMV)
     return launched(fn, bl::launch_gemv(packed, gamma, xq, absmax, T, N, K, y, acc, s));

@@ -14,6 +14,11 @@ namespace bl {
 constexpr float kEps = 1e-5f;
 constexpr float kQb = 127.0f;
 
+// T at or below which the automatic choice takes the decode kernel: measured
+// on 2560->6912 and 6912->2560, it is faster through T = 128 and the tiled
+// MFMA kernel from T = 256 on.
+constexpr int64_t kGemvMaxTokens = 128;
+
 // Exponent buckets of the exact gamma sum: one uint64 per binary32 exponent.
 constexpr int kGammaBuckets = 256;
 constexpr size_t kPackWorkspaceBytes = kGammaBuckets * sizeof(unsigned long long);

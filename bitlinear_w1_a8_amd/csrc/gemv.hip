@@ -677,12 +677,14 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
             (reinterpret_cast<uintptr_t>(probs[i].x) % 16) == 0 &&
             (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
   }
-  if (!fused) {  // act-quant then forward, problem by problem
+  if (!fused) {  // act-quant then forward (kernel chosen by T), problem by problem
     for (int i = 0; i < count; ++i) {
       const bl_linear& q = probs[i];
       hipError_t e = launch_quant(q.x, bf16, t, q.K, q.xq, q.absmax, nullptr, stream);
       if (e != hipSuccess) return e;
-      e = launch_gemv(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream);
+      e = t <= kGemvMaxTokens
+              ? launch_gemv(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream)
+              : launch_gemm(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -311,6 +311,10 @@ GROUPS = {
     "eight_problems": (2, "bf16", [(256 * (i + 1), 16 * (i + 1) + 3) for i in range(8)]),
     "fallback_t8": (8, "bf16", [(2560, 200), (512, 33)]),
     "fallback_k_not_256": (2, "f32", [(48, 20), (256, 16)]),
+    # T above the decode range: act-quant, then the tiled MFMA kernel
+    "fallback_t300_gemm": (300, "bf16", [(512, 700), (1024, 300)]),
+    # one token, enough row blocks that each of 4 waves owns 8 chunks
+    "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(8192, 26300)]),
 }
 
 
