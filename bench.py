@@ -17,8 +17,10 @@ same layer as 14 separate launches (act-quant, then forward, per projection)
 is reported beside it.
 
 The JSON line reports algorithmic GB/s of the whole step (value), the decode
-GEMV kernel against the HBM roofline, the CPU oracle timed on a bounded
-sample, and, as extra context, the prefill GEMM (T = 2048) in int8 TOP/s.
+kernel against the HBM roofline, the CPU oracle timed on a bounded sample,
+and, as extra context: the prefill GEMM (T = 2048) in int8 TOP/s, the batched
+decode crossover between the decode kernel and the tiled MFMA kernel, and the
+70B-class shapes at T = 1 (GB/s) and T = 256 (TOP/s).
 """
 
 import argparse
@@ -210,9 +212,102 @@ def cpu_baseline(oracle, wl, budget_s=12.0):
                       f"rescale) in {el:.1f} s; weights ternarised beforehand"}
 
 
+def rotated_time_us(torch, body, n, stream, reps=10):
+    """Microseconds per call of body(stream, i) for i over n rotated copies,
+    from HIP events over graph replays of all n calls."""
+    g = capture(torch, lambda s: [body(s, i) for i in range(n)], stream)
+    return time_graph(torch, g, reps, 2, stream) * 1e3 / (reps * n)
+
+
+def big_extra(torch, binding, wl, dev, stream):
+    """Context: the 70B-class shapes (8192->28672, 28672->8192) at T = 1
+    (GB/s of act-quant fused with the decode kernel, and of the decode kernel
+    alone on int8 input) and at T = 256 (TOP/s of act-quant + tiled MFMA
+    kernel), weights rotated over > 1 GB.  The latent weights are drawn on the
+    GPU (N(0, 0.01), seeded) and packed there: only their code distribution
+    matters for the timing."""
+    wk = wl.WORKLOADS[5]
+    lib = binding.load()
+    calls = Calls(lib)
+    out = {}
+    for mi, m in enumerate(wk.matrices):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5000 + mi)
+        w = torch.randn((m.n, m.k), device=dev, generator=gen) * 0.01
+        packed, gamma = binding.pack_weights(w)
+        del w
+        copies = [packed] + [packed.clone() for _ in range(int(np.ceil(ROT_BYTES / packed.numel())) - 1)]
+        rec = {"rotated_copies": len(copies)}
+        for t in (1, 256):
+            xg = torch.Generator(device=dev)
+            xg.manual_seed(6000 + 10 * mi + t)
+            x = torch.randn((t, m.k), device=dev, generator=xg).to(torch.bfloat16)
+            xq = torch.empty((t, m.k), dtype=torch.int8, device=dev)
+            am = torch.empty(t, dtype=torch.float32, device=dev)
+            y = torch.empty((t, m.n), dtype=torch.float32, device=dev)
+            descs = []
+            for c in copies:
+                arr = (binding.BlLinear * 1)()
+                arr[0] = binding.BlLinear(x.data_ptr(), c.data_ptr(), gamma.data_ptr(), m.n, m.k,
+                                          y.data_ptr(), xq.data_ptr(), am.data_ptr(), None)
+                descs.append(arr)
+            P = [ptr(c) for c in copies]
+            us_grp = rotated_time_us(
+                torch, lambda s, i: calls.grouped(descs[i], t, ctypes.c_void_p(s.cuda_stream)),
+                len(copies), stream)
+            calls.quant(ptr(x), ptr(xq), ptr(am), t, m.k, ctypes.c_void_p(stream.cuda_stream))
+            us_fwd = rotated_time_us(
+                torch, lambda s, i: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), t, m.n, m.k,
+                                                  ptr(y), 0, ctypes.c_void_p(s.cuda_stream)),
+                len(copies), stream)
+            if t == 1:
+                rec["t1_act_quant_plus_forward_us"] = round(us_grp, 2)
+                rec["t1_act_quant_plus_forward_gb_s"] = round(fused_bytes(1, m.n, m.k) / us_grp / 1e3, 1)
+                rec["t1_forward_us"] = round(us_fwd, 2)
+                rec["t1_forward_gb_s"] = round(gemv_bytes(1, m.n, m.k) / us_fwd / 1e3, 1)
+                rec["t1_forward_frac_of_hbm_peak"] = round(gemv_bytes(1, m.n, m.k) / us_fwd / 1e3 / HBM_PEAK_GBS, 4)
+            else:
+                ops = 2.0 * t * m.n * m.k
+                rec["t256_act_quant_plus_forward_us"] = round(us_grp, 2)
+                rec["t256_forward_us"] = round(us_fwd, 2)
+                rec["t256_forward_tops"] = round(ops / us_fwd / 1e6, 1)
+                rec["t256_forward_frac_of_int8_peak"] = round(ops / us_fwd / 1e6 / INT8_PEAK_TOPS, 4)
+        out[f"{m.k}->{m.n}"] = rec
+        del copies, packed
+        torch.cuda.empty_cache()
+    return out
+
+
+def crossover_extra(torch, mats, sets, dev, stream, calls):
+    """Batched decode: the decode kernel against the tiled MFMA kernel on
+    2560->6912 and 6912->2560 for T in {1, 8, 32, 64, 128, 256} (int8 input,
+    weights rotated over the layer sets); T* is the largest T at which the
+    decode kernel is still the faster."""
+    out = {}
+    for mi in (4, 6):
+        d = mats[mi]
+        n, k = d["m"].n, d["m"].k
+        rows = {}
+        for t in (1, 8, 32, 64, 128, 256):
+            xq = torch.randint(-127, 128, (t, k), dtype=torch.int8, device=dev)
+            am = torch.rand(t, device=dev) * 4 + 1
+            y = torch.empty((t, n), dtype=torch.float32, device=dev)
+            P = [ptr(s_[mi]) for s_ in sets]
+            us = [rotated_time_us(
+                torch, lambda s, i, a=algo: calls.forward(P[i], ptr(d["gamma"]), ptr(xq), ptr(am), t,
+                                                          n, k, ptr(y), a, ctypes.c_void_p(s.cuda_stream)),
+                len(sets), stream, reps=5) for algo in (1, 2)]
+            rows[str(t)] = {"decode_kernel_us": round(us[0], 2), "tiled_mfma_us": round(us[1], 2)}
+        tstar = max([int(t) for t, r in rows.items() if r["decode_kernel_us"] <= r["tiled_mfma_us"]] + [0])
+        out[f"{k}->{n}"] = {"by_T": rows, "T_star": tstar}
+    return out
+
+
 def prefill_extra(torch, binding, wl, dev, stream):
-    """Context: prefill GEMM (T = 2048) on both 2B shapes, TOP/s of the GEMM
-    kernel alone and of act-quant + GEMM."""
+    """Context: prefill (T = 2048) on both 2B shapes, TOP/s of the tiled MFMA
+    kernel alone and of act-quant + kernel.  As in a model, where every layer
+    has its own weights, consecutive calls rotate through 64 copies of the
+    packed matrix."""
     wk = wl.WORKLOADS[4]
     lib = binding.load()
     calls = Calls(lib)
@@ -220,33 +315,34 @@ def prefill_extra(torch, binding, wl, dev, stream):
     for mi, m in enumerate(wk.matrices):
         t = 2048
         packed, gamma = binding.pack_weights(torch.from_numpy(wk.weights(mi)).to(dev))
+        copies = [packed] + [packed.clone() for _ in range(63)]
         bits = wl.bf16_bits(wk.activations(mi, t))
         x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
         xq = torch.empty((t, m.k), dtype=torch.int8, device=dev)
         absmax = torch.empty(t, dtype=torch.float32, device=dev)
         y = torch.empty((t, m.n), dtype=torch.float32, device=dev)
-        P = [ptr(v) for v in (packed, gamma, xq, absmax, y, x)]
+        P = [ptr(c) for c in copies]
+        Q = [ptr(v) for v in (gamma, xq, absmax, y, x)]
+        calls.quant(Q[4], Q[1], Q[2], t, m.k, ctypes.c_void_p(stream.cuda_stream))
+        us1 = rotated_time_us(
+            torch, lambda s, i: calls.forward(P[i], Q[0], Q[1], Q[2], t, m.n, m.k, Q[3], 2,
+                                              ctypes.c_void_p(s.cuda_stream)),
+            len(copies), stream, reps=4)
 
-        def gemm_only(s, P=P, m=m):
+        def both(s, i):
             h = ctypes.c_void_p(s.cuda_stream)
-            calls.forward(P[0], P[1], P[2], P[3], t, m.n, m.k, P[4], 2, h)
+            calls.quant(Q[4], Q[1], Q[2], t, m.k, h)
+            calls.forward(P[i], Q[0], Q[1], Q[2], t, m.n, m.k, Q[3], 2, h)
 
-        def both(s, P=P, m=m):
-            h = ctypes.c_void_p(s.cuda_stream)
-            calls.quant(P[5], P[2], P[3], t, m.k, h)
-            calls.forward(P[0], P[1], P[2], P[3], t, m.n, m.k, P[4], 2, h)
-
-        reps = 50
-        g1 = capture(torch, gemm_only, stream)
-        ms1 = time_graph(torch, g1, reps, 5, stream) / reps
-        g2 = capture(torch, both, stream)
-        ms2 = time_graph(torch, g2, reps, 5, stream) / reps
+        us2 = rotated_time_us(torch, both, len(copies), stream, reps=4)
         ops = 2.0 * t * m.n * m.k
         out[f"{m.k}->{m.n}"] = {
-            "gemm_us": round(ms1 * 1e3, 2), "gemm_tops": round(ops / ms1 / 1e9, 1),
-            "gemm_frac_of_int8_peak": round(ops / ms1 / 1e9 / INT8_PEAK_TOPS, 4),
-            "quant_plus_gemm_us": round(ms2 * 1e3, 2),
-            "quant_plus_gemm_tops": round(ops / ms2 / 1e9, 1)}
+            "gemm_us": round(us1, 2), "gemm_tops": round(ops / us1 / 1e6, 1),
+            "gemm_frac_of_int8_peak": round(ops / us1 / 1e6 / INT8_PEAK_TOPS, 4),
+            "quant_plus_gemm_us": round(us2, 2),
+            "quant_plus_gemm_tops": round(ops / us2 / 1e6, 1)}
+        del copies, packed
+        torch.cuda.empty_cache()
     return out
 
 
@@ -382,6 +478,8 @@ def main():
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     if not args.no_extra:
         extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
+        extra["batched_decode_crossover"] = crossover_extra(torch, mats, sets, dev, stream, calls)
+        extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
 
     cpu = None
     if not args.no_cpu:

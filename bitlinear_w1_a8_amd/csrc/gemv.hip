@@ -589,6 +589,9 @@ namespace {
 #ifndef BL_GEMV_DEC_RAWLDS
 #define BL_GEMV_DEC_RAWLDS 32768  // largest raw activation bytes (fused act-quant) in LDS
 #endif
+#ifndef BL_GEMV_FUSE_MAX_WORK
+#define BL_GEMV_FUSE_MAX_WORK (4 << 20)   // largest sum of blocks x K quantised in fused launches
+#endif
 
 // Launch shape of the decode kernel for a group of `blocks` 16-row tiles
 // whose widest K is kmax: nw waves per block, each owning at most cpw
@@ -671,12 +674,17 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
 hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int bf16,
                                hipStream_t stream) {
   const int rb = bf16 ? 2 : 4;   // bytes per raw activation
+  // Fused, every block quantises the whole activation rows again: worth it
+  // while that redundant work stays below a separate act-quant launch
   bool fused = count <= kMaxGroup;
+  int64_t work = 0;
   for (int i = 0; fused && i < count; ++i) {
     fused = dec_shape_ok(t, probs[i].K, rb) &&
             (reinterpret_cast<uintptr_t>(probs[i].x) % 16) == 0 &&
             (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
+    work += (probs[i].N + 15) / 16 * probs[i].K;
   }
+  if (work > BL_GEMV_FUSE_MAX_WORK) fused = false;
   if (!fused) {  // act-quant then forward (kernel chosen by T), problem by problem
     for (int i = 0; i < count; ++i) {
       const bl_linear& q = probs[i];

@@ -178,9 +178,11 @@ typedef struct bl_linear {
  * by bitlinear_forward on each problem (same operations, same rounding), for
  * callers that run several projections of one layer back to back (e.g. the
  * query/key/value or gate/up projections of a decoder layer).  For decode
- * shapes (T <= 4, K % 256 == 0, T*K <= 32768) one kernel does all of it:
- * each block quantises the activations it needs in LDS, then streams its
- * weight rows; otherwise the steps run per problem.
+ * shapes (T <= 4, K % 256 == 0, raw activation rows of at most 32 KiB, and a
+ * modest total of weight rows times K) one kernel does all of it: each block
+ * quantises the activations it needs in LDS, then streams its weight rows;
+ * otherwise the steps run per problem (act-quant, then the kernel that
+ * bitlinear_forward would choose).
  *
  *   problems  HOST array of `count` descriptors (read during the call only).
  *   T         1 <= T <= 2^24 tokens, the same for every problem.

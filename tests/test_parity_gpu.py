@@ -313,8 +313,10 @@ GROUPS = {
     "fallback_k_not_256": (2, "f32", [(48, 20), (256, 16)]),
     # T above the decode range: act-quant, then the tiled MFMA kernel
     "fallback_t300_gemm": (300, "bf16", [(512, 700), (1024, 300)]),
-    # one token, enough row blocks that each of 4 waves owns 8 chunks
-    "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(8192, 26300)]),
+    # one token, K = 16384: 8 waves of 8 chunks each in the fused kernel
+    "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(16384, 300)]),
+    # many row blocks: over the fused-work limit, act-quant runs separately
+    "t1_bf16_many_blocks": (1, "bf16", [(8192, 8200), (8192, 8200)]),
 }
 
 
