@@ -18,3 +18,9 @@ from .bitlinear_ref import (  # noqa: F401
     ternarize,
     widen_bf16,
 )
+from .subln_ref import (  # noqa: F401
+    EPS_N,
+    rms_factor,
+    subln_plain,
+    subln_quant_act,
+)

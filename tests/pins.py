@@ -362,4 +362,77 @@ def pin_rescale(o):
     assert y[1, 2] == 0.0
 
 
+# ------------------------------------------------------------ SubLN + act-quant
+
+def pin_e6_subln(o):
+    e = GOLD["E6_subln"]
+    x = np.array(e["x"], np.float32)
+    q, scale, rowsum, a = o.subln_quant_act(x, np.array(e["gain"], np.float32), e["eps_n"])
+    assert q.tolist() == e["q"]
+    assert rowsum.tolist() == e["rowsum"]
+    assert a.tolist() == e["a"]
+    assert np.allclose(scale, e["scale"], rtol=1e-15, atol=0.0)
+
+
+def pin_subln_unit_gain_is_act_quant(o):
+    # with g = 1 the codes are step A1's of x itself
+    rng = np.random.default_rng(61)
+    x = (rng.standard_t(4, size=(7, 96)) * 3).astype(np.float32)
+    x[2] = 0.0
+    q, scale, rowsum, a = o.subln_quant_act(x, np.ones(96, np.float32))
+    q1, a1, r1 = o.quant_act(x)
+    assert np.array_equal(q, q1) and np.array_equal(a, a1) and np.array_equal(rowsum, r1)
+
+
+def pin_subln_closed_form(o):
+    # constant rows c with g = 1: every code is +-127 and the scale is
+    # |c| / sqrt(c^2 + eps) (a single correctly rounded binary64 expression)
+    cs = [1.0, -2.5, 3e-3, 1000.0, -0.0625]
+    x = np.array([[c] * 64 for c in cs], np.float32)
+    q, scale, _, _ = o.subln_quant_act(x, np.ones(64, np.float32), 1e-5)
+    for i, c in enumerate(cs):
+        c32 = float(np.float32(c))
+        assert set(q[i].tolist()) == {127 if c > 0 else -127}
+        want = abs(c32) / math.sqrt(c32 * c32 + 1e-5)
+        assert abs(float(scale[i]) - want) <= 1e-15 * want
+
+
+def pin_subln_zero_row(o):
+    x = np.zeros((2, 32), np.float32)
+    x[1, 3] = 1.0
+    q, scale, rowsum, a = o.subln_quant_act(x, np.full(32, 2.0, np.float32))
+    assert not q[0].any() and float(scale[0]) == 0.0 and int(rowsum[0]) == 0
+    assert np.all(np.isfinite(scale))
+
+
+def pin_subln_rms_of_x(o):
+    # the root mean square is taken over x, before the gain: with g = 4 the
+    # codes are those of x, and the scale is 4 * max|x| / rms(x), computed
+    # here with exact sums
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((3, 40)).astype(np.float32)
+    q, scale, _, _ = o.subln_quant_act(x, np.full(40, 4.0, np.float32), 1e-5)
+    q1, _, _ = o.quant_act(x)
+    assert np.array_equal(q, q1)
+    for t in range(3):
+        ms = math.fsum(float(v) * float(v) for v in x[t]) / 40
+        want = 4.0 * float(np.max(np.abs(x[t]))) / math.sqrt(ms + 1e-5)
+        assert abs(float(scale[t]) - want) <= 1e-12 * want
+
+
+def pin_subln_matches_literal_norm(o):
+    # against normalise-then-quantise written out in binary64: the codes may
+    # differ only where binary32 and binary64 round a product to different
+    # sides of a .5 boundary (rare, and by one); the scales agree to the
+    # binary32 rounding of x * g
+    rng = np.random.default_rng(63)
+    x = rng.standard_t(4, size=(64, 512)).astype(np.float32)
+    g = (1.0 + 0.3 * rng.standard_normal(512)).astype(np.float32)
+    q, scale, _, _ = o.subln_quant_act(x, g)
+    qp, mp = o.subln_plain(x, g)
+    d = np.abs(q.astype(np.int32) - qp.astype(np.int32))
+    assert d.max() <= 1 and np.count_nonzero(d) <= q.size // 1000
+    assert np.allclose(scale, mp, rtol=2e-7, atol=0.0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

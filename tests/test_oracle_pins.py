@@ -149,7 +149,38 @@ def _rescale_no_floor(acc, gamma, absmax):
     return np.asarray(acc, np.float64) * np.float64(gamma) * m[:, None] / 127.0
 
 
+def _subln(x, gain, eps_n=oracle.EPS_N, *, use_gain=True, rms_of="x", eps=True, scale_op="mul",
+           gain_in_codes=True, mean_abs=False):
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        x = oracle.widen_bf16(x)
+    x = np.asarray(x, np.float32)
+    g = np.asarray(gain, np.float32)
+    u = x * g[None, :] if use_gain else x
+    q, a, rowsum = oracle.quant_act(u if gain_in_codes else x)
+    if not gain_in_codes:
+        a = np.max(np.abs(u), axis=1).astype(np.float32)
+    src = (u if rms_of == "u" else x).astype(np.float64)
+    ms = np.mean(np.abs(src), axis=1) if mean_abs else np.mean(src * src, axis=1)
+    r = 1.0 / (ms + (eps_n if eps else 0.0)) if mean_abs else 1.0 / np.sqrt(ms + (eps_n if eps else 0.0))
+    with np.errstate(all="ignore"):
+        scale = a.astype(np.float64) * r if scale_op == "mul" else (
+            a.astype(np.float64) / r if scale_op == "div" else a.astype(np.float64))
+    return q, scale, rowsum, a
+
+
+def _subln_mutant(**kw):
+    return lambda x, gain, eps_n=oracle.EPS_N: _subln(x, gain, eps_n, **kw)
+
+
 MUTANTS = {
+    "subln_no_gain": dict(subln_quant_act=_subln_mutant(use_gain=False)),
+    "subln_rms_of_x_times_g": dict(subln_quant_act=_subln_mutant(rms_of="u")),
+    "subln_no_eps": dict(subln_quant_act=_subln_mutant(eps=False)),
+    "subln_scale_without_rms": dict(subln_quant_act=_subln_mutant(scale_op="none")),
+    "subln_scale_divided_by_rms": dict(subln_quant_act=_subln_mutant(scale_op="div")),
+    "subln_gain_only_in_scale": dict(subln_quant_act=_subln_mutant(gain_in_codes=False)),
+    "subln_mean_abs_not_rms": dict(subln_quant_act=_subln_mutant(mean_abs=True)),
     "gamma_per_row": dict(absmean_gamma=_per_row_gamma),
     "gamma_f32_running_sum": dict(absmean_gamma=_f32_sum_gamma),
     "gamma_f64_running_sum": dict(absmean_gamma=_f64_sequential_gamma),
