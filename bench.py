@@ -219,6 +219,46 @@ def rotated_time_us(torch, body, n, stream, reps=10):
     return time_graph(torch, g, reps, 2, stream) * 1e3 / (reps * n)
 
 
+def subln_extra(torch, binding, dev, stream):
+    """The sub-layer norm fused with act-quant against act-quant alone: bf16
+    rows of K in {2560, 6912} at T in {1, 2048}, over 64 distinct activation
+    buffers per graph; GB/s of algorithmic bytes (x and gain in, int8 codes,
+    scale and row sum out) against the 8 TB/s HBM peak."""
+    lib = binding.load()
+    out = {}
+    for t, k in ((1, 2560), (1, 6912), (2048, 2560), (2048, 6912)):
+        n = 64 if t == 1 else 8
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7000 + t + k)
+        xs = [torch.randn((t, k), device=dev, generator=gen).to(torch.bfloat16) for _ in range(n)]
+        gain = (1.0 + 0.3 * torch.randn(k, device=dev, generator=gen)).float()
+        xq = torch.empty((t, k), dtype=torch.int8, device=dev)
+        sc = torch.empty(t, dtype=torch.float32, device=dev)
+        rs = torch.empty(t, dtype=torch.int32, device=dev)
+
+        def norm(s, i):
+            rc = lib.bitlinear_subln_quant_act(ptr(xs[i]), 1, ptr(gain), 1e-5, t, k, ptr(xq), ptr(sc),
+                                               ptr(rs), ctypes.c_void_p(s.cuda_stream))
+            if rc:
+                raise RuntimeError(lib.bitlinear_last_error().decode())
+
+        def plain(s, i):
+            rc = lib.bitlinear_quant_act(ptr(xs[i]), 1, t, k, ptr(xq), ptr(sc), ptr(rs),
+                                         ctypes.c_void_p(s.cuda_stream))
+            if rc:
+                raise RuntimeError(lib.bitlinear_last_error().decode())
+
+        us_n = rotated_time_us(torch, norm, n, stream)
+        us_p = rotated_time_us(torch, plain, n, stream)
+        byts = 2 * t * k + 4 * k + t * k + 8 * t
+        out[f"T{t}_K{k}"] = {"subln_quant_us": round(us_n, 2),
+                             "subln_quant_gb_s": round(byts / us_n / 1e3, 1),
+                             "subln_frac_of_hbm_peak": round(byts / us_n / 1e3 / HBM_PEAK_GBS, 4),
+                             "act_quant_alone_us": round(us_p, 2)}
+        del xs
+    return out
+
+
 def big_extra(torch, binding, wl, dev, stream):
     """Context: the 70B-class shapes (8192->28672, 28672->8192) at T = 1
     (GB/s of act-quant fused with the decode kernel, and of the decode kernel
@@ -480,6 +520,7 @@ def main():
         extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
         extra["batched_decode_crossover"] = crossover_extra(torch, mats, sets, dev, stream, calls)
         extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
+        extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
 
     cpu = None
     if not args.no_cpu:

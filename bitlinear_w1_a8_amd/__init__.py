@@ -5,7 +5,8 @@ ABI of include/bitlinear.h); ``binding`` marshals torch tensors to it.  The
 names below load the library on first use and fail loudly if it is missing.
 """
 
-_EXPORTS = ("pack_weights", "quant_act", "forward", "bitlinear", "linear_grouped", "gemv_max_tokens",
+_EXPORTS = ("pack_weights", "quant_act", "subln_quant_act", "forward", "bitlinear", "linear_grouped",
+            "gemv_max_tokens",
             "BitLinearError", "load", "last_error")
 
 

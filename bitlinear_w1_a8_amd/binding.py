@@ -30,6 +30,8 @@ SIGNATURES = {
     "bitlinear_pack_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "bitlinear_pack_weights": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "bitlinear_quant_act": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "bitlinear_subln_quant_act": (_c_int, [_c_vp, _c_int, _c_vp, ctypes.c_float, _c_i64, _c_i64,
+                                           _c_vp, _c_vp, _c_vp, _c_vp]),
     "bitlinear_forward": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp,
                                    _c_vp, _c_vp]),
     "bitlinear_forward_algo": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
@@ -131,6 +133,28 @@ def quant_act(x, with_rowsum=True):
     _check(lib.bitlinear_quant_act(_ptr(x), dt, t, k, _ptr(xq), _ptr(absmax), _ptr(rowsum),
                                    _stream(x.device)))
     return xq, absmax, rowsum
+
+
+def subln_quant_act(x, gain, eps_n=1e-5, with_rowsum=True):
+    """Sub-layer norm (RMS with per-feature gain) fused with step A1 on the GPU:
+    x[T, K] (float32 or bfloat16), gain float32[K] -> (xq int8, scale f32[T],
+    rowsum i32[T] or None); scale takes the place of absmax in forward()."""
+    lib = load()
+    _need_cuda(x, "x")
+    _need_cuda(gain, "gain", torch.float32)
+    if x.dtype == torch.float32:
+        dt = BL_F32
+    elif x.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    t, k = x.shape
+    xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
+    scale = torch.empty(t, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(t, dtype=torch.int32, device=x.device) if with_rowsum else None
+    _check(lib.bitlinear_subln_quant_act(_ptr(x), dt, _ptr(gain), float(eps_n), t, k, _ptr(xq),
+                                         _ptr(scale), _ptr(rowsum), _stream(x.device)))
+    return xq, scale, rowsum
 
 
 def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None, acc_out=None):

@@ -5,6 +5,8 @@
 #include <string>
 
 #include "bitlinear.h"
+#include <cmath>
+
 #include "bl_internal.h"
 
 namespace {
@@ -86,6 +88,25 @@ int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t
     return fail(BL_ERR_ALIGN, "%s: x and xq need 16-byte, absmax and rowsum 4-byte alignment", fn);
   return launched(fn, bl::launch_quant(x, x_dtype == BL_BF16, T, K, xq, absmax, rowsum,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
+                              int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
+                              void* stream) {
+  const char* fn = "bitlinear_subln_quant_act";
+  if (!x || !gain || !xq || !scale) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (x_dtype != BL_F32 && x_dtype != BL_BF16)
+    return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (!(eps_n > 0.0f) || !std::isfinite(eps_n))
+    return fail(BL_ERR_ARG, "%s: eps_n must be finite and > 0", fn);
+  if (int rc = check_k(fn, K)) return rc;
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  if (!aligned(x, 16) || !aligned(gain, 16) || !aligned(xq, 16) || !aligned(scale, 4) ||
+      (rowsum && !aligned(rowsum, 4)))
+    return fail(BL_ERR_ALIGN, "%s: x, gain and xq need 16-byte, scale and rowsum 4-byte alignment",
+                fn);
+  return launched(fn, bl::launch_subln_quant(x, x_dtype == BL_BF16, gain, eps_n, T, K, xq, scale,
+                                             rowsum, static_cast<hipStream_t>(stream)));
 }
 
 int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,

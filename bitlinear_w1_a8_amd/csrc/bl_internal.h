@@ -29,6 +29,12 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, fl
 hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
                         float* absmax, int32_t* rowsum, hipStream_t stream);
 
+// Sub-layer norm (RMS with gain) in front of step A1; scale[t] gets the
+// token's dequantisation absmax r * max|x * g|.
+hipError_t launch_subln_quant(const void* x, int bf16, const float* gain, float eps_n, int64_t t,
+                              int64_t k, int8_t* xq, float* scale, int32_t* rowsum,
+                              hipStream_t stream);
+
 // Decode kernel: handles any T by taking tokens 64 at a time.
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,

@@ -136,6 +136,33 @@ int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed
 int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
                         float* absmax, int32_t* rowsum, void* stream);
 
+/* The sub-layer norm in front of step A1, fused with it.  The 2B4T report
+ * (section 2) puts subln before the quantised projections and drops every
+ * bias; the explainer's component table lists it in place of RMSNorm /
+ * LayerNorm.  No page gives its formula; it is taken here as an RMS norm with
+ * a per-feature gain g and no bias:
+ *   x_hat[t,k] = x[t,k] * g[k] / sqrt(mean_k x[t,k]^2 + eps_n).
+ * Per-token absmax quantisation cancels the positive per-token factor
+ * r = 1 / sqrt(mean_k x^2 + eps_n), so the result is step A1 applied to
+ * u = x * g (one binary32 product per element), with the token's scale
+ * r * max_k |u| in place of the absmax:
+ *   xq[t,k]  = clamp(round_half_even(u * (127 / max(max|u|, eps))), -127, 127),
+ *   scale[t] = r * max_k |u[t,k]|  (sum of squares in binary64; binary32 out).
+ * scale takes the place of absmax in bitlinear_forward.
+ *
+ *   x        [T, K] activations of dtype x_dtype (BL_F32 or BL_BF16), 16-byte aligned.
+ *   gain     [K] float32 per-feature gain (device), 16-byte aligned.
+ *   eps_n    the norm's epsilon, finite and > 0 (1e-5 is this library's reading).
+ *   T, K     1 <= T <= 2^24, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
+ *   xq       [T, K] int8 output, 16-byte aligned.
+ *   scale    [T] float32 output, 4-byte aligned.
+ *   rowsum   [T] int32 output sum_k xq[t,k], or NULL.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_ARG
+ * (eps_n), BL_ERR_HIP. */
+int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
+                              int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
+                              void* stream);
+
 /* Steps A2 and A3: y[t, n] = (sum_k t[n,k] * xq[t,k]) * gamma * max(absmax[t], eps) / 127.
  * The contraction follows "BitNet解读", computational efficiency (ternary
  * weights turn products into add, subtract or skip) and is exact in int32;

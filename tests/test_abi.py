@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for name in names:
         assert hasattr(lib, name), name
 
@@ -106,6 +106,22 @@ def test_forward_errors(lib):
     assert f(*good, 1, 16, 64, A16, None, 3, None) == BL_ERR_ARG
     assert f(*good, 1, 16, 64, A16, None, -1, None) == BL_ERR_ARG
     assert lib.bitlinear_forward(None, A16, A16, A16, 1, 16, 64, A16, None, None) == BL_ERR_NULL
+
+
+def test_subln_quant_act_errors(lib):
+    f = lib.bitlinear_subln_quant_act
+    ok = (A16, 1, A16, 1e-5, 4, 64, A16, A16, None, None)
+    assert f(None, *ok[1:]) == BL_ERR_NULL
+    assert f(ok[0], ok[1], None, *ok[3:]) == BL_ERR_NULL
+    assert f(*ok[:7], None, None, None) == BL_ERR_NULL
+    assert f(ok[0], 5, *ok[2:]) == BL_ERR_DTYPE
+    for bad in (0.0, -1e-5, float("inf"), float("nan")):
+        assert f(*ok[:3], bad, *ok[4:]) == BL_ERR_ARG
+    assert f(*ok[:4], 4, 72, *ok[6:]) == BL_ERR_SHAPE       # K % 16
+    assert f(*ok[:4], 0, 64, *ok[6:]) == BL_ERR_SHAPE
+    assert f(ok[0], ok[1], A16 + 4, *ok[3:]) == BL_ERR_ALIGN  # gain read 16 bytes at a time
+    assert f(*ok[:7], A16 + 2, None, None) == BL_ERR_ALIGN
+    assert "eps_n" in (f(*ok[:3], 0.0, *ok[4:]) and _err(lib))
 
 
 def test_last_error_is_per_thread(lib):

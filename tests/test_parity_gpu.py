@@ -299,6 +299,54 @@ def test_workload_full_size(bl, widx, mi):
         assert abs(float(np.mean(tern == 0)) - 0.3101) < 0.005
 
 
+# ------------------------------------------------------------------ SubLN + A1
+
+SUBLN_CASES = [(1, 2560, "bf16"), (4, 6912, "bf16"), (3, 256, "f32"), (2048, 2560, "bf16"),
+               (5, 28672, "bf16"), (7, 48, "f32"), (1, 131072, "bf16"), (65, 4096, "f32")]
+
+
+def _subln_inputs(t, k, dtype, seed):
+    rng = np.random.default_rng(seed)
+    x = wl.activations_student_t(t, k, 4, seed + 1)
+    if t > 2:
+        x[1] = 0.0                                       # an all-zero token
+    g = (1.0 + 0.5 * rng.standard_normal(k)).astype(np.float32)   # some gains negative
+    if dtype == "bf16":
+        bits = wl.bf16_bits(x)
+        return bits, dev_bf16(bits), g
+    return x, dev(x), g
+
+
+@pytest.mark.parametrize("t,k,dtype", SUBLN_CASES, ids=[f"T{t}_K{k}_{d}" for t, k, d in SUBLN_CASES])
+def test_subln_quant(bl, t, k, dtype):
+    xref, xin, g = _subln_inputs(t, k, dtype, 900 + t + k)
+    q_ref, scale_ref, rs_ref, a_ref = oracle.subln_quant_act(xref, g)
+    xq, scale, rowsum = bl.subln_quant_act(xin, dev(g))
+    q = host(xq)
+    bad = int(np.count_nonzero(q != q_ref))
+    assert bad == 0, f"{bad} of {q.size} int8 activations differ"
+    assert np.array_equal(host(rowsum), rs_ref)
+    sc = host(scale).astype(np.float64)
+    zero = a_ref == 0
+    assert np.all(sc[zero] == 0.0)
+    rel = np.abs(sc[~zero] - scale_ref[~zero]) / scale_ref[~zero]
+    assert rel.size == 0 or float(rel.max()) <= 2.5e-7, f"scale off by {rel.max():.3g}"
+
+
+def test_subln_then_forward(bl):
+    t, n, k = 4, 2560, 2560
+    w = wl.latent_weights(n, k, 0.02, 951)
+    packed, gamma, _, gamma_ref = check_pack(bl, w)
+    tern = oracle.ternarize(w, gamma_ref)
+    xref, xin, g = _subln_inputs(t, k, "bf16", 952)
+    q_ref, scale_ref, _, _ = oracle.subln_quant_act(xref, g)
+    xq, scale, _ = bl.subln_quant_act(xin, dev(g))
+    y, acc = bl.forward(packed, gamma, xq, scale, n, want_acc=True)
+    acc_ref = oracle.contract(q_ref, tern)
+    assert np.array_equal(host(acc), acc_ref)
+    check_y(host(y), acc_ref, gamma_ref, scale_ref.astype(np.float32))
+
+
 # ------------------------------------------------------------------ grouped A1-A3
 
 GROUPS = {
