@@ -24,3 +24,10 @@ from .subln_ref import (  # noqa: F401
     subln_plain,
     subln_quant_act,
 )
+from .ffn_ref import (  # noqa: F401
+    bf16_rne,
+    gated_relu2,
+    gated_relu2_plain,
+    out_scale_f32,
+    y_f32,
+)

@@ -435,4 +435,83 @@ def pin_subln_matches_literal_norm(o):
     assert np.allclose(scale, mp, rtol=2e-7, atol=0.0)
 
 
+# ------------------------------------------------------------ gated ReLU^2, bf16
+
+def _bf16_torch(v):
+    import torch   # an independent round-to-nearest-even to bfloat16
+    t = torch.tensor(np.asarray(v, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _gated_scalar(ag, au, gg, gu, a):
+    # the defined binary32 route, one operation at a time: each step in
+    # binary64 on binary32 operands, rounded once to binary32 (exact for +,
+    # -, *, / since 53 >= 2*24 + 2)
+    r32 = lambda v: float(np.float32(v))
+    m = r32(max(float(np.float32(a)), F32_EPS))
+    sg = r32(r32(float(np.float32(gg)) * m) / 127.0)
+    su = r32(r32(float(np.float32(gu)) * m) / 127.0)
+    g = r32(float(ag) * sg)
+    u = r32(float(au) * su)
+    r = max(g, 0.0)
+    return r32(r32(r * r) * u)
+
+
+def pin_e7_gated_relu2(o):
+    e = GOLD["E7_gated_relu2"]
+    h = o.gated_relu2(np.array(e["acc_gate"]), np.array(e["acc_up"]), e["gamma_gate"],
+                      e["gamma_up"], np.array(e["absmax"], np.float32))
+    assert [f"0x{v:04x}" for v in h.ravel().tolist()] == e["h_bf16"]
+
+
+def pin_gated_route(o):
+    # inputs where the order of the two products and a binary64 output scale
+    # change the bfloat16 bits (found by search); expected values from the
+    # scalar route above and torch's rounding
+    gg, gu, a = 0.0173, 0.0291, 3.7
+    ag = np.array([[2483, 2106, 2483, 320, 1280, 1587, 7, 0, 1000]])
+    au = np.array([[-481, 2789, 962, -905, 905, -1840, 5, 100, -1]])
+    h = o.gated_relu2(ag, au, gg, gu, np.array([a], np.float32))
+    want = _bf16_torch([_gated_scalar(x, y, gg, gu, a) for x, y in zip(ag[0], au[0])])
+    assert np.array_equal(h.ravel(), want)
+
+
+def pin_bf16_rne(o):
+    rng = np.random.default_rng(71)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    # exact halfway cases too: bit 15 set, lower bits clear, both parities
+    halves = (rng.integers(0, 1 << 15, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    v = np.concatenate([v, halves[np.isfinite(halves)], np.float32([0.0, -0.0, 1.0, 3.0e38])])
+    assert np.array_equal(o.bf16_rne(v), _bf16_torch(v))
+
+
+def pin_gated_invariants(o):
+    rng = np.random.default_rng(72)
+    ag = rng.integers(-5000, 5000, (4, 300))
+    au = rng.integers(-5000, 5000, (4, 300))
+    a = rng.uniform(0.1, 50, 4).astype(np.float32)
+    h = o.gated_relu2(ag, au, 0.02, 0.03, a)
+    # no output where the gate is not positive
+    assert np.all((h[ag <= 0] & 0x7fff) == 0)
+    # the up output's sign flips only the sign bit
+    assert np.array_equal(o.gated_relu2(ag, -au, 0.02, 0.03, a), h ^ np.uint16(0x8000))
+    # doubling the gate sums is exact and multiplies h by 4 (exponent + 2)
+    h2 = o.gated_relu2(2 * ag, au, 0.02, 0.03, a)
+    nz = (h & 0x7fff) != 0
+    assert np.array_equal(h2[nz], h[nz] + np.uint16(0x0100))
+
+
+def pin_gated_matches_binary64(o):
+    # against ReLU(g)^2 * u in binary64 rounded once to bfloat16: the bits may
+    # differ only at bfloat16 rounding boundaries, by one unit
+    rng = np.random.default_rng(73)
+    ag = rng.integers(-20000, 20000, (16, 2000))
+    au = rng.integers(-20000, 20000, (16, 2000))
+    a = rng.uniform(0.5, 20, 16).astype(np.float32)
+    h = o.gated_relu2(ag, au, 0.0173, 0.0291, a).astype(np.int32)
+    p = _bf16_torch(o.gated_relu2_plain(ag, au, 0.0173, 0.0291, a).astype(np.float32)).astype(np.int32)
+    d = np.abs(h - p)
+    assert d.max() <= 1 and np.count_nonzero(d) <= h.size // 500
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

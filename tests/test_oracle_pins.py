@@ -173,7 +173,53 @@ def _subln_mutant(**kw):
     return lambda x, gain, eps_n=oracle.EPS_N: _subln(x, gain, eps_n, **kw)
 
 
+def _bf16_trunc(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_half_away(x):
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)
+
+
+def _gated(acc_gate, acc_up, gamma_gate, gamma_up, absmax, *, relu=True, square=True, relu_up=False,
+           order="rr_u", scale64=False, rounder=None, swap=False):
+    if swap:
+        acc_gate, acc_up, gamma_gate, gamma_up = acc_up, acc_gate, gamma_up, gamma_gate
+    if scale64:
+        m = np.maximum(np.asarray(absmax, np.float32), oracle.EPS_A).astype(np.float64)
+        g = (np.asarray(acc_gate, np.float64) * (float(np.float32(gamma_gate)) * m / 127)[:, None]).astype(np.float32)
+        u = (np.asarray(acc_up, np.float64) * (float(np.float32(gamma_up)) * m / 127)[:, None]).astype(np.float32)
+    else:
+        g = oracle.y_f32(acc_gate, gamma_gate, absmax)
+        u = oracle.y_f32(acc_up, gamma_up, absmax)
+    r = np.maximum(g, np.float32(0)) if relu else g
+    if relu_up:
+        u = np.maximum(u, np.float32(0))
+    if not square:
+        h = r * u
+    elif order == "rr_u":
+        h = (r * r) * u
+    else:
+        h = r * (r * u)
+    return (rounder or oracle.bf16_rne)(h)
+
+
+def _gated_mutant(**kw):
+    return lambda ag, au, gg, gu, a: _gated(ag, au, gg, gu, a, **kw)
+
+
 MUTANTS = {
+    "gated_no_relu": dict(gated_relu2=_gated_mutant(relu=False)),
+    "gated_not_squared": dict(gated_relu2=_gated_mutant(square=False)),
+    "gated_relu_on_up_too": dict(gated_relu2=_gated_mutant(relu_up=True)),
+    "gated_other_product_order": dict(gated_relu2=_gated_mutant(order="r_ru")),
+    "gated_binary64_scale": dict(gated_relu2=_gated_mutant(scale64=True)),
+    "gated_bf16_truncate": dict(gated_relu2=_gated_mutant(rounder=_bf16_trunc)),
+    "gated_bf16_half_away": dict(gated_relu2=_gated_mutant(rounder=_bf16_half_away)),
+    "gated_gate_up_swapped": dict(gated_relu2=_gated_mutant(swap=True)),
+    "bf16_truncate": dict(bf16_rne=_bf16_trunc),
+    "bf16_half_away": dict(bf16_rne=_bf16_half_away),
     "subln_no_gain": dict(subln_quant_act=_subln_mutant(use_gain=False)),
     "subln_rms_of_x_times_g": dict(subln_quant_act=_subln_mutant(rms_of="u")),
     "subln_no_eps": dict(subln_quant_act=_subln_mutant(eps=False)),
