@@ -6,6 +6,7 @@ names below load the library on first use and fail loudly if it is missing.
 """
 
 _EXPORTS = ("pack_weights", "quant_act", "subln_quant_act", "forward", "bitlinear", "linear_grouped",
+            "interleave_rows", "gated_relu2",
             "gemv_max_tokens",
             "BitLinearError", "load", "last_error")
 

@@ -45,6 +45,9 @@ class BlLinear(ctypes.Structure):
                 ("K", _c_i64), ("y", _c_vp), ("xq", _c_vp), ("absmax", _c_vp), ("acc", _c_vp)]
 
 
+SIGNATURES["bitlinear_interleave_rows"] = (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp])
+SIGNATURES["bitlinear_gated_relu2"] = (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                                _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp])
 SIGNATURES["bitlinear_linear_grouped"] = (_c_int, [ctypes.POINTER(BlLinear), _c_int, _c_i64,
                                                    _c_int, _c_vp])
 
@@ -211,3 +214,45 @@ def linear_grouped(xs, weights, want_acc=False):
         outs.append((y, xq, absmax, acc))
     _check(lib.bitlinear_linear_grouped(descs, len(xs), t, dt, _stream(xs[0].device)))
     return outs
+
+
+def interleave_rows(packed_a, packed_b):
+    """Row interleave of two packed [N, K/4] matrices -> [2N, K/4] (row 2i
+    from a, 2i + 1 from b), the weight layout of gated_relu2."""
+    lib = load()
+    _need_cuda(packed_a, "packed_a", torch.uint8)
+    _need_cuda(packed_b, "packed_b", torch.uint8)
+    if packed_a.shape != packed_b.shape:
+        raise ValueError("the two packed matrices must have the same shape")
+    n, k4 = packed_a.shape
+    out = torch.empty((2 * n, k4), dtype=torch.uint8, device=packed_a.device)
+    _check(lib.bitlinear_interleave_rows(_ptr(packed_a), _ptr(packed_b), n, 4 * k4, _ptr(out),
+                                         _stream(packed_a.device)))
+    return out
+
+
+def gated_relu2(x, packed_gu, gamma_gate, gamma_up, want_acc=False):
+    """Gate and up projections of x [T, K] (float32 or bfloat16) with the
+    squared-ReLU gate, written as bfloat16: returns (h bfloat16 [T, N], xq,
+    absmax, acc int32 [T, 2N] or None); packed_gu from interleave_rows."""
+    lib = load()
+    _need_cuda(x, "x")
+    _need_cuda(packed_gu, "packed_gu", torch.uint8)
+    _need_cuda(gamma_gate, "gamma_gate", torch.float32)
+    _need_cuda(gamma_up, "gamma_up", torch.float32)
+    dt = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    t, k = x.shape
+    n2 = packed_gu.shape[0]
+    if n2 % 2 or packed_gu.shape[1] * 4 != k:
+        raise ValueError("packed_gu must be [2N, K/4]")
+    n = n2 // 2
+    h = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
+    absmax = torch.empty(t, dtype=torch.float32, device=x.device)
+    acc = torch.empty((t, n2), dtype=torch.int32, device=x.device) if want_acc else None
+    _check(lib.bitlinear_gated_relu2(_ptr(x), dt, _ptr(packed_gu), _ptr(gamma_gate),
+                                     _ptr(gamma_up), t, n, k, _ptr(h), _ptr(xq), _ptr(absmax),
+                                     _ptr(acc), _stream(x.device)))
+    return h, xq, absmax, acc

@@ -156,6 +156,40 @@ int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, in
                                               static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
+                              uint8_t* out, void* stream) {
+  const char* fn = "bitlinear_interleave_rows";
+  if (!a || !b || !out) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (int rc = check_k(fn, K)) return rc;
+  if (N < 1 || 2 * N > kMaxN || 2 * N * K > kMaxNK)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out, 4))
+    return fail(BL_ERR_ALIGN, "%s: a, b and out need 4-byte alignment", fn);
+  return launched(fn, bl::launch_interleave(a, b, N, K, out, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
+                          const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
+                          int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
+                          void* stream) {
+  const char* fn = "bitlinear_gated_relu2";
+  if (!x || !packed_gu || !gamma_gate || !gamma_up || !h || !xq || !absmax)
+    return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (x_dtype != BL_F32 && x_dtype != BL_BF16)
+    return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (int rc = check_k(fn, K)) return rc;
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  if (N < 1 || 2 * N > kMaxN || T * 2 * N > kMaxTN)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(x, 16) || !aligned(packed_gu, 16) || !aligned(xq, 16) || !aligned(gamma_gate, 4) ||
+      !aligned(gamma_up, 4) || !aligned(absmax, 4) || !aligned(h, 2) || (acc && !aligned(acc, 4)))
+    return fail(BL_ERR_ALIGN, "%s: x, packed_gu and xq need 16-byte, h 2-byte, the others "
+                "4-byte alignment", fn);
+  return launched(fn, bl::launch_gated(x, x_dtype == BL_BF16, packed_gu, gamma_gate, gamma_up, T,
+                                       2 * N, K, h, xq, absmax, acc,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
                       const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
                       int32_t* acc, void* stream) {

@@ -48,6 +48,28 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream);
 
+// Gate and up projections of one input with the gated ReLU^2 epilogue: the
+// packed matrix holds 2n rows, row 2i of the gate and row 2i+1 of the up
+// projection; h is [t, n / 2] bfloat16; acc, when given, the [t, n] exact sums.
+hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const float* gamma_gate,
+                        const float* gamma_up, int64_t t, int64_t n, int64_t k, uint16_t* h,
+                        int8_t* xq, float* absmax, int32_t* acc, hipStream_t stream);
+
+// The int8-input kernels of the gated path: the decode kernels (t <= 128) and
+// the tiled MFMA kernel.
+hipError_t launch_gemv_gated(const uint8_t* packed, const float* gamma_gate,
+                             const float* gamma_up, const int8_t* xq, const float* absmax,
+                             int64_t t, int64_t n, int64_t k, uint16_t* h, int32_t* acc,
+                             hipStream_t stream);
+hipError_t launch_gemm_gated(const uint8_t* packed, const float* gamma_gate,
+                             const float* gamma_up, const int8_t* xq, const float* absmax,
+                             int64_t t, int64_t n, int64_t k, uint16_t* h, int32_t* acc,
+                             hipStream_t stream);
+
+// Rows of two packed matrices interleaved: out row 2i = a row i, 2i+1 = b row i.
+hipError_t launch_interleave(const uint8_t* a, const uint8_t* b, int64_t n, int64_t k,
+                             uint8_t* out, hipStream_t stream);
+
 // ---------------------------------------------------------------- device helpers
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -62,6 +84,18 @@ __device__ __forceinline__ uint32_t codes_of(uint32_t word, int j) {
 __device__ __forceinline__ float out_scale(float gamma, float absmax) {
   const float m = fmaxf(absmax, kEps);
   return (gamma * m) / kQb;
+}
+
+// Gated ReLU^2 of one output pair, rounded to bfloat16 (nearest, ties to
+// even): g = acc_g * sg and u = acc_u * su (binary32), h = (max(g, 0)^2) * u
+// with the two products in that order.
+__device__ __forceinline__ uint16_t gated_relu2_bf16(int acc_g, int acc_u, float sg, float su) {
+  const float g = (float)acc_g * sg, u = (float)acc_u * su;
+  const float r = fmaxf(g, 0.0f);
+  const float h = (r * r) * u;
+  uint32_t b = __float_as_uint(h);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
 }
 
 }  // namespace bl

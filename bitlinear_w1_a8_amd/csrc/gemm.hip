@@ -230,7 +230,11 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // one stage do not alias reads of another and does not drain every
 // outstanding load before each LDS read (one array indexed by stage is not
 // enough for that).
-template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT>
+//
+// GATED: the weight rows come in (gate, up) pairs, 2i and 2i + 1, which sit in
+// neighbouring lanes of a fragment; the even lane takes its neighbour's sum
+// and writes the bfloat16 gated ReLU^2 of output i to h (y is not used).
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
                                                          const int8_t* __restrict__ xq,
@@ -238,8 +242,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
                                                          int T, int N, int K,
                                                          float* __restrict__ y,
                                                          int32_t* __restrict__ acc_out,
-                                                         int ksteps, int splits) {
+                                                         int ksteps, int splits,
+                                                         const float* __restrict__ gamma2,
+                                                         uint16_t* __restrict__ h_out) {
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
+  static_assert(!(SPLIT && GATED), "the gated epilogue needs whole sums");
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
@@ -253,6 +260,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   __shared__ __align__(16) unsigned char B2[STAGES > 2 ? kBBuf : 16];
   __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
+  __shared__ float scale2[GATED ? BM : 1];
   auto abuf = [&](auto st) -> unsigned char* {
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return A0;
@@ -294,6 +302,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     for (int r = tid; r < BM; r += NT) {
       const int tok = m0 + r;
       scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
+    }
+    if constexpr (GATED) {
+      const float g2 = gamma2[0];
+      for (int r = tid; r < BM; r += NT) {
+        const int tok = m0 + r;
+        scale2[r] = tok < T ? out_scale(g2, absmax[tok]) : 0.0f;
+      }
     }
   }
 
@@ -414,6 +429,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     if (kt + 2 < nk) step(I2{}, kt + 2);
   wait_vm<0>();   // no load may land in LDS after the block has finished
 
+  if constexpr (GATED) {
+    const int half = N >> 1;
+#pragma unroll
+    for (int i = 0; i < WMF; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 32 * WMF + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+        const int tok = m0 + r;
+        const float sg = scale[r], su = scale2[r];
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) {
+          const int n = n0 + wn * 32 * WNF + j * 32 + m;
+          const int sv = acc[i][j][v];
+          // every lane takes part: lane l gets lane l ^ 1's sum
+          const int other = __builtin_amdgcn_update_dpp(0, sv, 0xB1, 0xF, 0xF, false);
+          if (tok >= T || n >= N) continue;
+          const int64_t o = (int64_t)tok * N + n;
+          if (acc_out) acc_out[o] = sv;
+          if ((m & 1) == 0)
+            h_out[(int64_t)tok * half + (n >> 1)] = gated_relu2_bf16(sv, other, sg, su);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < WMF; ++i) {
 #pragma unroll
@@ -464,20 +504,22 @@ __global__ __launch_bounds__(256) void k_split_finish(float* __restrict__ y,
   }
 }
 
-template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES>
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool GATED = false>
 hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
-                   hipStream_t stream, int splits = 1, int ksteps = 0) {
+                   hipStream_t stream, int splits = 1, int ksteps = 0,
+                   const float* gamma2 = nullptr, uint16_t* h = nullptr) {
   // K parts of ksteps 128-wide steps each (the last may be shorter); the
   // caller sizes them so that every part has at least one step
   if (splits == 1) ksteps = (int)(k / BK);
   constexpr int BM = WAVES_M * 32 * WMF, BN = (WAVES / WAVES_M) * 32 * WNF;
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  auto kern = splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true>
-                         : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false>;
+  auto kern = GATED        ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, GATED>
+              : splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false>
+                           : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false>;
   kern<<<dim3((unsigned)(tiles * splits)), WAVES * 64, 0, stream>>>(
       reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc,
-      ksteps, splits);
+      ksteps, splits, gamma2, h);
   return hipGetLastError();
 }
 
@@ -558,6 +600,24 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
   if (big >= BL_GEMM_BIG_MIN_TILES)
     return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+}
+
+hipError_t launch_gemm_gated(const uint8_t* packed, const float* gamma_gate,
+                             const float* gamma_up, const int8_t* xq, const float* absmax,
+                             int64_t t, int64_t n, int64_t k, uint16_t* h, int32_t* acc,
+                             hipStream_t stream) {
+  // LDS-direct tiles only (no K split: the epilogue needs whole sums); other
+  // shapes go to the decode kernel, which takes any T
+  const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
+  if (!lds_ok)
+    return launch_gemv_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream);
+  const int64_t mt = (t + 127) / 128;
+  const int64_t wide = mt * ((n + 511) / 512);
+  if (wide >= BL_GEMM_WIDE_MIN_TILES)
+    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                     nullptr, acc, stream, 1, 0, gamma_up, h);
+  return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                   nullptr, acc, stream, 1, 0, gamma_up, h);
 }
 
 }  // namespace bl

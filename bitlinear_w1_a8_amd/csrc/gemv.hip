@@ -36,7 +36,9 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
                                               const int8_t* __restrict__ xq,
                                               const float* __restrict__ absmax, int T, int N,
                                               int K, float* __restrict__ y,
-                                              int32_t* __restrict__ acc_out) {
+                                              int32_t* __restrict__ acc_out,
+                                              const float* __restrict__ gamma2,
+                                              uint16_t* __restrict__ h) {
   extern __shared__ int red[];  // [nwaves][RT*NTT*4][64]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int qg = lane >> 4, r = lane & 15;
@@ -150,15 +152,38 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
 
   const float g = gamma[0];
   constexpr int kRows = 16 * RT, kToks = 16 * NTT;
-  for (int idx = threadIdx.x; idx < kRows * kToks; idx += blockDim.x) {
-    const int nl = idx % kRows, tl = idx / kRows;
-    const int n = n0 + nl;
-    if (n >= N || tl >= T) continue;
+  auto sum_of = [&](int nl, int tl) {
     const int rt = nl >> 4, i = nl & 15, tt = tl >> 4, j = tl & 15;
     const int slot = (rt * NTT + tt) * 4 + (i & 3);
     const int ln = (i >> 2) * 16 + j;
     int s = 0;
     for (int wv = 0; wv < nwaves; ++wv) s += red[(wv * kSlots + slot) * 64 + ln];
+    return s;
+  };
+  if (h) {
+    // gated: rows 2i (gate) and 2i + 1 (up) make output n0 / 2 + i
+    const float g2 = gamma2[0];
+    const int half = N >> 1;
+    for (int idx = threadIdx.x; idx < kRows / 2 * kToks; idx += blockDim.x) {
+      const int pl = idx % (kRows / 2), tl = idx / (kRows / 2);
+      const int n = n0 + 2 * pl;
+      if (n >= N || tl >= T) continue;
+      const int sg = sum_of(2 * pl, tl), su = sum_of(2 * pl + 1, tl);
+      const int64_t o = (int64_t)tl * N + n;
+      if (acc_out) {
+        acc_out[o] = sg;
+        acc_out[o + 1] = su;
+      }
+      const float a = absmax[tl];
+      h[(int64_t)tl * half + (n >> 1)] = gated_relu2_bf16(sg, su, out_scale(g, a), out_scale(g2, a));
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < kRows * kToks; idx += blockDim.x) {
+    const int nl = idx % kRows, tl = idx / kRows;
+    const int n = n0 + nl;
+    if (n >= N || tl >= T) continue;
+    const int s = sum_of(nl, tl);
     const int64_t o = (int64_t)tl * N + n;
     if (acc_out) acc_out[o] = s;
     y[o] = (float)s * out_scale(g, absmax[tl]);
@@ -204,6 +229,8 @@ struct DecProblem {
   int32_t* acc;           // optional exact sums
   int8_t* xq_out;         // fused modes: quantised activations out (block 0)
   float* absmax_out;      // fused modes: absmax out (block 0)
+  const float* gamma2;     // gated: the up projection's gamma (gamma is the gate's)
+  uint16_t* h;            // gated: [T, N / 2] bfloat16 out (then y is not written)
   int N, K;
   int per;                // chunks per wave: ceil((K / 256) / nw) <= CPW
 };
@@ -268,7 +295,7 @@ __device__ __forceinline__ float raw_elem(const uint4& v, int e) {
   }
 }
 
-template <int CPW, int MODE, bool ONE>
+template <int CPW, int MODE, bool ONE, bool GATED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kInt8 ? 8 : 6))) void k_gemv_dec(const DecGroup grp) {
   extern __shared__ __align__(16) unsigned char smem[];
   const DecProblem pr = grp.p[blockIdx.y];
@@ -278,6 +305,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
                    "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
                    "s"(pr.per), "s"(T), "s"(nwaves));
+  if constexpr (GATED) __asm__ volatile("" ::"s"(pr.gamma2), "s"(pr.h));
   const int N = pr.N, K = pr.K, per = pr.per;
   const int n0 = (int)blockIdx.x * 16;
   if (n0 >= N) return;                              // the grid spans the widest problem
@@ -307,8 +335,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
 
   // Issue order matters: vector memory operations retire in order, so what
   // is waited on first goes first.  The token absmax (int8 input) ...
+  // (gated outputs: token l >> 3 of lane l, eight outputs per token)
+  constexpr bool gated = GATED;
   float am = 0.0f;
-  if constexpr (MODE == kInt8) am = pr.absmax[min(lane >> 4, T - 1)];
+  if constexpr (MODE == kInt8) am = pr.absmax[min(gated ? lane >> 3 : lane >> 4, T - 1)];
   // ... then the activations, straight into LDS (lane l's 16 bytes land at
   // the wave's base + 16 l): int8 input, this wave's own k run; raw input
   // (step A1 fused), the whole rows, shared by the block ...
@@ -330,6 +360,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
                                          (dec_lds_t)(raw + 16 * base), 16, 0, 0);
   }
   const float g = pr.gamma[0];
+  float g2 = 0.0f;
+  if constexpr (GATED) g2 = pr.gamma2[0];
   // ... and last every weight chunk of this wave; slots past cnt repeat the
   // row's last chunk and meet a zero B operand below.
   uint4 buf[CPW];
@@ -520,6 +552,29 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
   ticket = __builtin_amdgcn_readfirstlane(ticket);
   if (ticket != nwaves - 1) return;
+  if constexpr (GATED) {
+    // rows 2i (gate) and 2i + 1 (up) of the tile make output n0 / 2 + i
+    const int half = N >> 1;
+    for (int idx = lane; idx < 8 * T; idx += 64) {
+      const int i = idx & 7, tl = idx >> 3;
+      const int nn = n0 + 2 * i;
+      if (nn >= N) continue;
+      const int sg = __hip_atomic_load(&tile[tl * 16 + 2 * i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int su = __hip_atomic_load(&tile[tl * 16 + 2 * i + 1], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (pr.acc) {
+        pr.acc[(int64_t)tl * N + nn] = sg;
+        pr.acc[(int64_t)tl * N + nn + 1] = su;
+      }
+      float a;
+      if constexpr (MODE == kInt8) a = idx < 64 ? am : pr.absmax[tl];
+      else a = __uint_as_float((uint32_t)amax[tl]);
+      pr.h[(int64_t)tl * half + (nn >> 1)] =
+          gated_relu2_bf16(sg, su, out_scale(g, a), out_scale(g2, a));
+    }
+    return;
+  }
   for (int idx = lane; idx < 16 * T; idx += 64) {
     const int i = idx & 15, tl = idx >> 4;
     const int nn = n0 + i;
@@ -545,7 +600,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
 
 template <int VEC, int RT, int NTT, int U>
 void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
-         int t, int n, int k, float* y, int32_t* acc, hipStream_t stream) {
+         int t, int n, int k, float* y, int32_t* acc, const float* gamma2, uint16_t* h,
+         hipStream_t stream) {
   const int k16 = k / 16;
   const int nchunks = (k16 + 4 * VEC - 1) / (4 * VEC);
   int nw = (nchunks + U - 1) / U;       // one pass of U chunks per wave where possible
@@ -554,20 +610,20 @@ void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const floa
   const int grid = (n + 16 * RT - 1) / (16 * RT);
   const size_t lds = (size_t)nw * RT * NTT * 4 * 64 * sizeof(int);
   k_gemv<VEC, RT, NTT, U><<<grid, nw * 64, lds, stream>>>(
-      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc);
+      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc, gamma2, h);
 }
 
 template <int VEC>
 void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
                 const float* absmax, int t, int n, int k, float* y, int32_t* acc,
-                hipStream_t stream) {
+                const float* gamma2, uint16_t* h, hipStream_t stream) {
   if (t <= 16)
-    run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
   else if (t <= 32)
     run<VEC, 2, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                    stream);
+                                                    gamma2, h, stream);
   else
-    run<VEC, 2, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    run<VEC, 2, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
 }
 
 }  // namespace
@@ -627,15 +683,15 @@ size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes) {
   return kDecHead + (size_t)t * (kmax + 16) + (size_t)t * kmax * raw_bytes;
 }
 
-template <int MODE, bool ONE>
+template <int MODE, bool ONE, bool GATED>
 void launch_dec(const DecGroup& grp, dim3 grid, const DecShape& sh, size_t lds,
                 hipStream_t stream) {
   if (sh.cpw == 2)
-    k_gemv_dec<2, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
+    k_gemv_dec<2, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
   else if (sh.cpw == 4)
-    k_gemv_dec<4, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
+    k_gemv_dec<4, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
   else
-    k_gemv_dec<8, MODE, ONE><<<grid, sh.nw * 64, lds, stream>>>(grp);
+    k_gemv_dec<8, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
 }
 
 template <int MODE>
@@ -646,10 +702,17 @@ hipError_t run_dec(DecGroup& grp, int count, int bx, const DecShape& sh, size_t 
   const dim3 grid((unsigned)bx, (unsigned)count);
   bool one = false;   // single-token specialisation of the fused prologue
   if constexpr (MODE != kInt8) one = grp.T == 1;
-  if (one)
-    launch_dec<MODE, MODE != kInt8>(grp, grid, sh, lds, stream);
-  else
-    launch_dec<MODE, false>(grp, grid, sh, lds, stream);
+  // gated epilogue: a group of one problem with h set (launch_gated)
+  if (grp.p[0].h != nullptr) {
+    if (one)
+      launch_dec<MODE, MODE != kInt8, true>(grp, grid, sh, lds, stream);
+    else
+      launch_dec<MODE, false, true>(grp, grid, sh, lds, stream);
+  } else if (one) {
+    launch_dec<MODE, MODE != kInt8, false>(grp, grid, sh, lds, stream);
+  } else {
+    launch_dec<MODE, false, false>(grp, grid, sh, lds, stream);
+  }
   return hipGetLastError();
 }
 
@@ -660,11 +723,11 @@ bool dec_ok(int64_t t, int64_t k, const void* packed, const void* xq) {
 
 hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t* xq,
                         const float* absmax, int t, int n, int k, float* y, int32_t* acc,
-                        hipStream_t stream) {
+                        const float* gamma2, uint16_t* h, hipStream_t stream) {
   DecGroup grp = {};
   grp.T = t;
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
-                        nullptr, nullptr, n, k, 0};
+                        nullptr, nullptr, gamma2, h, n, k, 0};
   const int blocks = (n + 15) / 16;
   return run_dec<kInt8>(grp, 1, blocks, dec_shape(blocks, k), dec_lds(t, k, 0), stream);
 }
@@ -703,7 +766,7 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
   for (int i = 0; i < count; ++i) {
     const bl_linear& q = probs[i];
     grp.p[i] = DecProblem{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr,
-                          q.y, q.acc, q.xq, q.absmax, (int)q.N, (int)q.K, 0};
+                          q.y, q.acc, q.xq, q.absmax, nullptr, nullptr, (int)q.N, (int)q.K, 0};
     const int64_t b = (q.N + 15) / 16;
     blocks += b;
     if (b > bx) bx = b;
@@ -716,24 +779,68 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
               : run_dec<kF32>(grp, count, (int)bx, sh, lds, stream);
 }
 
-hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
-                       int32_t* acc, hipStream_t stream) {
+namespace {
+
+// The int8-input decode kernels, plain (y) or gated (gamma2 and h given).
+hipError_t gemv_any(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
+                    const float* gamma2, uint16_t* h, hipStream_t stream) {
   if (dec_ok(t, k, packed, xq))
-    return run_dec_int8(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, stream);
+    return run_dec_int8(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, gamma2, h,
+                        stream);
   const bool vec4 = (k % 64) == 0 && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
   for (int64_t t0 = 0; t0 < t; t0 += kGemvTokens) {
     const int tc = (int)(t - t0 < kGemvTokens ? t - t0 : kGemvTokens);
     const int8_t* xs = xq + t0 * k;
-    float* ys = y + t0 * n;
+    float* ys = y ? y + t0 * n : nullptr;
     int32_t* as = acc ? acc + t0 * n : nullptr;
+    uint16_t* hs = h ? h + t0 * (n / 2) : nullptr;
     if (vec4)
-      run_tokens<4>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, stream);
+      run_tokens<4>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, gamma2, hs, stream);
     else
-      run_tokens<1>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, stream);
+      run_tokens<1>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, gamma2, hs, stream);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                       int32_t* acc, hipStream_t stream) {
+  return gemv_any(packed, gamma, xq, absmax, t, n, k, y, acc, nullptr, nullptr, stream);
+}
+
+hipError_t launch_gemv_gated(const uint8_t* packed, const float* gamma_gate,
+                             const float* gamma_up, const int8_t* xq, const float* absmax,
+                             int64_t t, int64_t n, int64_t k, uint16_t* h, int32_t* acc,
+                             hipStream_t stream) {
+  return gemv_any(packed, gamma_gate, xq, absmax, t, n, k, nullptr, acc, gamma_up, h, stream);
+}
+
+hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const float* gamma_gate,
+                        const float* gamma_up, int64_t t, int64_t n, int64_t k, uint16_t* h,
+                        int8_t* xq, float* absmax, int32_t* acc, hipStream_t stream) {
+  const int rb = bf16 ? 2 : 4;
+  const int64_t blocks = (n + 15) / 16;
+  // one launch for decode shapes (the same rule as a grouped call of one problem)
+  if (dec_shape_ok(t, k, rb) && (reinterpret_cast<uintptr_t>(x) % 16) == 0 &&
+      (reinterpret_cast<uintptr_t>(packed) % 16) == 0 && blocks * k <= BL_GEMV_FUSE_MAX_WORK) {
+    DecGroup grp = {};
+    grp.T = (int)t;
+    grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma_gate, x, nullptr,
+                          nullptr, acc, xq, absmax, gamma_up, h, (int)n, (int)k, 0};
+    const DecShape sh = dec_shape(blocks, k);
+    const size_t lds = dec_lds(t, k, rb);
+    return bf16 ? run_dec<kBf16>(grp, 1, (int)blocks, sh, lds, stream)
+                : run_dec<kF32>(grp, 1, (int)blocks, sh, lds, stream);
+  }
+  hipError_t e = launch_quant(x, bf16, t, k, xq, absmax, nullptr, stream);
+  if (e != hipSuccess) return e;
+  return t <= kGemvMaxTokens
+             ? launch_gemv_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream)
+             : launch_gemm_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream);
 }
 
 }  // namespace bl

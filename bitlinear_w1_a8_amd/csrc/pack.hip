@@ -138,6 +138,18 @@ __global__ __launch_bounds__(256) void k_ternarize_pack(const float4* __restrict
   }
 }
 
+// Row interleave of two packed matrices with the same shape: out row 2i is
+// row i of a, out row 2i + 1 row i of b; one packed word per thread step.
+__global__ __launch_bounds__(256) void k_interleave(const uint32_t* __restrict__ a,
+                                                    const uint32_t* __restrict__ b, int64_t k16,
+                                                    int64_t total, uint32_t* __restrict__ out) {
+  for (int64_t w = blockIdx.x * 256ll + threadIdx.x; w < total; w += (int64_t)gridDim.x * 256) {
+    const int64_t row = w / k16, col = w - row * k16;
+    const uint32_t* src = (row & 1) ? b : a;
+    out[w] = src[(row >> 1) * k16 + col];
+  }
+}
+
 int grid_for(int64_t items, int threads, int cap) {
   int64_t g = (items + threads - 1) / threads;
   if (g > cap) g = cap;
@@ -158,6 +170,15 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, fl
   const int64_t nwords = count / 16;
   k_ternarize_pack<<<grid_for(nwords, 256, 65536), 256, 0, stream>>>(
       reinterpret_cast<const float4*>(w), nwords, gamma, reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_interleave(const uint8_t* a, const uint8_t* b, int64_t n, int64_t k,
+                             uint8_t* out, hipStream_t stream) {
+  const int64_t k16 = k / 16, total = 2 * n * k16;
+  k_interleave<<<grid_for(total, 256, 65536), 256, 0, stream>>>(
+      reinterpret_cast<const uint32_t*>(a), reinterpret_cast<const uint32_t*>(b), k16, total,
+      reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 

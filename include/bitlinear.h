@@ -219,6 +219,47 @@ typedef struct bl_linear {
 int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
                              void* stream);
 
+/* Row interleave of two packed matrices of the same shape, for
+ * bitlinear_gated_relu2: out row 2i is row i of a, out row 2i + 1 row i of b
+ * (four ternary weights per byte in each row, as bitlinear_pack_weights
+ * writes them).  Each matrix keeps its own gamma.
+ *
+ *   a, b     [N, K/4] uint8 packed matrices (device), 4-byte aligned.
+ *   N, K     1 <= N <= 2^25, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
+ *   out      [2N, K/4] uint8 output (device), 4-byte aligned; must not overlap a or b.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
+                              uint8_t* out, void* stream);
+
+/* The gate and up projections of one input (steps A1-A3 each) and the
+ * squared-ReLU activation that the 2B4T report (section 2) puts in the
+ * feed-forward sublayer, read as a gated unit and written as bfloat16 for the
+ * down projection:
+ *   g = y_gate[t,n], u = y_up[t,n]  (binary32, exactly as bitlinear_forward
+ *       computes them: acc * (gamma * max(absmax, eps) / 127)),
+ *   h[t,n] = bf16_round_nearest_even((max(g, 0) * max(g, 0)) * u)
+ *       (two binary32 products in that order).
+ * The activations are quantised once (step A1) and shared by both
+ * projections; for decode shapes (T <= 4, K % 256 == 0, raw rows of at most
+ * 32 KiB) one kernel does everything, otherwise act-quant runs first and the
+ * contraction kernel (chosen by T) writes h in its epilogue.  The gate/up
+ * outputs are never stored in binary32.
+ *
+ *   x           [T, K] activations of dtype x_dtype (BL_F32 or BL_BF16), 16-byte aligned.
+ *   packed_gu   [2N, K/4] from bitlinear_interleave_rows(gate, up), 16-byte aligned.
+ *   gamma_gate, gamma_up   [1] float32 each (device), from bitlinear_pack_weights.
+ *   T, N, K     1 <= T <= 2^24, 1 <= N <= 2^25 (outputs per token), 16 <= K <= BITLINEAR_MAX_K,
+ *               K % 16 == 0.
+ *   h           [T, N] bfloat16 output (uint16 bit patterns), 2-byte aligned.
+ *   xq          [T, K] int8 activations (written), 16-byte aligned.
+ *   absmax      [T] token absmax (written), 4-byte aligned.
+ *   acc         [T, 2N] exact int32 sums, interleaved as the rows (gate, up), or NULL.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_HIP. */
+int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
+                          const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
+                          int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
 
@@ -167,3 +167,36 @@ def test_linear_grouped_errors(lib):
     assert f(bad, 2, 1, 1, None) == BL_ERR_ALIGN
     bad = (BlLinear * 1)(BlLinear(A16, A16, A16, 0, 256, A16, A16, A16, None))
     assert f(bad, 1, 1, 1, None) == BL_ERR_SHAPE
+
+
+def test_interleave_rows_errors(lib):
+    f = lib.bitlinear_interleave_rows
+    assert f(None, A16, 4, 64, A16, None) == BL_ERR_NULL
+    assert f(A16, A16, 4, 64, None, None) == BL_ERR_NULL
+    assert f(A16, A16, 0, 64, A16, None) == BL_ERR_SHAPE
+    assert f(A16, A16, (1 << 25) + 1, 64, A16, None) == BL_ERR_SHAPE
+    assert f(A16, A16, 4, 40, A16, None) == BL_ERR_SHAPE
+    assert f(A16, A16 + 2, 4, 64, A16, None) == BL_ERR_ALIGN
+
+
+def test_gated_relu2_errors(lib):
+    f = lib.bitlinear_gated_relu2
+    ok = [A16, 1, A16, A16, A16, 4, 100, 256, A16, A16, A16, None, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    for i in (0, 2, 3, 4, 8, 9, 10):
+        assert call(**{f"a{i}": None}) == BL_ERR_NULL
+    assert call(a1=2) == BL_ERR_DTYPE
+    assert call(a5=0) == BL_ERR_SHAPE
+    assert call(a6=0) == BL_ERR_SHAPE
+    assert call(a6=(1 << 25) + 1) == BL_ERR_SHAPE
+    assert call(a7=264) == BL_ERR_SHAPE            # K % 16
+    assert call(a2=A16 + 4) == BL_ERR_ALIGN        # packed rows read 16 bytes at a time
+    assert call(a8=A16 + 1) == BL_ERR_ALIGN        # bfloat16 output
+    assert call(a11=A16 + 2) == BL_ERR_ALIGN
+    assert "bitlinear_gated_relu2" in (call(a5=0) and _err(lib))

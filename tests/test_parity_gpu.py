@@ -396,3 +396,106 @@ def test_linear_grouped(bl, name):
         a = host(acc)
         assert int(np.count_nonzero(a != acc_ref)) == 0
         check_y(host(y), acc_ref, gamma_ref, a_ref)
+
+
+# ------------------------------------------------------------------ gated ReLU^2 into bfloat16
+
+def test_interleave_rows(bl):
+    rng = np.random.default_rng(991)
+    for n, k in [(1, 16), (5, 48), (300, 2560)]:
+        a = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+        b = rng.integers(0, 256, (n, k // 4), dtype=np.uint8)
+        want = np.empty((2 * n, k // 4), np.uint8)
+        want[0::2] = a
+        want[1::2] = b
+        assert np.array_equal(host(bl.interleave_rows(dev(a), dev(b))), want)
+
+
+# (T, N outputs, K, dtype): fused decode (T <= 4, K % 256 == 0), the int8
+# decode kernel (T <= 16), the 64-token decode kernel (K % 256 != 0, or
+# 16 < T <= 128), T above 128 with K % 128 != 0, the tiled MFMA kernel
+# (128 x 256 and 128 x 512 tiles), and a decode shape over the fused-work limit
+GATED_CASES = [(1, 6912, 2560, "bf16"), (3, 100, 512, "f32"), (4, 37, 256, "bf16"),
+               (9, 300, 1024, "bf16"), (16, 50, 2048, "f32"), (40, 77, 1008, "bf16"),
+               (70, 64, 320, "f32"), (130, 300, 1040, "bf16"), (300, 500, 2560, "bf16"),
+               (1024, 6144, 512, "bf16"), (2, 8200, 8192, "bf16"), (1, 28672, 8192, "bf16")]
+
+
+def _gated_inputs(bl, t, n, k, dtype, seed):
+    wg = wl.latent_weights(n, k, 0.02, seed)
+    wu = wl.latent_weights(n, k, 0.03, seed + 1)
+    pg, gg, _, gg_ref = check_pack(bl, wg)
+    pu, gu, _, gu_ref = check_pack(bl, wu)
+    tg = oracle.ternarize(wg, gg_ref)
+    tu = oracle.ternarize(wu, gu_ref)
+    x = wl.activations_student_t(t, k, 4, seed + 2)
+    if t > 2:
+        x[1] = 0.0                                  # an all-zero token
+    if dtype == "bf16":
+        bits = wl.bf16_bits(x)
+        xin, xref = dev_bf16(bits), bits
+    else:
+        xin, xref = dev(x), x
+    return bl.interleave_rows(pg, pu), gg, gu, xin, xref, tg, tu, gg_ref, gu_ref
+
+
+def _check_gated(h, xq, absmax, acc, xref, tg, tu, gg_ref, gu_ref, rows=None):
+    q_ref, a_ref, _ = oracle.quant_act(xref)
+    if rows is not None:
+        q_ref, a_ref = q_ref[rows], a_ref[rows]
+        h, xq, absmax, acc = h[rows], xq[rows], absmax[rows], acc[rows]
+    assert np.array_equal(xq, q_ref)
+    assert np.array_equal(absmax.view(np.uint32), a_ref.view(np.uint32))
+    ag = oracle.contract(q_ref, tg)
+    au = oracle.contract(q_ref, tu)
+    assert np.array_equal(acc[:, 0::2], ag) and np.array_equal(acc[:, 1::2], au)
+    h_ref = oracle.gated_relu2(ag, au, gg_ref, gu_ref, a_ref)
+    bad = int(np.count_nonzero(h != h_ref))
+    assert bad == 0, f"{bad} of {h.size} bfloat16 outputs differ"
+
+
+def _bits(t):
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("t,n,k,dtype", GATED_CASES,
+                         ids=[f"T{t}_N{n}_K{k}_{d}" for t, n, k, d in GATED_CASES])
+def test_gated_relu2(bl, t, n, k, dtype):
+    pgu, gg, gu, xin, xref, tg, tu, gg_ref, gu_ref = _gated_inputs(bl, t, n, k, dtype, 7000 + t + k)
+    h, xq, absmax, acc = bl.gated_relu2(xin, pgu, gg, gu, want_acc=True)
+    _check_gated(_bits(h), host(xq), host(absmax), host(acc), xref, tg, tu, gg_ref, gu_ref)
+    # without the optional sums: the same bits
+    h2, _, _, _ = bl.gated_relu2(xin, pgu, gg, gu)
+    assert np.array_equal(_bits(h2), _bits(h))
+
+
+def test_gated_relu2_prefill_full_size_sampled(bl):
+    """The 2B gate/up projections at T = 2048 (128 x 512 tiles), checked on
+    sampled tokens, the zero token among them."""
+    t, n, k = 2048, 6912, 2560
+    pgu, gg, gu, xin, xref, tg, tu, gg_ref, gu_ref = _gated_inputs(bl, t, n, k, "bf16", 7100)
+    h, xq, absmax, acc = bl.gated_relu2(xin, pgu, gg, gu, want_acc=True)
+    rows = np.sort(np.concatenate([[0, 1, 127, 128, t - 1],
+                                   np.random.default_rng(7101).choice(t, 27, replace=False)]))
+    rows = np.unique(rows)
+    _check_gated(_bits(h), host(xq), host(absmax), host(acc), xref, tg, tu, gg_ref, gu_ref, rows)
+
+
+def test_gated_relu2_then_down(bl):
+    """The FFN of one decode step: gate/up with the gated epilogue, then the
+    down projection on the bfloat16 h with act-quant fused (grouped call)."""
+    t, n, k = 1, 6912, 2560
+    pgu, gg, gu, xin, xref, tg, tu, gg_ref, gu_ref = _gated_inputs(bl, t, n, k, "bf16", 7200)
+    h, _, _, _ = bl.gated_relu2(xin, pgu, gg, gu)
+    wd = wl.latent_weights(k, n, 0.02, 7203)
+    pd, gd, _, gd_ref = check_pack(bl, wd)
+    (y, xq, absmax, acc), = bl.linear_grouped([h], [(pd, gd)], want_acc=True)
+    q_ref, a_ref, _ = oracle.quant_act(xref)
+    h_ref = oracle.gated_relu2(oracle.contract(q_ref, tg), oracle.contract(q_ref, tu),
+                               gg_ref, gu_ref, a_ref)
+    qd, ad, _ = oracle.quant_act(h_ref)
+    assert np.array_equal(host(xq), qd)
+    acc_ref = oracle.contract(qd, oracle.ternarize(wd, gd_ref))
+    assert np.array_equal(host(acc), acc_ref)
+    check_y(host(y), acc_ref, gd_ref, ad)
