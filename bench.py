@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=256)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extra", action="store_true", help="skip the prefill GEMM context run")
+    p.add_argument("--extra", default="all",
+                   help="context runs to do: 'all' or a comma list of prefill, crossover, 70b, "
+                        "subln, gated")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--fused-only", action="store_true",
@@ -386,6 +389,80 @@ def prefill_extra(torch, binding, wl, dev, stream):
     return out
 
 
+def gated_extra(torch, binding, dev, stream):
+    """The gate/up pair of the 2B FFN (2560 -> 2 x 6912) with the gated
+    ReLU^2 epilogue writing bfloat16 h, against the same two projections
+    writing binary32 outputs (without the activation): T = 1 (one launch
+    each, act-quant fused) and T = 2048 (act-quant, then the tiled MFMA
+    kernel; two GEMMs against one).  Weights drawn on the GPU (N(0, 0.02),
+    seeded), rotated over > 1 GB at T = 1 and 64 copies at T = 2048."""
+    lib = binding.load()
+    calls = Calls(lib)
+    k, n = 2560, 6912
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8100)
+    pg, gg = binding.pack_weights(torch.randn((n, k), device=dev, generator=gen) * 0.02)
+    pu, gu = binding.pack_weights(torch.randn((n, k), device=dev, generator=gen) * 0.02)
+    pgu = binding.interleave_rows(pg, pu)
+    out = {}
+    for t in (1, 2048):
+        ncopy = int(np.ceil(ROT_BYTES / pgu.numel())) if t == 1 else 64
+        cg = [pg] + [pg.clone() for _ in range(ncopy - 1)]
+        cu = [pu] + [pu.clone() for _ in range(ncopy - 1)]
+        cgu = [pgu] + [pgu.clone() for _ in range(ncopy - 1)]
+        x = torch.randn((t, k), device=dev, generator=gen).to(torch.bfloat16)
+        xq = torch.empty((t, k), dtype=torch.int8, device=dev)
+        am = torch.empty(t, dtype=torch.float32, device=dev)
+        yg = torch.empty((t, n), dtype=torch.float32, device=dev)
+        yu = torch.empty((t, n), dtype=torch.float32, device=dev)
+        h = torch.empty((t, n), dtype=torch.bfloat16, device=dev)
+        X, XQ, AM, YG, YU, H, GG, GU = (ptr(v) for v in (x, xq, am, yg, yu, h, gg, gu))
+
+        def gated(s, i):
+            rc = lib.bitlinear_gated_relu2(X, 1, ptr(cgu[i]), GG, GU, t, n, k, H, XQ, AM, None,
+                                           ctypes.c_void_p(s.cuda_stream))
+            if rc:
+                raise RuntimeError(lib.bitlinear_last_error().decode())
+
+        if t == 1:
+            descs = []
+            for i in range(ncopy):
+                arr = (binding.BlLinear * 2)()
+                arr[0] = binding.BlLinear(x.data_ptr(), cg[i].data_ptr(), gg.data_ptr(), n, k,
+                                          yg.data_ptr(), xq.data_ptr(), am.data_ptr(), None)
+                arr[1] = binding.BlLinear(x.data_ptr(), cu[i].data_ptr(), gu.data_ptr(), n, k,
+                                          yu.data_ptr(), xq.data_ptr(), am.data_ptr(), None)
+                descs.append(arr)
+
+            def plain(s, i):
+                calls.grouped(descs[i], 1, ctypes.c_void_p(s.cuda_stream))
+        else:
+            def plain(s, i):
+                hs = ctypes.c_void_p(s.cuda_stream)
+                calls.quant(X, XQ, AM, t, k, hs)
+                calls.forward(ptr(cg[i]), GG, XQ, AM, t, n, k, YG, 0, hs)
+                calls.forward(ptr(cu[i]), GU, XQ, AM, t, n, k, YU, 0, hs)
+
+        reps = 10 if t == 1 else 4
+        us_g = rotated_time_us(torch, gated, ncopy, stream, reps=reps)
+        us_p = rotated_time_us(torch, plain, ncopy, stream, reps=reps)
+        rec = {"gated_bf16_us": round(us_g, 2), "two_projections_f32_us": round(us_p, 2),
+               "rotated_copies": ncopy}
+        if t == 1:
+            byts = 2 * n * k // 4 + 2 * k + 2 * n + k + 4
+            rec["gated_gb_s"] = round(byts / us_g / 1e3, 1)
+            rec["gated_frac_of_hbm_peak"] = round(byts / us_g / 1e3 / HBM_PEAK_GBS, 4)
+        else:
+            ops = 2.0 * t * 2 * n * k
+            rec["gated_tops"] = round(ops / us_g / 1e6, 1)
+            rec["gated_frac_of_int8_peak"] = round(ops / us_g / 1e6 / INT8_PEAK_TOPS, 4)
+            rec["two_projections_tops"] = round(ops / us_p / 1e6, 1)
+        out[f"T{t}_K{k}_N2x{n}"] = rec
+        del cg, cu, cgu
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -516,11 +593,19 @@ def main():
     extra.update({"layer_sets_rotated": n_sets,
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
+    want = set(args.extra.split(",")) if args.extra != "all" else {
+        "prefill", "crossover", "70b", "subln", "gated"}
     if not args.no_extra:
-        extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
-        extra["batched_decode_crossover"] = crossover_extra(torch, mats, sets, dev, stream, calls)
-        extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
-        extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
+        if "prefill" in want:
+            extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
+        if "crossover" in want:
+            extra["batched_decode_crossover"] = crossover_extra(torch, mats, sets, dev, stream, calls)
+        if "70b" in want:
+            extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
+        if "subln" in want:
+            extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
+        if "gated" in want:
+            extra["gated_relu2_ffn"] = gated_extra(torch, binding, dev, stream)
 
     cpu = None
     if not args.no_cpu:
