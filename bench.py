@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill GEMM context run")
     p.add_argument("--extra", default="all",
                    help="context runs to do: 'all' or a comma list of prefill, crossover, 70b, "
-                        "subln, gated")
+                        "subln, gated, lut")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--fused-only", action="store_true",
@@ -463,6 +463,45 @@ def gated_extra(torch, binding, dev, stream):
     return out
 
 
+def lut_extra(torch, binding, mats, sets, dev, stream, calls):
+    """The table-lookup decode kernel (bitnet.cpp TL1/TL2 style) against the
+    matrix-core decode kernel at T = 1 on int8 input: the 2B shapes (weights
+    rotated over the layer sets) and 8192 -> 28672 (weights drawn on the GPU,
+    rotated over > 1 GB)."""
+    out = {}
+    for mi in (0, 4, 6):
+        d = mats[mi]
+        n, k = d["m"].n, d["m"].k
+        xq = torch.randint(-127, 128, (1, k), dtype=torch.int8, device=dev)
+        am = torch.rand(1, device=dev) * 4 + 1
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        P = [ptr(s_[mi]) for s_ in sets]
+        us = [rotated_time_us(
+            torch, lambda s, i, a=algo: calls.forward(P[i], ptr(d["gamma"]), ptr(xq), ptr(am), 1, n, k,
+                                                      ptr(y), a, ctypes.c_void_p(s.cuda_stream)),
+            len(sets), stream, reps=5) for algo in (3, 1)]
+        out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "decode_kernel_us": round(us[1], 2),
+                            "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1)}
+    n, k = 28672, 8192
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5100)
+    packed, gamma = binding.pack_weights(torch.randn((n, k), device=dev, generator=gen) * 0.01)
+    copies = [packed] + [packed.clone() for _ in range(int(np.ceil(ROT_BYTES / packed.numel())) - 1)]
+    xq = torch.randint(-127, 128, (1, k), dtype=torch.int8, device=dev)
+    am = torch.rand(1, device=dev) * 4 + 1
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    P = [ptr(c) for c in copies]
+    us = [rotated_time_us(
+        torch, lambda s, i, a=algo: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), 1, n, k, ptr(y), a,
+                                                  ctypes.c_void_p(s.cuda_stream)),
+        len(copies), stream, reps=5) for algo in (3, 1)]
+    out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "decode_kernel_us": round(us[1], 2),
+                        "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1)}
+    del copies, packed
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -594,7 +633,7 @@ def main():
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     want = set(args.extra.split(",")) if args.extra != "all" else {
-        "prefill", "crossover", "70b", "subln", "gated"}
+        "prefill", "crossover", "70b", "subln", "gated", "lut"}
     if not args.no_extra:
         if "prefill" in want:
             extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
@@ -606,6 +645,8 @@ def main():
             extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
         if "gated" in want:
             extra["gated_relu2_ffn"] = gated_extra(torch, binding, dev, stream)
+        if "lut" in want:
+            extra["lut_decode_comparison"] = lut_extra(torch, binding, mats, sets, dev, stream, calls)
 
     cpu = None
     if not args.no_cpu:

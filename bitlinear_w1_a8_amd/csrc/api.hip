@@ -128,6 +128,8 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
     return launched(fn, bl::launch_gemv(packed, gamma, xq, absmax, T, N, K, y, acc, s));
   if (algo == BL_ALGO_GEMM)
     return launched(fn, bl::launch_gemm(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+  if (algo == BL_ALGO_LUT)
+    return launched(fn, bl::launch_gemv_lut(packed, gamma, xq, absmax, T, N, K, y, acc, s));
   return fail(BL_ERR_ARG, "%s: unknown algo %d", fn, algo);
 }
 

@@ -86,7 +86,10 @@ typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 typedef enum {
   BL_ALGO_AUTO = 0, /* decode kernel for T <= bitlinear_gemv_max_tokens(), else GEMM */
   BL_ALGO_GEMV = 1, /* streaming decode kernel, any T (tokens taken 64 at a time) */
-  BL_ALGO_GEMM = 2  /* LDS-tiled int8 MFMA kernel, any T */
+  BL_ALGO_GEMM = 2, /* LDS-tiled int8 MFMA kernel, any T */
+  BL_ALGO_LUT = 3   /* table-lookup decode kernel in the style of bitnet.cpp's TL1/TL2
+                       ("微软 BitNet ...", section 1.3), any T (weights re-read per
+                       token): a comparison design with the same results */
 } bl_algo;
 
 /* Version of this interface (BITLINEAR_ABI_VERSION). */

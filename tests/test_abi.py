@@ -103,7 +103,7 @@ def test_forward_errors(lib):
     assert f(A16, A16, A16 + 8, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16 + 2, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16, A16 + 1, 0, None) == BL_ERR_ALIGN
-    assert f(*good, 1, 16, 64, A16, None, 3, None) == BL_ERR_ARG
+    assert f(*good, 1, 16, 64, A16, None, 4, None) == BL_ERR_ARG
     assert f(*good, 1, 16, 64, A16, None, -1, None) == BL_ERR_ARG
     assert lib.bitlinear_forward(None, A16, A16, A16, 1, 16, 64, A16, None, None) == BL_ERR_NULL
 

@@ -195,7 +195,9 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               (3, 37, 512), (16, 50, 2048), (2, 17, 8192), (1, 3, 256), (1, 1000, 28672),
               # prefill kernel: K split into 38 parts (the last one short) on
               # ragged T and N; the 128 x 256 tiles; the 128 x 512 tiles
-              (200, 1500, 28672), (1100, 3800, 512), (1500, 8100, 256)]
+              (200, 1500, 28672), (1100, 3800, 512), (1500, 8100, 256),
+              # table-lookup kernel: 4-wave blocks with word loads and a short last chunk
+              (40, 900, 3088)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
@@ -211,7 +213,7 @@ def _forward_inputs(t, n, k, seed, zero_rows=True):
     return tern, q, absmax, gamma
 
 
-@pytest.mark.parametrize("algo", ["gemv", "gemm"])
+@pytest.mark.parametrize("algo", ["gemv", "gemm", "lut"])
 @pytest.mark.parametrize("t,n,k", FWD_SHAPES, ids=[f"T{t}_N{n}_K{k}" for t, n, k in FWD_SHAPES])
 def test_forward_shapes(bl, t, n, k, algo):
     tern, q, absmax, gamma = _forward_inputs(t, n, k, 100 * t + n + k)
@@ -230,7 +232,7 @@ def test_forward_extremes(bl):
     q[2, ::2] = -127
     absmax = np.array([5.0, 0.25, 1e-7], np.float32)
     gamma = np.float32(3.0)
-    for algo in ("gemv", "gemm"):
+    for algo in ("gemv", "gemm", "lut"):
         a = check_forward(bl, dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q),
                           dev(absmax), tern, q, gamma, absmax, algo)
         assert a[0, 0] == 127 * k
@@ -291,7 +293,8 @@ def test_workload_full_size(bl, widx, mi):
     for t in w.tokens:
         x = w.activations(mi, t)
         xq, absmax, q_ref, a_ref = check_quant(bl, x, w.x_dtype)
-        algos = ["auto"] + (["gemv", "gemm"] if widx == 3 else [])
+        algos = ["auto"] + (["gemv", "gemm", "lut"] if widx == 3 else []) + (
+            ["lut"] if widx == 2 else [])
         for algo in algos:
             check_forward(bl, packed, gamma, xq, absmax, tern, q_ref, gamma_ref, a_ref, algo)
     if widx in (2, 5):
