@@ -31,3 +31,9 @@ from .ffn_ref import (  # noqa: F401
     out_scale_f32,
     y_f32,
 )
+from .binary_ref import (  # noqa: F401
+    binarize,
+    forward_binary,
+    pack_binary,
+    pack_weights_binary,
+)

@@ -16,6 +16,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
@@ -512,6 +513,71 @@ def pin_gated_matches_binary64(o):
     p = _bf16_torch(o.gated_relu2_plain(ag, au, 0.0173, 0.0291, a).astype(np.float32)).astype(np.int32)
     d = np.abs(h - p)
     assert d.max() <= 1 and np.count_nonzero(d) <= h.size // 500
+
+
+# ------------------------------------------------------------ binary weights (W1A8)
+
+def _decode_binary(packed, k):
+    # read back bit by bit from the stated layout: weight k = 32g + 4j + i at
+    # bit 8i + j of little-endian word g of its row; bit 1 means +1
+    n = packed.shape[0]
+    t = np.zeros((n, k), np.int8)
+    for r in range(n):
+        for kk in range(k):
+            g, rem = divmod(kk, 32)
+            j, i = divmod(rem, 4)
+            byte = packed[r, 4 * g + i]
+            t[r, kk] = 1 if (byte >> j) & 1 else -1
+    return t
+
+
+def pin_e8_binary(o):
+    e = GOLD["E8_binary"]
+    w = np.array(e["w"], np.float32)
+    packed, gamma = o.pack_weights_binary(w)
+    assert [[f"0x{b:02x}" for b in row] for row in packed] == e["packed"]
+    assert float(gamma) == e["gamma"]
+
+
+def pin_binary_decoder(o):
+    rng = np.random.default_rng(81)
+    w = rng.standard_normal((9, 96)).astype(np.float32)
+    w[0, :5] = [0.0, -0.0, 1e-45, -1e-45, 0.0]
+    t = o.binarize(w)
+    assert set(np.unique(t)) <= {-1, 1}
+    want = np.where(np.signbit(w) & (w != 0), -1, 1)     # zeros of either sign -> +1
+    assert np.array_equal(t, want)
+    assert np.array_equal(_decode_binary(o.pack_binary(t), 96), t)
+
+
+def pin_binary_rows_and_symmetry(o):
+    assert np.all(o.pack_binary(np.ones((2, 64), np.int8)) == 0xFF)
+    assert np.all(o.pack_binary(-np.ones((2, 64), np.int8)) == 0x00)
+    rng = np.random.default_rng(82)
+    w = rng.standard_normal((5, 64)).astype(np.float32)
+    w[w == 0] = 1.0
+    p = o.pack_binary(o.binarize(w))
+    assert np.array_equal(o.pack_binary(o.binarize(-w)), ~p)
+    with pytest.raises(ValueError):
+        o.pack_binary(np.ones((1, 48), np.int8))          # K % 32 != 0
+    with pytest.raises(ValueError):
+        o.pack_binary(np.zeros((1, 32), np.int8))         # 0 is not a binary level
+
+
+def pin_binary_forward_by_hand(o):
+    # tiny case against plain Python loops over the definitions
+    rng = np.random.default_rng(83)
+    w = (rng.standard_normal((3, 32)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((2, 32)).astype(np.float32)
+    y, acc, _, gamma = o.forward_binary(w, x)
+    q, a, _ = o.quant_act(x)
+    assert float(gamma) == float(np.float32(math.fsum(abs(float(v)) for v in w.ravel()) / w.size))
+    for tt in range(2):
+        for n in range(3):
+            s = sum((1 if w[n, k] >= 0 else -1) * int(q[tt, k]) for k in range(32))
+            assert acc[tt, n] == s
+            want = s * float(gamma) * max(float(a[tt]), float(np.float32(1e-5))) / 127
+            assert abs(y[tt, n] - want) <= 1e-12 * max(1.0, abs(want))
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

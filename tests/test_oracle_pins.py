@@ -209,7 +209,45 @@ def _gated_mutant(**kw):
     return lambda ag, au, gg, gu, a: _gated(ag, au, gg, gu, a, **kw)
 
 
+def _binarize_zero_to_minus(w):
+    w = np.asarray(w, np.float32)
+    return np.where(w > 0, 1, -1).astype(np.int8)
+
+
+def _binarize_centered(w):
+    # the original binary BitNet's Sign(W - mean W): not what the pages give
+    w = np.asarray(w, np.float32)
+    c = w - np.float32(np.mean(w, dtype=np.float64))
+    return np.where(c >= 0, 1, -1).astype(np.int8)
+
+
+def _pack_binary_with(bitpos=lambda j, i: 8 * i + j, one_is_plus=True):
+    def pack(t):
+        t = np.asarray(t)
+        n, k = t.shape
+        if k % 32 != 0:
+            raise ValueError("K")
+        if not np.all((t == -1) | (t == 1)):
+            raise ValueError("binary")
+        bits = ((t > 0) if one_is_plus else (t < 0)).astype(np.uint32).reshape(n, k // 32, 8, 4)
+        words = np.zeros((n, k // 32), np.uint32)
+        for j in range(8):
+            for i in range(4):
+                words |= bits[:, :, j, i] << np.uint32(bitpos(j, i))
+        return words.astype("<u4").view(np.uint8).reshape(n, k // 8)
+    return pack
+
+
+def _pack_weights_binary_with(binarize):
+    return lambda w: (oracle.pack_binary(binarize(w)), oracle.absmean_gamma(w))
+
+
 MUTANTS = {
+    "binary_zero_to_minus": dict(binarize=_binarize_zero_to_minus),
+    "binary_centered_sign": dict(binarize=_binarize_centered,
+                                 pack_weights_binary=_pack_weights_binary_with(_binarize_centered)),
+    "binary_bit_order_swapped": dict(pack_binary=_pack_binary_with(bitpos=lambda j, i: 4 * j + i)),
+    "binary_bit_means_minus": dict(pack_binary=_pack_binary_with(one_is_plus=False)),
     "gated_no_relu": dict(gated_relu2=_gated_mutant(relu=False)),
     "gated_not_squared": dict(gated_relu2=_gated_mutant(square=False)),
     "gated_relu_on_up_too": dict(gated_relu2=_gated_mutant(relu_up=True)),
