@@ -6,7 +6,7 @@ names below load the library on first use and fail loudly if it is missing.
 """
 
 _EXPORTS = ("pack_weights", "quant_act", "subln_quant_act", "forward", "bitlinear", "linear_grouped",
-            "interleave_rows", "gated_relu2",
+            "interleave_rows", "gated_relu2", "pack_weights_binary", "forward_binary",
             "gemv_max_tokens",
             "BitLinearError", "load", "last_error")
 

@@ -45,6 +45,10 @@ class BlLinear(ctypes.Structure):
                 ("K", _c_i64), ("y", _c_vp), ("xq", _c_vp), ("absmax", _c_vp), ("acc", _c_vp)]
 
 
+SIGNATURES["bitlinear_pack_weights_binary"] = (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp,
+                                                        _c_sz, _c_vp])
+SIGNATURES["bitlinear_forward_binary"] = (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                                   _c_vp, _c_vp, _c_int, _c_vp])
 SIGNATURES["bitlinear_interleave_rows"] = (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp])
 SIGNATURES["bitlinear_gated_relu2"] = (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
                                                 _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp])
@@ -256,3 +260,36 @@ def gated_relu2(x, packed_gu, gamma_gate, gamma_up, want_acc=False):
                                      _ptr(gamma_up), t, n, k, _ptr(h), _ptr(xq), _ptr(absmax),
                                      _ptr(acc), _stream(x.device)))
     return h, xq, absmax, acc
+
+
+def pack_weights_binary(w):
+    """Step A0 for binary weights on the GPU: float32 [N, K] -> (packed uint8
+    [N, K/8], gamma float32[1]); K a multiple of 256, at most 32768."""
+    lib = load()
+    _need_cuda(w, "w", torch.float32)
+    n, k = w.shape
+    packed = torch.empty((n, k // 8), dtype=torch.uint8, device=w.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws_bytes = lib.bitlinear_pack_workspace_bytes(n, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
+    _check(lib.bitlinear_pack_weights_binary(_ptr(w), n, k, _ptr(packed), _ptr(gamma), _ptr(ws),
+                                             ws_bytes, _stream(w.device)))
+    return packed, gamma
+
+
+def forward_binary(packed, gamma, xq, absmax, algo="auto", want_acc=False):
+    """Steps A2 + A3 on binary weights: -> y float32[T, N] (and acc int32)."""
+    lib = load()
+    _need_cuda(packed, "packed", torch.uint8)
+    _need_cuda(gamma, "gamma", torch.float32)
+    _need_cuda(xq, "xq", torch.int8)
+    _need_cuda(absmax, "absmax", torch.float32)
+    t, k = xq.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 8 != k:
+        raise ValueError("packed must be [N, K/8]")
+    y = torch.empty((t, n), dtype=torch.float32, device=xq.device)
+    acc = torch.empty((t, n), dtype=torch.int32, device=xq.device) if want_acc else None
+    _check(lib.bitlinear_forward_binary(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
+                                        _ptr(y), _ptr(acc), ALGOS[algo], _stream(xq.device)))
+    return (y, acc) if want_acc else y

@@ -17,6 +17,7 @@ constexpr int64_t kMaxT = int64_t(1) << 24;
 constexpr int64_t kMaxN = int64_t(1) << 26;
 constexpr int64_t kMaxNK = int64_t(1) << 38;  // keeps every gamma bucket below 2^62
 constexpr int64_t kMaxTN = int64_t(1) << 36;  // y up to 256 GiB
+constexpr int64_t kMaxBinaryK = 32768;         // int8 rows of the binary decode kernel fit LDS
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -156,6 +157,48 @@ int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, in
   }
   return launched(fn, bl::launch_linear_group(problems, count, T, x_dtype == BL_BF16,
                                               static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                  float* gamma, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const char* fn = "bitlinear_pack_weights_binary";
+  if (!w || !packed || !gamma || !workspace) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (K < 256 || K > kMaxBinaryK || K % 256 != 0)
+    return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 256 in [256, %lld]", fn,
+                (long long)K, (long long)kMaxBinaryK);
+  if (N < 1 || N > kMaxN || N * K > kMaxNK)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 8))
+    return fail(BL_ERR_ALIGN, "%s: w and packed need 16-byte, gamma 4-byte, workspace 8-byte alignment", fn);
+  if (workspace_bytes < bl::kPackWorkspaceBytes)
+    return fail(BL_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                bl::kPackWorkspaceBytes);
+  return launched(fn, bl::launch_pack_binary(w, N, K, packed, gamma,
+                                             static_cast<unsigned long long*>(workspace),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                             const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                             int32_t* acc, int algo, void* stream) {
+  const char* fn = "bitlinear_forward_binary";
+  if (!packed || !gamma || !xq || !absmax || !y)
+    return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (K < 256 || K > kMaxBinaryK || K % 256 != 0)
+    return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 256 in [256, %lld]", fn,
+                (long long)K, (long long)kMaxBinaryK);
+  if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
+  if (N < 1 || N > kMaxN || T * N > kMaxTN || T * K >= (int64_t(1) << 31) ||
+      N * (K / 32) >= (int64_t(1) << 31))
+    return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      !aligned(y, 4) || (acc && !aligned(acc, 4)))
+    return fail(BL_ERR_ALIGN, "%s: packed and xq need 16-byte, the others 4-byte alignment", fn);
+  if (algo != BL_ALGO_AUTO && algo != BL_ALGO_GEMV && algo != BL_ALGO_GEMM)
+    return fail(BL_ERR_ARG, "%s: algo %d not available for binary weights", fn, algo);
+  return launched(fn, bl::launch_forward_binary(packed, gamma, xq, absmax, T, N, K, y, acc, algo,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,

@@ -26,6 +26,21 @@ constexpr size_t kPackWorkspaceBytes = kGammaBuckets * sizeof(unsigned long long
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
                        unsigned long long* buckets, hipStream_t stream);
 
+// gamma = mean |W| alone (exact sum, one rounding), shared by both weight formats.
+hipError_t launch_gamma(const float* w, int64_t n, int64_t k, float* gamma,
+                        unsigned long long* buckets, hipStream_t stream);
+
+// Binary weights (+1 / -1, one bit each): step A0, and steps A2 + A3 (K % 256 == 0).
+hipError_t launch_pack_binary(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                              float* gamma, unsigned long long* buckets, hipStream_t stream);
+hipError_t launch_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                                 const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                                 int32_t* acc, int algo, hipStream_t stream);
+// The tiled MFMA kernel on one-bit weights (any T, K % 128 == 0).
+hipError_t launch_gemm_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                              const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                              int32_t* acc, hipStream_t stream);
+
 hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
                         float* absmax, int32_t* rowsum, hipStream_t stream);
 
@@ -89,6 +104,42 @@ __device__ __forceinline__ uint32_t codes_of(uint32_t word, int j) {
 __device__ __forceinline__ float out_scale(float gamma, float absmax) {
   const float m = fmaxf(absmax, kEps);
   return (gamma * m) / kQb;
+}
+
+// DPP row reductions (16 lanes), then the four rows through readlane.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Block barrier for LDS traffic only.  __syncthreads() also orders global
+// memory, and on this target loads and stores share one counter, so it would
+// wait for every weight load in flight.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_sync() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));   // lgkmcnt, expcnt: no wait
 }
 
 // Gated ReLU^2 of one output pair, rounded to bfloat16 (nearest, ties to

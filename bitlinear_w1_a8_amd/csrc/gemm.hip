@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t signed_codes(uint32_t word, int j) {
   return __builtin_amdgcn_perm(kTernTable, kTernTable, codes_of(word, j));
 }
 
+// One-bit weights (bit 1 = +1, 0 = -1): bits j of the four bytes of a word are
+// four consecutive k; byte-permute them through {-1, +1}.
+constexpr uint32_t kBinTable = 0x000001FFu;   // bytes {0xFF, 0x01}
+__device__ __forceinline__ uint32_t signed_bits(uint32_t word, int j) {
+  return __builtin_amdgcn_perm(kBinTable, kBinTable, (word >> j) & 0x01010101u);
+}
+
 template <int WMF, int WNF>
 __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ packed,
                                                    const float* __restrict__ gamma,
@@ -207,14 +214,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ 
 //   packed weights: 1 KiB = 32 rows x 32 bytes (8 words = 128 k), row-major.
 // Each wave reads its four weight words per fragment with one 16-byte LDS
 // read and expands them in registers, as in the kernel above.
-// s_waitcnt vmcnt(N) with the other counters left alone (N < 16)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  // vmcnt N (bits 3:0 and 15:14), expcnt 7, lgkmcnt 15: only loads are waited on
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -231,10 +230,16 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // outstanding load before each LDS read (one array indexed by stage is not
 // enough for that).
 //
+// WBITS = 1: one-bit weights (K / 8 bytes per row; bit 8i + j of word g is
+// k = 32g + 4j + i).  A K step then holds 4 words per row (16 bytes), step s
+// and lane half h take word s, bits 4h .. 4h + 3 of each byte: k = 32s + 16h +
+// [0, 16), which is 16-byte activation slot 2s + h.
+//
 // GATED: the weight rows come in (gate, up) pairs, 2i and 2i + 1, which sit in
 // neighbouring lanes of a fragment; the even lane takes its neighbour's sum
 // and writes the bfloat16 gated ReLU^2 of output i to h (y is not used).
-template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED>
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED,
+          int WBITS = 2>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
                                                          const int8_t* __restrict__ xq,
@@ -250,8 +255,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
-  constexpr int kABuf = BM * BK, kBBuf = BN * (BK / 4);   // bytes per stage
-  constexpr int kAChunks = BM / 8 / WAVES, kBChunks = BN / 32 / WAVES;  // 1 KiB loads per wave
+  static_assert(WBITS == 1 || WBITS == 2, "one- or two-bit weights");
+  constexpr int kBRow = BK * WBITS / 8;                    // packed bytes per row per K step
+  constexpr int kABuf = BM * BK, kBBuf = BN * kBRow;       // bytes per stage
+  constexpr int kAChunks = BM / 8 / WAVES, kBChunks = kBBuf / 1024 / WAVES;  // 1 KiB loads per wave
   static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the wave count");
   __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf];
   __shared__ __align__(16) unsigned char A2[STAGES > 2 ? kABuf : 16];
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int K16 = K >> 4;
+  const int KW = K >> (WBITS == 2 ? 4 : 5);   // packed words per row
 
   const int ntn = (N + BN - 1) / BN, ntm = (T + BM - 1) / BM;
   const int tiles = ntn * ntm;
@@ -328,9 +335,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
   for (int i = 0; i < kBChunks; ++i) {
     const int c = wave * kBChunks + i;
-    int n = n0 + 32 * c + (lane >> 1);
-    n = n < N ? n : N - 1;
-    boff[i] = (uint32_t)n * (uint32_t)K16 + 4u * (lane & 1);
+    if constexpr (WBITS == 2) {   // 1 KiB = 32 rows x 32 bytes
+      int n = n0 + 32 * c + (lane >> 1);
+      n = n < N ? n : N - 1;
+      boff[i] = (uint32_t)n * (uint32_t)KW + 4u * (lane & 1);
+    } else {                      // 1 KiB = 64 rows x 16 bytes
+      int n = n0 + 64 * c + lane;
+      n = n < N ? n : N - 1;
+      boff[i] = (uint32_t)n * (uint32_t)KW;
+    }
   }
   auto issue = [&](int kt, unsigned char* As, unsigned char* Bs) {
     const uint32_t k0 = kbase + (uint32_t)kt * BK;
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
                                        (lds_ptr_t)(As + (wave * kAChunks + i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> 4))),
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)))),
                                        (lds_ptr_t)(Bs + (wave * kBChunks + i) * 1024), 16, 0, 0);
   };
 
@@ -379,13 +392,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     // is never read again
     issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, abuf(R{}), bbuf(R{}));
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
-    const unsigned char* Bt = bbuf(stage_c) + (wn * 32 * WNF + m) * (BK / 4) + 16 * h;
+    const unsigned char* Bt =
+        bbuf(stage_c) + (wn * 32 * WNF + m) * kBRow + (WBITS == 2 ? 16 * h : 0);
     uint4 bw[WNF];
 #pragma unroll
-    for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * (BK / 4));
+    for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * kBRow);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int off = 16 * ((4 * h + s) ^ aswz);
+      const int off = 16 * ((WBITS == 2 ? 4 * h + s : 2 * s + h) ^ aswz);
       v4i a[WMF];
 #pragma unroll
       for (int i = 0; i < WMF; ++i) {
@@ -396,8 +410,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       for (int j = 0; j < WNF; ++j) {
         // expand one weight fragment right before its MFMAs (few live registers)
         const uint32_t w = s == 0 ? bw[j].x : s == 1 ? bw[j].y : s == 2 ? bw[j].z : bw[j].w;
-        const v4i b = {(int)signed_codes(w, 0), (int)signed_codes(w, 1),
-                       (int)signed_codes(w, 2), (int)signed_codes(w, 3)};
+        v4i b;
+        if constexpr (WBITS == 2) {
+          b = v4i{(int)signed_codes(w, 0), (int)signed_codes(w, 1), (int)signed_codes(w, 2),
+                  (int)signed_codes(w, 3)};
+        } else {
+          const uint32_t wh = w >> (4 * h);
+          b = v4i{(int)signed_bits(wh, 0), (int)signed_bits(wh, 1), (int)signed_bits(wh, 2),
+                  (int)signed_bits(wh, 3)};
+        }
 #pragma unroll
         for (int i = 0; i < WMF; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
@@ -408,7 +429,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     // by the barrier.  A plain s_barrier, not __syncthreads(): the latter's
     // release fence would also wait for the refill issued above.  The only
     // LDS writes in the loop are these loads, which the wait covers.
-    wait_vm<kLoads * (STAGES - 2)>();
+    wait_vmem<kLoads * (STAGES - 2)>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     if (kt + 1 < nk) step(I1{}, kt + 1);
   if constexpr (STAGES == 4)
     if (kt + 2 < nk) step(I2{}, kt + 2);
-  wait_vm<0>();   // no load may land in LDS after the block has finished
+  wait_vmem<0>();   // no load may land in LDS after the block has finished
 
   if constexpr (GATED) {
     const int half = N >> 1;
@@ -504,7 +525,7 @@ __global__ __launch_bounds__(256) void k_split_finish(float* __restrict__ y,
   }
 }
 
-template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool GATED = false>
+template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool GATED = false, int WBITS = 2>
 hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
                    hipStream_t stream, int splits = 1, int ksteps = 0,
@@ -514,7 +535,8 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
   if (splits == 1) ksteps = (int)(k / BK);
   constexpr int BM = WAVES_M * 32 * WMF, BN = (WAVES / WAVES_M) * 32 * WNF;
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  auto kern = GATED        ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, GATED>
+  auto kern = WBITS == 1   ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>
+              : GATED      ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, GATED>
               : splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false>
                            : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false>;
   kern<<<dim3((unsigned)(tiles * splits)), WAVES * 64, 0, stream>>>(
@@ -618,6 +640,19 @@ hipError_t launch_gemm_gated(const uint8_t* packed, const float* gamma_gate,
                                                      nullptr, acc, stream, 1, 0, gamma_up, h);
   return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
                                                    nullptr, acc, stream, 1, 0, gamma_up, h);
+}
+
+hipError_t launch_gemm_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                              const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                              int32_t* acc, hipStream_t stream) {
+  // the host keeps the kernel's 32-bit offsets in range (K % 128 == 0 by the caller)
+  const int64_t mt = (t + 127) / 128;
+  const int64_t wide = mt * ((n + 511) / 512);
+  if (wide >= BL_GEMM_WIDE_MIN_TILES)
+    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                         stream);
+  return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                       stream);
 }
 
 }  // namespace bl

@@ -245,42 +245,6 @@ struct DecGroup {
 constexpr int kDecHead = 64 + 256 * 4 + 4 + 16 * 4 + 12;   // padded to 16 bytes
 static_assert(kDecHead % 16 == 0, "LDS header alignment");
 
-// DPP row reductions (16 lanes), then the four rows through readlane.
-__device__ __forceinline__ int wave_max_nonneg(int v) {
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));  // row_mirror
-  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
-  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
-// Block barrier for LDS traffic only.  __syncthreads() also orders global
-// memory, and on this target loads and stores share one counter, so it would
-// wait for every weight load in flight.  The empty asm statements keep the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_sync() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));   // lgkmcnt, expcnt: no wait
-}
-
 typedef __attribute__((address_space(3))) void* dec_lds_t;
 typedef __attribute__((address_space(1))) void* dec_glb_t;
 

@@ -32,13 +32,6 @@ constexpr int kLutThreads = kLutWaves * 64;
 constexpr int kLutVecs = kLutWords / 4 / 4 / kLutWaves;   // 16-byte vectors per lane per chunk
 constexpr int kLutGroups = kLutWords * 8 / kLutThreads;   // table groups per thread
 
-__device__ __forceinline__ void lut_lds_sync() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only: weight loads stay in flight
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 template <bool VEC4>
 __global__ __launch_bounds__(kLutThreads) void k_gemv_lut(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
@@ -87,7 +80,7 @@ __global__ __launch_bounds__(kLutThreads) void k_gemv_lut(const uint32_t* __rest
         for (int q = 0; q < 4; ++q) wv[mm][q] = w0 + q < words ? wrow[w_base + w0 + q] : 0u;
       }
     }
-    lut_lds_sync();   // the previous chunk's lookups are done
+    lds_sync();   // the previous chunk's lookups are done
 #pragma unroll
     for (int u = 0; u < kLutGroups; ++u) {
       const int grp = tid + u * kLutThreads;
@@ -110,7 +103,7 @@ __global__ __launch_bounds__(kLutThreads) void k_gemv_lut(const uint32_t* __rest
         *reinterpret_cast<uint2*>(t + 4 * cb) = pr;
       }
     }
-    lut_lds_sync();
+    lds_sync();
     // lookups: one per nibble, words past the chunk skipped
 #pragma unroll
     for (int mm = 0; mm < kLutVecs; ++mm) {
@@ -129,7 +122,7 @@ __global__ __launch_bounds__(kLutThreads) void k_gemv_lut(const uint32_t* __rest
   sum += __shfl_xor(sum, 1);
   sum += __shfl_xor(sum, 2);
   if (sub == 0) part[wave][lane >> 2] = sum;
-  lut_lds_sync();
+  lds_sync();
   if (wave == 0 && lane < 16) {
     const int r = blockIdx.x * 16 + lane;
     if (r < N) {

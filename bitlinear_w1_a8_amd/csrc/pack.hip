@@ -159,14 +159,22 @@ int grid_for(int64_t items, int threads, int cap) {
 
 }  // namespace
 
-hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
-                       unsigned long long* buckets, hipStream_t stream) {
+hipError_t launch_gamma(const float* w, int64_t n, int64_t k, float* gamma,
+                        unsigned long long* buckets, hipStream_t stream) {
   const int64_t count = n * k;
   k_zero_u64<<<1, kGammaBuckets, 0, stream>>>(buckets, kGammaBuckets);
   const int64_t n4 = count / 4;
   k_gamma_hist<<<grid_for(n4, kHistThreads, 2048), kHistThreads, 0, stream>>>(
       reinterpret_cast<const float4*>(w), n4, buckets);
   k_gamma_finalize<<<1, 64, 0, stream>>>(buckets, count, gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                       unsigned long long* buckets, hipStream_t stream) {
+  const int64_t count = n * k;
+  hipError_t e = launch_gamma(w, n, k, gamma, buckets, stream);
+  if (e != hipSuccess) return e;
   const int64_t nwords = count / 16;
   k_ternarize_pack<<<grid_for(nwords, 256, 65536), 256, 0, stream>>>(
       reinterpret_cast<const float4*>(w), nwords, gamma, reinterpret_cast<uint32_t*>(packed));

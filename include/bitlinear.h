@@ -222,6 +222,42 @@ typedef struct bl_linear {
 int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
                              void* stream);
 
+/* Step A0 for binary weights (+1 / -1, one bit each).  The original BitNet
+ * has only these two values (the 2B4T explainer, section 2; "BitNet解读", on
+ * the zero weight); no page gives the rule, which is read as the absmean
+ * scheme with two levels: gamma = mean |W| over all N*K entries (eq. (3), as
+ * bitlinear_pack_weights computes it), t = +1 where W >= 0 (either zero) and
+ * -1 where W < 0.  Layout: row n at byte n*K/8; weight k = 32g + 4j + i of a
+ * row is bit 8i + j of its little-endian 32-bit word g (bit 1 = +1).
+ *
+ *   w         [N, K] float32 latent weights, row-major, 16-byte aligned.
+ *   N, K      1 <= N <= 2^26, 256 <= K <= 32768, K % 256 == 0.
+ *   packed    [N, K/8] uint8 output, 16-byte aligned.
+ *   gamma     [1] float32 output (device), 4-byte aligned.
+ *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K) bytes.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
+int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                  float* gamma, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Steps A2 and A3 on binary weights: y[t, n] = (sum_k t[n,k] * xq[t,k]) *
+ * gamma * max(absmax[t], eps) / 127 with t in {-1, +1}, exact in int32, as
+ * bitlinear_forward.  BL_ALGO_AUTO takes the decode kernel for T <= 16 with
+ * T*K <= 32768, else the tiled MFMA kernel; BL_ALGO_GEMV (the decode kernel,
+ * tokens taken as many as fit at a time) and BL_ALGO_GEMM force one; results
+ * are identical for every choice.
+ *
+ *   packed   [N, K/8] from bitlinear_pack_weights_binary, 16-byte aligned.
+ *   gamma    [1] float32 (device).
+ *   xq, absmax, y, acc   as bitlinear_forward.
+ *   T, N, K  1 <= T <= 2^24, 1 <= N <= 2^26, 256 <= K <= 32768, K % 256 == 0,
+ *            T*K < 2^31, N*K/32 < 2^31.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (BL_ALGO_LUT or
+ * unknown), BL_ERR_HIP. */
+int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                             const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                             int32_t* acc, int algo, void* stream);
+
 /* Row interleave of two packed matrices of the same shape, for
  * bitlinear_gated_relu2: out row 2i is row i of a, out row 2i + 1 row i of b
  * (four ternary weights per byte in each row, as bitlinear_pack_weights

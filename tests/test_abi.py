@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
 
@@ -200,3 +200,24 @@ def test_gated_relu2_errors(lib):
     assert call(a8=A16 + 1) == BL_ERR_ALIGN        # bfloat16 output
     assert call(a11=A16 + 2) == BL_ERR_ALIGN
     assert "bitlinear_gated_relu2" in (call(a5=0) and _err(lib))
+
+
+def test_binary_errors(lib):
+    f = lib.bitlinear_pack_weights_binary
+    assert f(None, 4, 256, A16, A16, A16, 4096, None) == BL_ERR_NULL
+    assert f(A16, 4, 128, A16, A16, A16, 4096, None) == BL_ERR_SHAPE      # K % 256
+    assert f(A16, 4, 32768 + 256, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A16, 0, 256, A16, A16, A16, 4096, None) == BL_ERR_SHAPE
+    assert f(A16 + 4, 4, 256, A16, A16, A16, 4096, None) == BL_ERR_ALIGN
+    assert f(A16, 4, 256, A16, A16, A16, 8, None) == BL_ERR_WORKSPACE
+    g = lib.bitlinear_forward_binary
+    ok = (A16, A16, A16, A16, 2, 64, 512, A16, None, 0, None)
+    assert g(None, *ok[1:]) == BL_ERR_NULL
+    assert g(*ok[:7], None, None, 0, None) == BL_ERR_NULL
+    assert g(*ok[:6], 768 + 32, *ok[7:]) == BL_ERR_SHAPE
+    assert g(*ok[:4], 0, *ok[5:]) == BL_ERR_SHAPE
+    assert g(*ok[:5], 0, *ok[6:]) == BL_ERR_SHAPE
+    assert g(A16 + 8, *ok[1:]) == BL_ERR_ALIGN
+    assert g(*ok[:9], 3, None) == BL_ERR_ARG                        # no table-lookup kernel
+    assert g(*ok[:9], 9, None) == BL_ERR_ARG
+    assert "binary" in (g(*ok[:9], 3, None) and _err(lib))

@@ -502,3 +502,73 @@ def test_gated_relu2_then_down(bl):
     acc_ref = oracle.contract(qd, oracle.ternarize(wd, gd_ref))
     assert np.array_equal(host(acc), acc_ref)
     check_y(host(y), acc_ref, gd_ref, ad)
+
+
+# ------------------------------------------------------------------ binary weights (W1A8)
+
+BIN_PACK_SHAPES = [(1, 256), (17, 512), (300, 2560), (2560, 6912), (64, 32768)]
+
+
+@pytest.mark.parametrize("n,k", BIN_PACK_SHAPES, ids=[f"N{n}_K{k}" for n, k in BIN_PACK_SHAPES])
+def test_pack_binary(bl, n, k):
+    w = wl.latent_weights(n, k, 0.02, 3000 + n + k)
+    w[0, :8] = [0.0, -0.0, 1e-45, -1e-45, 0.0, -0.0, 3.0, -3.0]
+    packed_ref, gamma_ref = oracle.pack_weights_binary(w)
+    packed, gamma = bl.pack_weights_binary(dev(w))
+    assert host(gamma).view(np.uint32)[0] == np.float32(gamma_ref).view(np.uint32)
+    p = host(packed)
+    bad = int(np.count_nonzero(p != packed_ref))
+    assert bad == 0, f"{bad} of {p.size} packed bytes differ"
+
+
+# (T, N, K, algo): the decode kernel (whole and half 512-k chunks, one chunk
+# per wave, eight chunks per wave, K = 32768 at one token per launch, forced
+# for T > 16 in token groups) and the tiled MFMA kernel (both tile widths,
+# ragged T and N)
+BIN_FWD = [(1, 2560, 2560, "auto"), (1, 6912, 2560, "auto"), (1, 2560, 6912, "auto"),
+           (4, 37, 768, "auto"), (16, 50, 2048, "auto"), (3, 100, 256, "auto"),
+           (1, 8192, 28672, "auto"), (1, 64, 32768, "auto"), (2, 300, 28672, "gemv"),
+           (40, 77, 1024, "gemv"), (40, 77, 1024, "auto"), (300, 500, 2560, "auto"),
+           (1100, 3800, 512, "auto"), (17, 1000, 6912, "gemm"), (5, 33, 256, "gemm")]
+
+
+@pytest.mark.parametrize("t,n,k,algo", BIN_FWD, ids=[f"T{t}_N{n}_K{k}_{a}" for t, n, k, a in BIN_FWD])
+def test_forward_binary(bl, t, n, k, algo):
+    w = wl.latent_weights(n, k, 0.02, 3100 + t + n + k)
+    x = wl.activations_student_t(t, k, 4, 3200 + t + k)
+    if t > 2:
+        x[1] = 0.0                                       # an all-zero token
+    packed, gamma = bl.pack_weights_binary(dev(w))
+    q_ref, a_ref, _ = oracle.quant_act(x)
+    y, acc = bl.forward_binary(packed, gamma, dev(q_ref), dev(a_ref), algo=algo, want_acc=True)
+    _, gamma_ref = oracle.pack_weights_binary(w)
+    acc_ref = oracle.contract(q_ref, oracle.binarize(w))
+    a = host(acc)
+    bad = int(np.count_nonzero(a != acc_ref))
+    assert bad == 0, f"{bad} of {a.size} int32 sums differ"
+    check_y(host(y), acc_ref, gamma_ref, a_ref)
+
+
+def test_forward_binary_extremes(bl):
+    """All q = +-127 against all-+1 / all--1 / alternating rows, and an all-zero
+    matrix (every weight +1, gamma = 0): the largest sums and exact zeros."""
+    t, n, k = 3, 48, 4096
+    w = np.ones((n, k), np.float32)
+    w[1::2] = -1.0
+    w[5, ::2] = -1.0
+    q = np.full((t, k), 127, np.int8)
+    q[1] = -127
+    q[2, ::2] = -127
+    absmax = np.array([5.0, 0.25, 1e-7], np.float32)
+    packed, gamma = bl.pack_weights_binary(dev(w))
+    for algo in ("gemv", "gemm"):
+        y, acc = bl.forward_binary(packed, gamma, dev(q), dev(absmax), algo=algo, want_acc=True)
+        acc_ref = oracle.contract(q, oracle.binarize(w))
+        a = host(acc)
+        assert np.array_equal(a, acc_ref) and a[0, 0] == 127 * k
+        check_y(host(y), acc_ref, oracle.pack_weights_binary(w)[1], absmax)
+    wz = np.zeros((n, k), np.float32)
+    packed, gamma = bl.pack_weights_binary(dev(wz))
+    assert np.all(host(packed) == 0xFF) and host(gamma)[0] == 0.0
+    y = host(bl.forward_binary(packed, gamma, dev(q), dev(absmax)))
+    assert np.all(y == 0.0)           # -0 where the sum is negative, as acc * +0 gives
