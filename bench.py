@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill GEMM context run")
     p.add_argument("--extra", default="all",
                    help="context runs to do: 'all' or a comma list of prefill, crossover, 70b, "
-                        "subln, gated, lut")
+                        "subln, gated, lut, binary")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--fused-only", action="store_true",
@@ -502,6 +502,56 @@ def lut_extra(torch, binding, mats, sets, dev, stream, calls):
     return out
 
 
+def binary_extra(torch, binding, dev, stream):
+    """Binary (+1/-1, one bit each) weights against the ternary format on the
+    same shapes: T = 1 (decode kernels, int8 input, weights rotated over
+    > 1 GB) on 2560->6912, 6912->2560 and 8192->28672, and T = 2048 (tiled
+    MFMA kernels, 64 rotated copies) on 2560->6912.  Weights drawn on the GPU
+    (N(0, 0.02), seeded)."""
+    lib = binding.load()
+    calls = Calls(lib)
+    out = {}
+    for (k, n, t) in ((2560, 6912, 1), (6912, 2560, 1), (8192, 28672, 1), (2560, 6912, 2048)):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(9100 + k + t)
+        w = torch.randn((n, k), device=dev, generator=gen) * 0.02
+        pt, gt = binding.pack_weights(w)
+        pb, gb = binding.pack_weights_binary(w)
+        del w
+        xq = torch.randint(-127, 128, (t, k), dtype=torch.int8, device=dev)
+        am = torch.rand(t, device=dev) * 4 + 1
+        y = torch.empty((t, n), dtype=torch.float32, device=dev)
+        rec = {}
+        for name, p, g in (("ternary", pt, gt), ("binary", pb, gb)):
+            ncopy = int(np.ceil(ROT_BYTES / p.numel())) if t == 1 else 64
+            copies = [p] + [p.clone() for _ in range(ncopy - 1)]
+            P = [ptr(c) for c in copies]
+            if name == "ternary":
+                fn = lambda s, i: calls.forward(P[i], ptr(g), ptr(xq), ptr(am), t, n, k, ptr(y), 0,
+                                                ctypes.c_void_p(s.cuda_stream))
+            else:
+                def fn(s, i):
+                    rc = lib.bitlinear_forward_binary(P[i], ptr(g), ptr(xq), ptr(am), t, n, k, ptr(y),
+                                                      None, 0, ctypes.c_void_p(s.cuda_stream))
+                    if rc:
+                        raise RuntimeError(lib.bitlinear_last_error().decode())
+            us = rotated_time_us(torch, fn, ncopy, stream, reps=5 if t == 1 else 4)
+            wbytes = p.numel()
+            if t == 1:
+                byts = wbytes + k + 4 + 4 * n + 4
+                rec[name] = {"us": round(us, 2), "gb_s": round(byts / us / 1e3, 1),
+                             "frac_of_hbm_peak": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)}
+            else:
+                ops = 2.0 * t * n * k
+                rec[name] = {"us": round(us, 2), "tops": round(ops / us / 1e6, 1),
+                             "frac_of_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
+            del copies
+        out[f"T{t}_{k}->{n}"] = rec
+        del pt, pb
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -633,7 +683,7 @@ def main():
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     want = set(args.extra.split(",")) if args.extra != "all" else {
-        "prefill", "crossover", "70b", "subln", "gated", "lut"}
+        "prefill", "crossover", "70b", "subln", "gated", "lut", "binary"}
     if not args.no_extra:
         if "prefill" in want:
             extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
@@ -645,6 +695,8 @@ def main():
             extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
         if "gated" in want:
             extra["gated_relu2_ffn"] = gated_extra(torch, binding, dev, stream)
+        if "binary" in want:
+            extra["binary_weights"] = binary_extra(torch, binding, dev, stream)
         if "lut" in want:
             extra["lut_decode_comparison"] = lut_extra(torch, binding, mats, sets, dev, stream, calls)
 

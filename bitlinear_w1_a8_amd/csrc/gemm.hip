@@ -535,10 +535,17 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
   if (splits == 1) ksteps = (int)(k / BK);
   constexpr int BM = WAVES_M * 32 * WMF, BN = (WAVES / WAVES_M) * 32 * WNF;
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
-  auto kern = WBITS == 1   ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>
-              : GATED      ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, GATED>
-              : splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false>
-                           : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false>;
+  // only the kernels a configuration uses are instantiated
+  auto pick = [&]() {
+    if constexpr (WBITS == 1)
+      return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>;
+    else if constexpr (GATED)
+      return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, true>;
+    else
+      return splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false>
+                        : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false>;
+  };
+  auto kern = pick();
   kern<<<dim3((unsigned)(tiles * splits)), WAVES * 64, 0, stream>>>(
       reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc,
       ksteps, splits, gamma2, h);
