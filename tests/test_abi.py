@@ -221,3 +221,24 @@ def test_binary_errors(lib):
     assert g(*ok[:9], 3, None) == BL_ERR_ARG                        # no table-lookup kernel
     assert g(*ok[:9], 9, None) == BL_ERR_ARG
     assert "binary" in (g(*ok[:9], 3, None) and _err(lib))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No CPU fallback: without the built library every entry point raises."""
+    from bitlinear_w1_a8_amd import binding
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libbitlinear.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(ImportError):
+        binding.load()
+    with pytest.raises(ImportError):
+        binding.gemv_max_tokens()
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "bitlinear_w1_a8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f

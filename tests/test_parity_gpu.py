@@ -572,3 +572,54 @@ def test_forward_binary_extremes(bl):
     assert np.all(host(packed) == 0xFF) and host(gamma)[0] == 0.0
     y = host(bl.forward_binary(packed, gamma, dev(q), dev(absmax)))
     assert np.all(y == 0.0)           # -0 where the sum is negative, as acc * +0 gives
+
+
+# ------------------------------------------------------------------ HIP graph capture
+
+def test_graph_replays_match_eager(bl):
+    """The entry points a decode or prefill loop would capture, replayed from
+    a HIP graph several times with unrelated eager work in between: every
+    replay equals the eager result bit for bit (no memset nodes are recorded;
+    the K-split path clears with a kernel)."""
+    k, n = 2560, 640
+    ws = []
+    for i in range(3):
+        w = wl.latent_weights(n, k, 0.02, 8000 + i)
+        ws.append(bl.pack_weights(dev(w)))
+    x1 = dev_bf16(wl.bf16_bits(wl.activations_normal(1, k, 8010)))
+    pg, gg = ws[0]
+    pu, gu = ws[1]
+    pgu = bl.interleave_rows(pg, pu)
+    wbig = wl.latent_weights(1500, 28672, 0.02, 8011)
+    pbig, gbig = bl.pack_weights(dev(wbig))
+    xq_big, am_big, _ = bl.quant_act(dev(wl.activations_normal(200, 28672, 8012)))
+    pb, gb = bl.pack_weights_binary(dev(wl.latent_weights(n, k, 0.02, 8013)))
+    xq1, am1, _ = bl.quant_act(x1)
+
+    def calls():
+        outs = [o[0] for o in bl.linear_grouped([x1, x1, x1], ws)]
+        outs.append(bl.gated_relu2(x1, pgu, gg, gu)[0])
+        outs.append(bl.forward(pbig, gbig, xq_big, am_big, 1500, algo="gemm"))  # K split
+        outs.append(bl.forward_binary(pb, gb, xq1, am1))
+        return outs
+
+    eager = [host(o).copy() for o in [t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+                                      for t in calls()]]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        calls()                                          # warm up on the capture stream
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        static = calls()
+    for rep in range(4):
+        for t in static:
+            t.fill_(7)                                   # stale values must be overwritten
+        junk = torch.randn(4096, device="cuda").sum()    # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t.view(torch.int16) if t.dtype == torch.bfloat16 else t) for t in static]
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {rep}, output {i}"
+        del junk
