@@ -15,9 +15,10 @@ constexpr float kEps = 1e-5f;
 constexpr float kQb = 127.0f;
 
 // T at or below which the automatic choice takes the decode kernel: measured
-// on 2560->6912 and 6912->2560, it is faster through T = 128 and the tiled
-// MFMA kernel from T = 256 on.
-constexpr int64_t kGemvMaxTokens = 128;
+// on 2560->6912 and 6912->2560 against the tiled MFMA kernel with its tile
+// choice, the decode kernel is faster through T = 32 on both, within 5% at
+// T = 64 (faster on one, slower on the other) and twice as slow at T = 128.
+constexpr int64_t kGemvMaxTokens = 64;
 
 // Exponent buckets of the exact gamma sum: one uint64 per binary32 exponent.
 constexpr int kGammaBuckets = 256;
@@ -75,7 +76,7 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
                         const float* gamma_up, int64_t t, int64_t n, int64_t k, uint16_t* h,
                         int8_t* xq, float* absmax, int32_t* acc, hipStream_t stream);
 
-// The int8-input kernels of the gated path: the decode kernels (t <= 128) and
+// The int8-input kernels of the gated path: the decode kernels (t <= 64) and
 // the tiled MFMA kernel.
 hipError_t launch_gemv_gated(const uint8_t* packed, const float* gamma_gate,
                              const float* gamma_up, const int8_t* xq, const float* absmax,

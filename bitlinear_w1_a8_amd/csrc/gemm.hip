@@ -575,14 +575,16 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 }  // namespace
 
 #ifndef BL_GEMM_BIG_MIN_TILES
-#define BL_GEMM_BIG_MIN_TILES 384   // use 256 x 128 tiles when at least this many exist
-#endif
-
-#ifndef BL_GEMM_LDS_MIN_TILES
-#define BL_GEMM_LDS_MIN_TILES 128   // LDS-direct tiles from this many tiles on
+#define BL_GEMM_BIG_MIN_TILES 384   // K % 128 != 0: 256 x 128 tiles when at least this many exist
 #endif
 #ifndef BL_GEMM_WIDE_MIN_TILES
-#define BL_GEMM_WIDE_MIN_TILES 192  // 128 x 512 tiles when they keep this many CUs busy
+#define BL_GEMM_WIDE_MIN_TILES 160  // 128 x 512 tiles from this many on
+#endif
+#ifndef BL_GEMM_NARROW_MIN_TILES
+#define BL_GEMM_NARROW_MIN_TILES 224  // 128 x 256 tiles from this many on (rows at least 90% used)
+#endif
+#ifndef BL_GEMM_M64_MIN_TILES
+#define BL_GEMM_M64_MIN_TILES 256   // 64 x 256 tiles from this many on, else 64 x 128
 #endif
 #ifndef BL_GEMM_STAGES
 #define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
@@ -590,45 +592,78 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_SPLIT_ITEMS
 #define BL_GEMM_SPLIT_ITEMS 256     // K split: (part, tile) items aimed for
 #endif
-#ifndef BL_GEMM_SPLIT_MIN_OPS
-#define BL_GEMM_SPLIT_MIN_OPS 17179869184.0   // K split only from 2*T*N*K = 2^34 on
+#ifndef BL_GEMM_SPLIT_MIN_K
+#define BL_GEMM_SPLIT_MIN_K 16384   // K split only for long rows ...
 #endif
+#ifndef BL_GEMM_SPLIT_MAX_TILES
+#define BL_GEMM_SPLIT_MAX_TILES 128 // ... that make fewer than this many 64 x 128 tiles
+#endif
+
+namespace {
+
+// Tile shape of the LDS-direct kernel for a problem, from measurements on
+// MI355X over T in 160..8192 and the 2B / 70B-class shapes: the widest tiles
+// that still give most CUs a block, 64-row tiles (several blocks per CU) when
+// 128-row ones would leave CUs idle or rows unused, and a K split only for
+// long K with very few tiles.
+enum class Tiles { kWide, kNarrow, kM64W256, kM64W128, kSplit };
+
+Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow_w128) {
+  const int64_t m128 = (t + 127) / 128, m64 = (t + 63) / 64;
+  const int64_t wide = m128 * ((n + 511) / 512), narrow = m128 * ((n + 255) / 256);
+  const int64_t w256 = m64 * ((n + 255) / 256), w128 = m64 * ((n + 127) / 128);
+  const bool rows_used = 10 * t >= 9 * 128 * m128;   // 128-row tiles at least 90% full
+  if (wide >= BL_GEMM_WIDE_MIN_TILES) return Tiles::kWide;
+  if (narrow >= BL_GEMM_NARROW_MIN_TILES && rows_used) return Tiles::kNarrow;
+  if (w256 >= BL_GEMM_M64_MIN_TILES || !allow_w128) return Tiles::kM64W256;
+  if (allow_split && k >= BL_GEMM_SPLIT_MIN_K && w128 < BL_GEMM_SPLIT_MAX_TILES && k / BK >= 8)
+    return Tiles::kSplit;
+  return Tiles::kM64W128;
+}
+
+}  // namespace
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                        int32_t* acc, hipStream_t stream) {
-  // LDS-direct tiles: 8 waves of 128 x 64 (128 x 512) where the grid is wide
-  // enough, else 4 waves (128 x 256), which fill twice as many CUs, else the
-  // 128 x 512 tiles with K split into parts when the problem is large
   const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
-  const int64_t mt = (t + 127) / 128;
-  const int64_t wide = mt * ((n + 511) / 512), narrow = mt * ((n + 255) / 256);
-  if (lds_ok && wide >= BL_GEMM_WIDE_MIN_TILES)
-    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
-  if (lds_ok && narrow >= BL_GEMM_LDS_MIN_TILES)
-    return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
-  const int64_t nkt = k / BK;
-  if (lds_ok && nkt >= 8 && 2.0 * (double)t * (double)n * (double)k >= BL_GEMM_SPLIT_MIN_OPS &&
-      t * n < (int64_t(1) << 31)) {
-    int64_t parts = (BL_GEMM_SPLIT_ITEMS + wide - 1) / wide;
-    int64_t steps = (nkt + parts - 1) / parts;
-    if (steps < 4) steps = 4;
-    parts = (nkt + steps - 1) / steps;             // every part has at least one step
-    const int64_t total = t * n;
-    k_clear_i32<<<(unsigned)std::min<int64_t>((total + 255) / 256, 4096), 256, 0, stream>>>(
-        reinterpret_cast<int*>(y), total);
-    hipError_t e = run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                       stream, (int)parts, (int)steps);
-    if (e != hipSuccess) return e;
-    const int col_blocks = (int)((n + 1023) / 1024);
-    k_split_finish<<<(unsigned)(t * col_blocks), 256, 0, stream>>>(y, acc, gamma, absmax, (int)n,
-                                                                   col_blocks);
-    return hipGetLastError();
+  if (!lds_ok) {
+    // K % 128 != 0 (or offsets beyond 32 bits): the register-staged kernel
+    const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
+    if (big >= BL_GEMM_BIG_MIN_TILES)
+      return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   }
-  const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
-  if (big >= BL_GEMM_BIG_MIN_TILES)
-    return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
-  return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+  switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true)) {
+    case Tiles::kWide:
+      return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    case Tiles::kNarrow:
+      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    case Tiles::kM64W256:
+      return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    case Tiles::kM64W128:
+      return run_lds<4, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+    case Tiles::kSplit: {
+      // 128 x 512 tiles, K in parts: y is cleared, takes the exact int32
+      // partial sums by atomics and is rescaled in place
+      const int64_t nkt = k / BK, wide = ((t + 127) / 128) * ((n + 511) / 512);
+      int64_t parts = (BL_GEMM_SPLIT_ITEMS + wide - 1) / wide;
+      int64_t steps = (nkt + parts - 1) / parts;
+      if (steps < 4) steps = 4;
+      parts = (nkt + steps - 1) / steps;             // every part has at least one step
+      const int64_t total = t * n;
+      k_clear_i32<<<(unsigned)std::min<int64_t>((total + 255) / 256, 4096), 256, 0, stream>>>(
+          reinterpret_cast<int*>(y), total);
+      hipError_t e = run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                         stream, (int)parts, (int)steps);
+      if (e != hipSuccess) return e;
+      const int col_blocks = (int)((n + 1023) / 1024);
+      k_split_finish<<<(unsigned)(t * col_blocks), 256, 0, stream>>>(y, acc, gamma, absmax, (int)n,
+                                                                     col_blocks);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_gated(const uint8_t* packed, const float* gamma_gate,
@@ -640,26 +675,39 @@ hipError_t launch_gemm_gated(const uint8_t* packed, const float* gamma_gate,
   const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
   if (!lds_ok)
     return launch_gemv_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream);
-  const int64_t mt = (t + 127) / 128;
-  const int64_t wide = mt * ((n + 511) / 512);
-  if (wide >= BL_GEMM_WIDE_MIN_TILES)
-    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
-                                                     nullptr, acc, stream, 1, 0, gamma_up, h);
-  return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
-                                                   nullptr, acc, stream, 1, 0, gamma_up, h);
+  switch (choose_tiles(t, n, k, false, true)) {
+    case Tiles::kWide:
+      return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                       nullptr, acc, stream, 1, 0, gamma_up, h);
+    case Tiles::kNarrow:
+      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                       nullptr, acc, stream, 1, 0, gamma_up, h);
+    case Tiles::kM64W256:
+      return run_lds<4, 1, 2, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                       nullptr, acc, stream, 1, 0, gamma_up, h);
+    default:
+      return run_lds<4, 2, 1, 2, BL_GEMM_STAGES, true>(packed, gamma_gate, xq, absmax, t, n, k,
+                                                       nullptr, acc, stream, 1, 0, gamma_up, h);
+  }
 }
 
 hipError_t launch_gemm_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
                               const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                               int32_t* acc, hipStream_t stream) {
-  // the host keeps the kernel's 32-bit offsets in range (K % 128 == 0 by the caller)
-  const int64_t mt = (t + 127) / 128;
-  const int64_t wide = mt * ((n + 511) / 512);
-  if (wide >= BL_GEMM_WIDE_MIN_TILES)
-    return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                         stream);
-  return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                       stream);
+  // the host keeps the kernel's 32-bit offsets in range (K % 128 == 0 by the
+  // caller); one-bit rows give a 64 x 128 tile too few bytes per wave, so
+  // 64 x 256 is the smallest tile here
+  switch (choose_tiles(t, n, k, false, false)) {
+    case Tiles::kWide:
+      return run_lds<8, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y,
+                                                           acc, stream);
+    case Tiles::kNarrow:
+      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y,
+                                                           acc, stream);
+    default:
+      return run_lds<4, 1, 2, 2, BL_GEMM_STAGES, false, 1>(packed, gamma, xq, absmax, t, n, k, y,
+                                                           acc, stream);
+  }
 }
 
 }  // namespace bl

@@ -417,11 +417,13 @@ def test_interleave_rows(bl):
 # (T, N outputs, K, dtype): fused decode (T <= 4, K % 256 == 0), the int8
 # decode kernel (T <= 16), the 64-token decode kernel (K % 256 != 0, or
 # 16 < T <= 128), T above 128 with K % 128 != 0, the tiled MFMA kernel
-# (128 x 256 and 128 x 512 tiles), and a decode shape over the fused-work limit
+# (every tile shape), and a decode shape over the fused-work limit
 GATED_CASES = [(1, 6912, 2560, "bf16"), (3, 100, 512, "f32"), (4, 37, 256, "bf16"),
                (9, 300, 1024, "bf16"), (16, 50, 2048, "f32"), (40, 77, 1008, "bf16"),
                (70, 64, 320, "f32"), (130, 300, 1040, "bf16"), (300, 500, 2560, "bf16"),
-               (1024, 6144, 512, "bf16"), (2, 8200, 8192, "bf16"), (1, 28672, 8192, "bf16")]
+               (1024, 6144, 512, "bf16"), (2, 8200, 8192, "bf16"), (1, 28672, 8192, "bf16"),
+               # gated MFMA kernel on 64 x 256 and 128 x 256 tiles
+               (1100, 1900, 512, "bf16"), (256, 14336, 1024, "bf16")]
 
 
 def _gated_inputs(bl, t, n, k, dtype, seed):
@@ -529,7 +531,9 @@ BIN_FWD = [(1, 2560, 2560, "auto"), (1, 6912, 2560, "auto"), (1, 2560, 6912, "au
            (4, 37, 768, "auto"), (16, 50, 2048, "auto"), (3, 100, 256, "auto"),
            (1, 8192, 28672, "auto"), (1, 64, 32768, "auto"), (2, 300, 28672, "gemv"),
            (40, 77, 1024, "gemv"), (40, 77, 1024, "auto"), (300, 500, 2560, "auto"),
-           (1100, 3800, 512, "auto"), (17, 1000, 6912, "gemm"), (5, 33, 256, "gemm")]
+           (1100, 3800, 512, "auto"), (17, 1000, 6912, "gemm"), (5, 33, 256, "gemm"),
+           # one-bit MFMA kernel on 128 x 256 and 128 x 512 tiles
+           (256, 28672, 1024, "gemm"), (2048, 6912, 256, "gemm")]
 
 
 @pytest.mark.parametrize("t,n,k,algo", BIN_FWD, ids=[f"T{t}_N{n}_K{k}_{a}" for t, n, k, a in BIN_FWD])
