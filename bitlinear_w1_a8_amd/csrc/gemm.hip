@@ -221,6 +221,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
 }
 
+#ifndef BL_GEMM_GROUP_M
+#define BL_GEMM_GROUP_M 4   // row blocks per group of the tile order
+#endif
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
@@ -300,7 +304,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   int item = blockIdx.x;
   if (items >= 8 && (items % 8) == 0) item = (blockIdx.x % 8) * (items / 8) + blockIdx.x / 8;
   const int part = SPLIT ? item / tiles : 0, tile = item - part * tiles;
-  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+  // grouped order: BL_GEMM_GROUP_M row blocks at a time, down the rows first,
+  // so that the contiguous range of tiles one XCD runs covers a squarer block
+  // of the output (fewer distinct operand tiles through its L2)
+  const int in_group = BL_GEMM_GROUP_M * ntn;
+  const int gid = tile / in_group, first_m = gid * BL_GEMM_GROUP_M;
+  const int gsize = min(ntm - first_m, BL_GEMM_GROUP_M);
+  const int r_in = tile - gid * in_group;
+  const int m0 = (first_m + r_in % gsize) * BM, n0 = (r_in / gsize) * BN;
   const uint32_t kbase = (uint32_t)part * (uint32_t)ksteps * BK;   // first k of this part
 
   // per-token output scale first: its loads retire before the pipeline starts
