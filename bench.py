@@ -468,10 +468,11 @@ def gated_extra(torch, binding, dev, stream):
 
 
 def lut_extra(torch, binding, mats, sets, dev, stream, calls):
-    """The table-lookup decode kernel (bitnet.cpp TL1/TL2 style) against the
-    matrix-core decode kernel at T = 1 on int8 input: the 2B shapes (weights
-    rotated over the layer sets) and 8192 -> 28672 (weights drawn on the GPU,
-    rotated over > 1 GB)."""
+    """The two comparison designs of the decode step, the table-lookup kernel
+    (bitnet.cpp TL1/TL2 style) and the packed-int8-dot (v_dot4) kernel,
+    against the matrix-core decode kernel at T = 1 on int8 input: the 2B
+    shapes (weights rotated over the layer sets) and 8192 -> 28672 (weights
+    drawn on the GPU, rotated over > 1 GB)."""
     out = {}
     for mi in (0, 4, 6):
         d = mats[mi]
@@ -483,9 +484,11 @@ def lut_extra(torch, binding, mats, sets, dev, stream, calls):
         us = [rotated_time_us(
             torch, lambda s, i, a=algo: calls.forward(P[i], ptr(d["gamma"]), ptr(xq), ptr(am), 1, n, k,
                                                       ptr(y), a, ctypes.c_void_p(s.cuda_stream)),
-            len(sets), stream, reps=5) for algo in (3, 1)]
-        out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "decode_kernel_us": round(us[1], 2),
-                            "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1)}
+            len(sets), stream, reps=5) for algo in (3, 4, 1)]
+        out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "dot4_us": round(us[1], 2),
+                            "decode_kernel_us": round(us[2], 2),
+                            "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1),
+                            "dot4_gb_s": round(gemv_bytes(1, n, k) / us[1] / 1e3, 1)}
     n, k = 28672, 8192
     gen = torch.Generator(device=dev)
     gen.manual_seed(5100)
@@ -498,9 +501,11 @@ def lut_extra(torch, binding, mats, sets, dev, stream, calls):
     us = [rotated_time_us(
         torch, lambda s, i, a=algo: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), 1, n, k, ptr(y), a,
                                                   ctypes.c_void_p(s.cuda_stream)),
-        len(copies), stream, reps=5) for algo in (3, 1)]
-    out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "decode_kernel_us": round(us[1], 2),
-                        "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1)}
+        len(copies), stream, reps=5) for algo in (3, 4, 1)]
+    out[f"{k}->{n}"] = {"lut_us": round(us[0], 2), "dot4_us": round(us[1], 2),
+                        "decode_kernel_us": round(us[2], 2),
+                        "lut_gb_s": round(gemv_bytes(1, n, k) / us[0] / 1e3, 1),
+                        "dot4_gb_s": round(gemv_bytes(1, n, k) / us[1] / 1e3, 1)}
     del copies, packed
     torch.cuda.empty_cache()
     return out

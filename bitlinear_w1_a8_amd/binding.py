@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbitlinear.so")
 
 BL_F32, BL_BF16 = 0, 1
-ALGOS = {"auto": 0, "gemv": 1, "gemm": 2, "lut": 3}
+ALGOS = {"auto": 0, "gemv": 1, "gemm": 2, "lut": 3, "dot4": 4}
 
 _lib = None
 

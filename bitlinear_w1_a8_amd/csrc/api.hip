@@ -131,6 +131,8 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
     return launched(fn, bl::launch_gemm(packed, gamma, xq, absmax, T, N, K, y, acc, s));
   if (algo == BL_ALGO_LUT)
     return launched(fn, bl::launch_gemv_lut(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+  if (algo == BL_ALGO_DOT4)
+    return launched(fn, bl::launch_gemv_dot4(packed, gamma, xq, absmax, T, N, K, y, acc, s));
   return fail(BL_ERR_ARG, "%s: unknown algo %d", fn, algo);
 }
 
@@ -196,7 +198,7 @@ int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const in
       !aligned(y, 4) || (acc && !aligned(acc, 4)))
     return fail(BL_ERR_ALIGN, "%s: packed and xq need 16-byte, the others 4-byte alignment", fn);
   if (algo != BL_ALGO_AUTO && algo != BL_ALGO_GEMV && algo != BL_ALGO_GEMM)
-    return fail(BL_ERR_ARG, "%s: algo %d not available for binary weights", fn, algo);
+    return fail(BL_ERR_ARG, "%s: algo %d not available for binary weights", fn, algo);  // LUT, DOT4
   return launched(fn, bl::launch_forward_binary(packed, gamma, xq, absmax, T, N, K, y, acc, algo,
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -61,6 +61,11 @@ hipError_t launch_gemv_lut(const uint8_t* packed, const float* gamma, const int8
                            const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
                            int32_t* acc, hipStream_t stream);
 
+// Packed-int8-dot decode kernel (comparison design), any T (one token per block row).
+hipError_t launch_gemv_dot4(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                            const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
+                            int32_t* acc, hipStream_t stream);
+
 // Steps A1-A3 for a group of problems (bitlinear_linear_grouped).
 hipError_t launch_linear_group(const struct bl_linear* probs, int count, int64_t t, int bf16,
                                hipStream_t stream);

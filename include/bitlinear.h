@@ -89,7 +89,10 @@ typedef enum {
   BL_ALGO_GEMM = 2, /* LDS-tiled int8 MFMA kernel, any T */
   BL_ALGO_LUT = 3   /* table-lookup decode kernel in the style of bitnet.cpp's TL1/TL2
                        ("微软 BitNet ...", section 1.3), any T (weights re-read per
-                       token): a comparison design with the same results */
+                       token): a comparison design with the same results */,
+  BL_ALGO_DOT4 = 4  /* decode kernel on packed int8 dot instructions (v_dot4) instead of
+                       the matrix cores, any T (weights re-read per token): a comparison
+                       design with the same results */
 } bl_algo;
 
 /* Version of this interface (BITLINEAR_ABI_VERSION). */
@@ -252,8 +255,8 @@ int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t*
  *   xq, absmax, y, acc   as bitlinear_forward.
  *   T, N, K  1 <= T <= 2^24, 1 <= N <= 2^26, 256 <= K <= 32768, K % 256 == 0,
  *            T*K < 2^31, N*K/32 < 2^31.
- * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (BL_ALGO_LUT or
- * unknown), BL_ERR_HIP. */
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (BL_ALGO_LUT,
+ * BL_ALGO_DOT4 or unknown), BL_ERR_HIP. */
 int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
                              const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
                              int32_t* acc, int algo, void* stream);

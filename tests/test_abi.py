@@ -103,7 +103,7 @@ def test_forward_errors(lib):
     assert f(A16, A16, A16 + 8, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16 + 2, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16, A16 + 1, 0, None) == BL_ERR_ALIGN
-    assert f(*good, 1, 16, 64, A16, None, 4, None) == BL_ERR_ARG
+    assert f(*good, 1, 16, 64, A16, None, 5, None) == BL_ERR_ARG
     assert f(*good, 1, 16, 64, A16, None, -1, None) == BL_ERR_ARG
     assert lib.bitlinear_forward(None, A16, A16, A16, 1, 16, 64, A16, None, None) == BL_ERR_NULL
 
@@ -219,6 +219,7 @@ def test_binary_errors(lib):
     assert g(*ok[:5], 0, *ok[6:]) == BL_ERR_SHAPE
     assert g(A16 + 8, *ok[1:]) == BL_ERR_ALIGN
     assert g(*ok[:9], 3, None) == BL_ERR_ARG                        # no table-lookup kernel
+    assert g(*ok[:9], 4, None) == BL_ERR_ARG                        # nor a v_dot4 one
     assert g(*ok[:9], 9, None) == BL_ERR_ARG
     assert "binary" in (g(*ok[:9], 3, None) and _err(lib))
 

@@ -213,7 +213,7 @@ def _forward_inputs(t, n, k, seed, zero_rows=True):
     return tern, q, absmax, gamma
 
 
-@pytest.mark.parametrize("algo", ["gemv", "gemm", "lut"])
+@pytest.mark.parametrize("algo", ["gemv", "gemm", "lut", "dot4"])
 @pytest.mark.parametrize("t,n,k", FWD_SHAPES, ids=[f"T{t}_N{n}_K{k}" for t, n, k in FWD_SHAPES])
 def test_forward_shapes(bl, t, n, k, algo):
     tern, q, absmax, gamma = _forward_inputs(t, n, k, 100 * t + n + k)
@@ -232,7 +232,7 @@ def test_forward_extremes(bl):
     q[2, ::2] = -127
     absmax = np.array([5.0, 0.25, 1e-7], np.float32)
     gamma = np.float32(3.0)
-    for algo in ("gemv", "gemm", "lut"):
+    for algo in ("gemv", "gemm", "lut", "dot4"):
         a = check_forward(bl, dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q),
                           dev(absmax), tern, q, gamma, absmax, algo)
         assert a[0, 0] == 127 * k
@@ -293,8 +293,8 @@ def test_workload_full_size(bl, widx, mi):
     for t in w.tokens:
         x = w.activations(mi, t)
         xq, absmax, q_ref, a_ref = check_quant(bl, x, w.x_dtype)
-        algos = ["auto"] + (["gemv", "gemm", "lut"] if widx == 3 else []) + (
-            ["lut"] if widx == 2 else [])
+        algos = ["auto"] + (["gemv", "gemm", "lut", "dot4"] if widx == 3 else []) + (
+            ["lut", "dot4"] if widx == 2 else [])
         for algo in algos:
             check_forward(bl, packed, gamma, xq, absmax, tern, q_ref, gamma_ref, a_ref, algo)
     if widx in (2, 5):
