@@ -434,7 +434,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
         for (int i = 0; i < WMF; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep K steps apart: bounds live registers
+      // no scheduling fence between sub-steps: letting the compiler overlap
+      // one sub-step's LDS reads with the previous one's MFMAs measured 1-4%
+      // faster at the same register count
     }
     // Tile kt+1 must have landed: this wave's loads by the wait, everyone's
     // by the barrier.  A plain s_barrier, not __syncthreads(): the latter's
