@@ -21,6 +21,7 @@
 // tile's loads in flight during the current tile's MFMAs.  Tiles are ordered
 // so that consecutive tiles of one XCD share activation rows in its L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "bl_internal.h"
@@ -572,12 +573,18 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
   const int64_t tiles = ((n + BN - 1) / BN) * ((t + BM - 1) / BM);
   const size_t lds = 2 * (size_t)BM * kLd + BM * sizeof(float);
   auto kern = k_gemm<WMF, WNF>;
-  static bool lds_set = false;  // once per process (idempotent if raced)
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the LDS limit is raised once per device (setting it again is harmless,
+  // so two threads racing here is fine)
+  static std::atomic<uint64_t> lds_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit == 0 || !(lds_set.load(std::memory_order_relaxed) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    lds_set = true;
+    lds_set.fetch_or(bit, std::memory_order_relaxed);
   }
   kern<<<dim3((unsigned)tiles), kThreads, lds, stream>>>(reinterpret_cast<const uint32_t*>(packed),
                                                          gamma, xq, absmax, (int)t, (int)n,
