@@ -612,6 +612,9 @@ namespace {
 #ifndef BL_GEMV_FUSE_MAX_WORK
 #define BL_GEMV_FUSE_MAX_WORK (4 << 20)   // largest sum of blocks x K quantised in fused launches
 #endif
+#ifndef BL_GEMV_FUSE_MAX_WORK_T1
+#define BL_GEMV_FUSE_MAX_WORK_T1 (16 << 20)   // the same for one token
+#endif
 
 // Launch shape of the decode kernel for a group of `blocks` 16-row tiles
 // whose widest K is kmax: nw waves per block, each owning at most cpw
@@ -641,6 +644,14 @@ bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
   if ((k % 256) != 0 || t * k > BL_GEMV_DEC_XLDS) return false;
   if (raw_bytes == 0) return t <= 16;
   return t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
+}
+
+// Fused launches redo the token absmax in every block: worth it while that
+// redundant work costs less than a separate act-quant launch.  Measured on
+// 8192-wide rows: at one token fusing wins up to 1792 blocks (14.7M staged
+// elements; 16.4 against 18.5 us), at two tokens it loses there.
+bool fuse_work_ok(int64_t t, int64_t work) {
+  return work <= (t == 1 ? BL_GEMV_FUSE_MAX_WORK_T1 : BL_GEMV_FUSE_MAX_WORK);
 }
 
 size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes) {
@@ -711,7 +722,7 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
             (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
     work += (probs[i].N + 15) / 16 * probs[i].K;
   }
-  if (work > BL_GEMV_FUSE_MAX_WORK) fused = false;
+  if (!fuse_work_ok(t, work)) fused = false;
   if (!fused) {  // act-quant then forward (kernel chosen by T), problem by problem
     for (int i = 0; i < count; ++i) {
       const bl_linear& q = probs[i];
@@ -790,7 +801,7 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
   const int64_t blocks = (n + 15) / 16;
   // one launch for decode shapes (the same rule as a grouped call of one problem)
   if (dec_shape_ok(t, k, rb) && (reinterpret_cast<uintptr_t>(x) % 16) == 0 &&
-      (reinterpret_cast<uintptr_t>(packed) % 16) == 0 && blocks * k <= BL_GEMV_FUSE_MAX_WORK) {
+      (reinterpret_cast<uintptr_t>(packed) % 16) == 0 && fuse_work_ok(t, blocks * k)) {
     DecGroup grp = {};
     grp.T = (int)t;
     grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma_gate, x, nullptr,

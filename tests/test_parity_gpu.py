@@ -366,8 +366,12 @@ GROUPS = {
     "fallback_t300_gemm": (300, "bf16", [(512, 700), (1024, 300)]),
     # one token, K = 16384: 8 waves of 8 chunks each in the fused kernel
     "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(16384, 300)]),
-    # many row blocks: over the fused-work limit, act-quant runs separately
+    # many row blocks: fused at one token (8.4M staged elements, under 16M)
     "t1_bf16_many_blocks": (1, "bf16", [(8192, 8200), (8192, 8200)]),
+    # one token whose raw row does not fit the staging limit: act-quant runs separately
+    "t1_k28672_unfused": (1, "bf16", [(28672, 100)]),
+    # two tokens over the two-token work limit (4M): act-quant runs separately
+    "t2_bf16_many_blocks": (2, "bf16", [(8192, 8200)]),
 }
 
 
