@@ -318,10 +318,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   } else {
     const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
     const int nvec = T * K / (MODE == kBf16 ? 8 : 4);
-    for (int base = wave * 64; base < nvec; base += nthreads)
-      if (base + lane < nvec)
-        __builtin_amdgcn_global_load_lds((dec_glb_t)(xr + 16 * (base + lane)),
-                                         (dec_lds_t)(raw + 16 * base), 16, 0, 0);
+    // wave 0 fetches the whole raw rows, ahead of every weight load of the
+    // block: shared out over the waves, the last share would queue behind the
+    // other waves' weight loads, and the prologue waits for all of it
+    // (measured: the 2B decode layer 871 -> 923 GB/s)
+    if (wave == 0) {
+      for (int base = 0; base < nvec; base += 64)
+        if (base + lane < nvec)
+          __builtin_amdgcn_global_load_lds((dec_glb_t)(xr + 16 * (base + lane)),
+                                           (dec_lds_t)(raw + 16 * base), 16, 0, 0);
+    }
   }
   const float g = pr.gamma[0];
   float g2 = 0.0f;
@@ -357,8 +363,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   } else {
     // Step A1 in the block.  The absmax of each token (T <= 4) over all of
     // K, from every wave's share of the raw rows ...
-    wait_vmem<CPW>();                               // this wave's share landed
-    lds_sync();                                     // ... every wave's; header cleared
+    wait_vmem<CPW>();                               // wave 0: the raw rows landed
+    lds_sync();                                     // ... for every wave; header cleared
     constexpr int E = MODE == kBf16 ? 8 : 4;        // elements per 16 bytes
     const int per_tok = K / E, nvec = T * per_tok;
     const uint4* raw4 = reinterpret_cast<const uint4*>(raw);
