@@ -105,6 +105,19 @@ def _need_cuda(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_shape(t, name, shape):
+    """The library reads and writes exactly these extents: a tensor of another
+    shape would be read or written past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(name, *ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{name}: all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
 def gemv_max_tokens():
     return int(load().bitlinear_gemv_max_tokens())
 
@@ -113,6 +126,8 @@ def pack_weights(w):
     """Step A0 on the GPU: float32 W[N, K] -> (packed uint8[N, K/4], gamma float32[1])."""
     lib = load()
     _need_cuda(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
     n, k = w.shape
     packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
     gamma = torch.empty(1, dtype=torch.float32, device=w.device)
@@ -133,6 +148,8 @@ def quant_act(x, with_rowsum=True):
         dt = BL_BF16
     else:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, K]")
     t, k = x.shape
     xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
     absmax = torch.empty(t, dtype=torch.float32, device=x.device)
@@ -155,7 +172,11 @@ def subln_quant_act(x, gain, eps_n=1e-5, with_rowsum=True):
         dt = BL_BF16
     else:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, K]")
     t, k = x.shape
+    _need_shape(gain, "gain", (k,))
+    _same_device("subln_quant_act", x, gain)
     xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
     scale = torch.empty(t, dtype=torch.float32, device=x.device)
     rowsum = torch.empty(t, dtype=torch.int32, device=x.device) if with_rowsum else None
@@ -171,11 +192,23 @@ def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None,
     _need_cuda(gamma, "gamma", torch.float32)
     _need_cuda(xq, "xq", torch.int8)
     _need_cuda(absmax, "absmax", torch.float32)
+    if xq.dim() != 2:
+        raise ValueError("xq must be [T, K]")
     t, k = xq.shape
+    _need_shape(packed, "packed", (n, k // 4))
+    _need_shape(gamma, "gamma", (1,))
+    _need_shape(absmax, "absmax", (t,))
+    if out is not None:
+        _need_cuda(out, "out", torch.float32)
+        _need_shape(out, "out", (t, n))
     y = out if out is not None else torch.empty((t, n), dtype=torch.float32, device=xq.device)
     acc = acc_out
+    if acc is not None:
+        _need_cuda(acc, "acc_out", torch.int32)
+        _need_shape(acc, "acc_out", (t, n))
     if want_acc and acc is None:
         acc = torch.empty((t, n), dtype=torch.int32, device=xq.device)
+    _same_device("forward", packed, gamma, xq, absmax, y, acc)
     _check(lib.bitlinear_forward_algo(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
                                       _ptr(y), _ptr(acc), ALGOS[algo], _stream(xq.device)))
     return (y, acc) if want_acc else y
@@ -200,14 +233,21 @@ def linear_grouped(xs, weights, want_acc=False):
     dt = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}.get(xs[0].dtype)
     if dt is None:
         raise TypeError(f"x must be float32 or bfloat16, got {xs[0].dtype}")
+    if len(xs) > 8:
+        raise ValueError("at most 8 problems per call")
     t = xs[0].shape[0]
     outs, descs = [], (BlLinear * len(xs))()
     for i, (x, (packed, gamma)) in enumerate(zip(xs, weights)):
         _need_cuda(x, "x", xs[0].dtype)
         _need_cuda(packed, "packed", torch.uint8)
         _need_cuda(gamma, "gamma", torch.float32)
+        if x.dim() != 2 or x.shape[0] != t:
+            raise ValueError(f"problem {i}: x must be [T, K] with the same T as the others")
         k = x.shape[1]
         n = packed.shape[0]
+        _need_shape(packed, f"problem {i}: packed", (n, k // 4))
+        _need_shape(gamma, f"problem {i}: gamma", (1,))
+        _same_device("linear_grouped", xs[0], x, packed, gamma)
         y = torch.empty((t, n), dtype=torch.float32, device=x.device)
         xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
         absmax = torch.empty(t, dtype=torch.float32, device=x.device)
@@ -226,8 +266,9 @@ def interleave_rows(packed_a, packed_b):
     lib = load()
     _need_cuda(packed_a, "packed_a", torch.uint8)
     _need_cuda(packed_b, "packed_b", torch.uint8)
-    if packed_a.shape != packed_b.shape:
-        raise ValueError("the two packed matrices must have the same shape")
+    if packed_a.dim() != 2 or packed_a.shape != packed_b.shape:
+        raise ValueError("the two packed matrices must be [N, K/4] of the same shape")
+    _same_device("interleave_rows", packed_a, packed_b)
     n, k4 = packed_a.shape
     out = torch.empty((2 * n, k4), dtype=torch.uint8, device=packed_a.device)
     _check(lib.bitlinear_interleave_rows(_ptr(packed_a), _ptr(packed_b), n, 4 * k4, _ptr(out),
@@ -247,10 +288,15 @@ def gated_relu2(x, packed_gu, gamma_gate, gamma_up, want_acc=False):
     dt = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}.get(x.dtype)
     if dt is None:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2 or packed_gu.dim() != 2:
+        raise ValueError("x must be [T, K] and packed_gu [2N, K/4]")
     t, k = x.shape
     n2 = packed_gu.shape[0]
     if n2 % 2 or packed_gu.shape[1] * 4 != k:
         raise ValueError("packed_gu must be [2N, K/4]")
+    _need_shape(gamma_gate, "gamma_gate", (1,))
+    _need_shape(gamma_up, "gamma_up", (1,))
+    _same_device("gated_relu2", x, packed_gu, gamma_gate, gamma_up)
     n = n2 // 2
     h = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
     xq = torch.empty((t, k), dtype=torch.int8, device=x.device)
@@ -267,6 +313,8 @@ def pack_weights_binary(w):
     [N, K/8], gamma float32[1]); K a multiple of 256, at most 32768."""
     lib = load()
     _need_cuda(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
     n, k = w.shape
     packed = torch.empty((n, k // 8), dtype=torch.uint8, device=w.device)
     gamma = torch.empty(1, dtype=torch.float32, device=w.device)
@@ -284,10 +332,15 @@ def forward_binary(packed, gamma, xq, absmax, algo="auto", want_acc=False):
     _need_cuda(gamma, "gamma", torch.float32)
     _need_cuda(xq, "xq", torch.int8)
     _need_cuda(absmax, "absmax", torch.float32)
+    if xq.dim() != 2 or packed.dim() != 2:
+        raise ValueError("xq must be [T, K] and packed [N, K/8]")
     t, k = xq.shape
     n = packed.shape[0]
     if packed.shape[1] * 8 != k:
         raise ValueError("packed must be [N, K/8]")
+    _need_shape(gamma, "gamma", (1,))
+    _need_shape(absmax, "absmax", (t,))
+    _same_device("forward_binary", packed, gamma, xq, absmax)
     y = torch.empty((t, n), dtype=torch.float32, device=xq.device)
     acc = torch.empty((t, n), dtype=torch.int32, device=xq.device) if want_acc else None
     _check(lib.bitlinear_forward_binary(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
