@@ -18,9 +18,11 @@ is reported beside it.
 
 The JSON line reports algorithmic GB/s of the whole step (value), the decode
 kernel against the HBM roofline, the CPU oracle timed on a bounded sample,
-and, as extra context: the prefill GEMM (T = 2048) in int8 TOP/s, the batched
-decode crossover between the decode kernel and the tiled MFMA kernel, and the
-70B-class shapes at T = 1 (GB/s) and T = 256 (TOP/s).
+and, as extra context: the device's measured ceilings (launch floor, HBM read
+stream, int8 matrix-core loop), the spread of the step time, the prefill GEMM
+(T = 2048) in int8 TOP/s, the batched decode crossover between the decode
+kernel and the tiled MFMA kernel, and the 70B-class shapes at T = 1 (GB/s)
+and T = 256 (TOP/s).
 """
 
 import argparse
@@ -54,8 +56,8 @@ def parse():
                         "five times each (eager), then a 256 MiB device copy, and exit: the "
                         "program that the prefill rocprofv3 summaries profile")
     p.add_argument("--extra", default="all",
-                   help="context runs to do: 'all' or a comma list of prefill, crossover, 70b, "
-                        "subln, gated, lut, binary")
+                   help="context runs to do: 'all' or a comma list of calib, prefill, crossover, "
+                        "70b, subln, gated, lut, binary")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--fused-only", action="store_true",
@@ -182,6 +184,59 @@ def time_graph(torch, g, reps, warm, stream):
     end.synchronize()
     torch.cuda.synchronize()
     return start.elapsed_time(end)  # ms
+
+
+def calibration(torch, binding, dev, stream):
+    """The device's own ceilings, measured with the library's helper kernels:
+    the launch floor (an empty kernel per graph node), the HBM read stream
+    (one 70B-class packed matrix per launch over 20 rotated buffers, as the
+    decode kernels stream their weights, and one 1 GiB buffer, both read at
+    full width) and the
+    int8 matrix-core rate (back-to-back v_mfma_i32_32x32x32_i8 on registers,
+    four waves per SIMD)."""
+    lib = binding.load()
+    h = lambda s: ctypes.c_void_p(s.cuda_stream)
+
+    def ok(rc):
+        if rc:
+            raise RuntimeError(lib.bitlinear_last_error().decode())
+
+    out = {}
+    n = 256
+    g = capture(torch, lambda s: [ok(lib.bitlinear_calib_empty(h(s))) for _ in range(n)], stream)
+    out["empty_kernel_launch_us"] = round(time_graph(torch, g, 8, 2, stream) * 1e3 / (8 * n), 3)
+    sink = torch.empty(lib.bitlinear_calib_sink_len(), dtype=torch.int32, device=dev)
+    # reads of one 70B-class packed matrix (58.7 MB), rotated over 20 buffers
+    # (> 1 GB, four times the MALL) as the decode kernels' weights are, and
+    # one read of 1 GiB.  The rate depends on the buffer size on this device
+    # (64 MiB buffers read about 20% slower than 56 MiB ones), so the ceiling
+    # is taken at the size the decode kernels stream.
+    for nbytes, copies, key in ((58720256, 20, "hbm_read_stream_70b_matrix_rotated"),
+                                (1 << 30, 1, "hbm_read_stream_1gib")):
+        bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        us = rotated_time_us(
+            torch, lambda s, i: ok(lib.bitlinear_calib_read(ptr(bufs[i]), nbytes, ptr(sink), h(s))),
+            copies, stream, reps=max(2, 20 // copies))
+        out[key + "_gb_s"] = round(nbytes / us / 1e3, 1)
+        out[key + "_frac_of_peak"] = round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)
+        del bufs
+    iters = 1024
+    g = capture(torch, lambda s: ok(lib.bitlinear_calib_mfma(iters, 1, ptr(sink), h(s))), stream)
+    us = time_graph(torch, g, 10, 2, stream) * 1e3 / 10
+    ops = 2.0 * 4 * iters * 4096 * 32768
+    out["int8_mfma_loop_tops"] = round(ops / us / 1e6, 1)
+    out["int8_mfma_loop_frac_of_peak"] = round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_graph_chunks(torch, g, reps, chunks, stream):
+    """Milliseconds per replay in each of `chunks` consecutive timed runs."""
+    per = max(1, reps // chunks)
+    out = []
+    for _ in range(chunks):
+        out.append(time_graph(torch, g, per, 0, stream) / per)
+    return out
 
 
 def cpu_baseline(oracle, wl, budget_s=12.0):
@@ -705,12 +760,21 @@ def main():
                 "avg_launch_us": round(fused_us, 3),
                 "algorithmic_bytes_per_launch": int(fused_launch_bytes)}
 
+    if not args.fused_only:
+        # spread of the step time: the same graph in 16 shorter timed runs
+        chunk_ms = time_graph_chunks(torch, g_fused, reps, 16, stream)
+        q = np.percentile(np.array(chunk_ms) / n_sets, [10, 50, 90])
+        extra["ms_per_step_p10_p50_p90"] = [round(float(v), 5) for v in q]
     extra.update({"layer_sets_rotated": n_sets,
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     want = set(args.extra.split(",")) if args.extra != "all" else {
-        "prefill", "crossover", "70b", "subln", "gated", "lut", "binary"}
+        "calib", "prefill", "crossover", "70b", "subln", "gated", "lut", "binary"}
     if not args.no_extra:
+        if "calib" in want:
+            extra["device_ceilings"] = calibration(torch, binding, dev, stream)
+            roofline["measured_read_stream_gb_s"] = \
+                extra["device_ceilings"]["hbm_read_stream_70b_matrix_rotated_gb_s"]
         if "prefill" in want:
             extra["prefill_t2048"] = prefill_extra(torch, binding, wl, dev, stream)
         if "crossover" in want:
@@ -725,6 +789,19 @@ def main():
             extra["binary_weights"] = binary_extra(torch, binding, dev, stream)
         if "lut" in want:
             extra["lut_decode_comparison"] = lut_extra(torch, binding, mats, sets, dev, stream, calls)
+
+    # the same figures against the device's measured ceilings
+    ceil = extra.get("device_ceilings")
+    if ceil:
+        stream_gbs = ceil["hbm_read_stream_70b_matrix_rotated_gb_s"]
+        mfma_tops = ceil["int8_mfma_loop_tops"]
+        for rec_ in extra.get("70b_class", {}).values():
+            rec_["t1_forward_frac_of_measured_read_stream"] = round(
+                rec_["t1_forward_gb_s"] / stream_gbs, 4)
+            rec_["t256_forward_frac_of_measured_mfma_loop"] = round(
+                rec_["t256_forward_tops"] / mfma_tops, 4)
+        for rec_ in extra.get("prefill_t2048", {}).values():
+            rec_["gemm_frac_of_measured_mfma_loop"] = round(rec_["gemm_tops"] / mfma_tops, 4)
 
     cpu = None
     if not args.no_cpu:

@@ -54,6 +54,10 @@ SIGNATURES["bitlinear_gated_relu2"] = (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_
                                                 _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp])
 SIGNATURES["bitlinear_linear_grouped"] = (_c_int, [ctypes.POINTER(BlLinear), _c_int, _c_i64,
                                                    _c_int, _c_vp])
+SIGNATURES["bitlinear_calib_sink_len"] = (_c_i64, [])
+SIGNATURES["bitlinear_calib_empty"] = (_c_int, [_c_vp])
+SIGNATURES["bitlinear_calib_read"] = (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp])
+SIGNATURES["bitlinear_calib_mfma"] = (_c_int, [_c_i64, _c_int, _c_vp, _c_vp])
 
 
 class BitLinearError(RuntimeError):
@@ -346,3 +350,38 @@ def forward_binary(packed, gamma, xq, absmax, algo="auto", want_acc=False):
     _check(lib.bitlinear_forward_binary(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
                                         _ptr(y), _ptr(acc), ALGOS[algo], _stream(xq.device)))
     return (y, acc) if want_acc else y
+
+
+def calib_empty(device=None):
+    """One empty kernel on the current stream of `device` (the launch floor)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    _check(load().bitlinear_calib_empty(_stream(dev)))
+
+
+def calib_read(buf, sink=None):
+    """Read the whole of `buf` (a contiguous CUDA tensor, 16-byte aligned, size a
+    multiple of 16 bytes) at full width; returns the int32 sink whose first 2048
+    entries XOR to the XOR of the buffer's 32-bit words."""
+    lib = load()
+    _need_cuda(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(lib.bitlinear_calib_sink_len(), dtype=torch.int32, device=buf.device)
+    _need_cuda(sink, "sink", torch.int32)
+    _need_shape(sink, "sink", (lib.bitlinear_calib_sink_len(),))
+    _check(lib.bitlinear_calib_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
+    return sink
+
+
+def calib_mfma(iters, byte=1, device=None, sink=None):
+    """4096 waves x iters rounds of four v_mfma_i32_32x32x32_i8 (4 * iters *
+    4096 * 32768 int8 multiply-adds); returns the int32 sink, each of whose
+    first 4096 entries is 4 * iters * 32 * byte^2 (mod 2^32)."""
+    lib = load()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    if sink is None:
+        sink = torch.empty(lib.bitlinear_calib_sink_len(), dtype=torch.int32, device=dev)
+    _need_cuda(sink, "sink", torch.int32)
+    _need_shape(sink, "sink", (lib.bitlinear_calib_sink_len(),))
+    _check(lib.bitlinear_calib_mfma(int(iters), int(byte), _ptr(sink), _stream(sink.device)))
+    return sink

@@ -243,4 +243,32 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* x
   return bitlinear_forward_algo(packed, gamma, xq, absmax, T, N, K, y, acc, BL_ALGO_AUTO, stream);
 }
 
+int64_t bitlinear_calib_sink_len(void) { return bl::kCalibSinkLen; }
+
+int bitlinear_calib_empty(void* stream) {
+  return launched("bitlinear_calib_empty", bl::launch_calib_empty(static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  const char* fn = "bitlinear_calib_read";
+  if (!buf || !sink) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40))
+    return fail(BL_ERR_SHAPE, "%s: bytes=%lld must be a positive multiple of 16, at most 2^40", fn,
+                (long long)bytes);
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(BL_ERR_ALIGN, "%s: buf needs 16-byte, sink 4-byte alignment", fn);
+  return launched(fn, bl::launch_calib_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream) {
+  const char* fn = "bitlinear_calib_mfma";
+  if (!sink) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (iters < 1 || iters > (int64_t(1) << 20) || byte < -128 || byte > 127)
+    return fail(BL_ERR_ARG, "%s: iters=%lld must be in [1, 2^20] and byte=%d in [-128, 127]", fn,
+                (long long)iters, byte);
+  if (!aligned(sink, 4)) return fail(BL_ERR_ALIGN, "%s: sink needs 4-byte alignment", fn);
+  return launched(fn, bl::launch_calib_mfma((int)iters, byte, sink,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -20,6 +20,16 @@ constexpr float kQb = 127.0f;
 // T = 64 (faster on one, slower on the other) and twice as slow at T = 128.
 constexpr int64_t kGemvMaxTokens = 64;
 
+// Measurement helpers (calib.hip): the launch floor, the HBM read stream and
+// the int8 matrix-core rate of the device; the read writes kCalibReadBlocks
+// sink entries, the MFMA loop kCalibMfmaWaves.
+constexpr int kCalibReadBlocks = 2048;
+constexpr int kCalibMfmaWaves = 4096;
+constexpr int64_t kCalibSinkLen = 4096;
+hipError_t launch_calib_empty(hipStream_t stream);
+hipError_t launch_calib_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_calib_mfma(int iters, int byte, int32_t* sink, hipStream_t stream);
+
 // Exponent buckets of the exact gamma sum: one uint64 per binary32 exponent.
 constexpr int kGammaBuckets = 256;
 constexpr size_t kPackWorkspaceBytes = kGammaBuckets * sizeof(unsigned long long);

@@ -302,6 +302,36 @@ int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
                           int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
                           void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement helpers.  Not part of the forward: they measure, on the device
+ * at hand, the ceilings that the forward's kernels are judged against (the
+ * launch floor, the HBM read stream, the int8 matrix-core rate).  Errors as
+ * for every call above; they touch no memory but their own arguments.
+ * ------------------------------------------------------------------------ */
+
+/* Entries (uint32 or int32) that the sink of the two calls below must hold. */
+int64_t bitlinear_calib_sink_len(void);
+
+/* One empty kernel on `stream`: the cost of a launch with no work. */
+int bitlinear_calib_empty(void* stream);
+
+/* Reads the `bytes` bytes at `buf` (device, 16-byte aligned; `bytes` a
+ * positive multiple of 16, at most 2^40) once, with 16-byte loads over a
+ * grid that fills the device.  sink[i] for i < 2048 receives the XOR of the
+ * 32-bit words that block i read, so the XOR of those 2048 entries is the
+ * XOR of the whole buffer; the rest of the sink is not written.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (bytes), BL_ERR_ALIGN. */
+int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* 4096 waves (four per SIMD on 256 CUs) each issue `iters` rounds of four
+ * independent v_mfma_i32_32x32x32_i8 with every element of A and B equal to
+ * the int8 value `byte`: 4 * iters * 4096 * 32768 int8 multiply-adds in
+ * all (count two operations each for a TOP/s figure).  sink[w] for w < 4096
+ * receives 4 * iters * 32 * byte^2 modulo 2^32 (as int32).
+ * Errors: BL_ERR_NULL, BL_ERR_ARG (iters outside [1, 2^20], byte outside
+ * [-128, 127]). */
+int bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

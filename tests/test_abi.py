@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
 
@@ -222,6 +222,27 @@ def test_binary_errors(lib):
     assert g(*ok[:9], 4, None) == BL_ERR_ARG                        # nor a v_dot4 one
     assert g(*ok[:9], 9, None) == BL_ERR_ARG
     assert "binary" in (g(*ok[:9], 3, None) and _err(lib))
+
+
+def test_calib_errors(lib):
+    """The measurement helpers check their arguments like every other call."""
+    assert lib.bitlinear_calib_sink_len() == 4096
+    r = lib.bitlinear_calib_read
+    assert r(None, 1024, A16, None) == BL_ERR_NULL
+    assert r(A16, 1024, None, None) == BL_ERR_NULL
+    assert r(A16, 0, A16, None) == BL_ERR_SHAPE
+    assert r(A16, 1000, A16, None) == BL_ERR_SHAPE                  # not a multiple of 16
+    assert r(A16, (1 << 40) + 16, A16, None) == BL_ERR_SHAPE
+    assert r(A16 + 8, 1024, A16, None) == BL_ERR_ALIGN
+    assert r(A16, 1024, A_ODD, None) == BL_ERR_ALIGN
+    m = lib.bitlinear_calib_mfma
+    assert m(16, 1, None, None) == BL_ERR_NULL
+    assert m(0, 1, A16, None) == BL_ERR_ARG
+    assert m((1 << 20) + 1, 1, A16, None) == BL_ERR_ARG
+    assert m(16, 128, A16, None) == BL_ERR_ARG
+    assert m(16, -129, A16, None) == BL_ERR_ARG
+    assert m(16, 1, A_ODD, None) == BL_ERR_ALIGN
+    assert "iters" in (m(0, 1, A16, None) and _err(lib))
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
