@@ -631,3 +631,122 @@ def test_graph_replays_match_eager(bl):
         for i, (a, b) in enumerate(zip(got, eager)):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {rep}, output {i}"
         del junk
+
+
+# ------------------------------------------------------------------ seeded random sweep
+#
+# Shapes drawn from a fixed seed (the ids name each one): every entry point,
+# every kernel choice, on sizes no hand-picked list above holds.  The same
+# element-by-element bar as the cases above.
+
+def _draw(seed, count, fn):
+    rng = np.random.default_rng(seed)
+    return [fn(rng) for _ in range(count)]
+
+
+_T_CHOICES = [1, 1, 1, 2, 3, 4, 5, 8, 13, 16, 17, 31, 64, 65, 100, 257]
+
+SWEEP_FWD = _draw(9101, 20, lambda r: (int(r.choice(_T_CHOICES)), int(r.integers(1, 1200)),
+                                       16 * int(r.integers(1, 385))))
+
+
+@pytest.mark.parametrize("t,n,k", SWEEP_FWD, ids=[f"T{t}_N{n}_K{k}" for t, n, k in SWEEP_FWD])
+def test_sweep_forward(bl, t, n, k):
+    tern, q, absmax, gamma = _forward_inputs(t, n, k, 9200 + t + n + k)
+    args = (dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q), dev(absmax))
+    for algo in ("auto", "gemv", "gemm", "lut", "dot4"):
+        check_forward(bl, *args, tern, q, gamma, absmax, algo)
+
+
+def _group(r):
+    t = int(r.choice([1, 1, 2, 3, 4, 5, 9, 70]))
+    count = int(r.integers(1, 9))
+    dtype = "bf16" if r.random() < 0.7 else "f32"
+    shapes = []
+    for _ in range(count):
+        k = 256 * int(r.integers(1, 25)) if r.random() < 0.8 else 16 * int(r.integers(1, 200))
+        shapes.append((k, int(r.integers(1, 900))))
+    return t, dtype, shapes
+
+
+SWEEP_GROUPS = _draw(9102, 10, _group)
+
+
+@pytest.mark.parametrize("t,dtype,shapes", SWEEP_GROUPS,
+                         ids=[f"T{t}_{d}_" + "_".join(f"{k}x{n}" for k, n in s)
+                              for t, d, s in SWEEP_GROUPS])
+def test_sweep_grouped(bl, t, dtype, shapes):
+    xs, ws, refs = [], [], []
+    for i, (k, n) in enumerate(shapes):
+        tern, _, _, gamma = _forward_inputs(1, n, k, 9300 + 7 * i + k + n, zero_rows=True)
+        x = wl.activations_student_t(t, k, 4, 9400 + 7 * i + k)
+        if t > 2:
+            x[t - 1] = 0.0                                   # an all-zero token
+        if dtype == "bf16":
+            bits = wl.bf16_bits(x)
+            xs.append(dev_bf16(bits))
+            q_ref, a_ref, _ = oracle.quant_act(bits)
+        else:
+            xs.append(dev(x))
+            q_ref, a_ref, _ = oracle.quant_act(x)
+        ws.append((dev(oracle.pack_ternary(tern)), dev(np.array([gamma]))))
+        refs.append((tern, q_ref, a_ref, gamma))
+    outs = bl.linear_grouped(xs, ws, want_acc=True)
+    for (y, xq, absmax, acc), (tern, q_ref, a_ref, gamma) in zip(outs, refs):
+        assert np.array_equal(host(xq), q_ref)
+        assert np.array_equal(host(absmax).view(np.uint32), a_ref.view(np.uint32))
+        acc_ref = oracle.contract(q_ref, tern)
+        assert int(np.count_nonzero(host(acc) != acc_ref)) == 0
+        check_y(host(y), acc_ref, gamma, a_ref)
+
+
+SWEEP_GATED = _draw(9103, 8, lambda r: (int(r.choice([1, 1, 2, 3, 4, 7, 16, 33, 150])),
+                                        int(r.integers(1, 700)),
+                                        (256 if r.random() < 0.7 else 16) * int(r.integers(1, 17)),
+                                        "bf16" if r.random() < 0.6 else "f32"))
+
+
+@pytest.mark.parametrize("t,n,k,dtype", SWEEP_GATED,
+                         ids=[f"T{t}_N{n}_K{k}_{d}" for t, n, k, d in SWEEP_GATED])
+def test_sweep_gated(bl, t, n, k, dtype):
+    pgu, gg, gu, xin, xref, tg, tu, gg_ref, gu_ref = _gated_inputs(bl, t, n, k, dtype, 9500 + t + n + k)
+    h, xq, absmax, acc = bl.gated_relu2(xin, pgu, gg, gu, want_acc=True)
+    _check_gated(_bits(h), host(xq), host(absmax), host(acc), xref, tg, tu, gg_ref, gu_ref)
+
+
+SWEEP_BIN = _draw(9104, 8, lambda r: (int(r.choice(_T_CHOICES)), int(r.integers(1, 1200)),
+                                      256 * int(r.integers(1, 33)),
+                                      str(r.choice(["auto", "gemv", "gemm"]))))
+
+
+@pytest.mark.parametrize("t,n,k,algo", SWEEP_BIN, ids=[f"T{t}_N{n}_K{k}_{a}" for t, n, k, a in SWEEP_BIN])
+def test_sweep_binary(bl, t, n, k, algo):
+    w = wl.latent_weights(n, k, 0.02, 9600 + t + n + k)
+    x = wl.activations_student_t(t, k, 4, 9700 + t + k)
+    packed_ref, gamma_ref = oracle.pack_weights_binary(w)
+    packed, gamma = bl.pack_weights_binary(dev(w))
+    assert np.array_equal(host(packed), packed_ref)
+    assert host(gamma).view(np.uint32)[0] == np.float32(gamma_ref).view(np.uint32)
+    q_ref, a_ref, _ = oracle.quant_act(x)
+    y, acc = bl.forward_binary(packed, gamma, dev(q_ref), dev(a_ref), algo=algo, want_acc=True)
+    acc_ref = oracle.contract(q_ref, oracle.binarize(w))
+    assert int(np.count_nonzero(host(acc) != acc_ref)) == 0
+    check_y(host(y), acc_ref, gamma_ref, a_ref)
+
+
+SWEEP_SUBLN = _draw(9105, 6, lambda r: (int(r.choice([1, 2, 5, 64, 300])), 16 * int(r.integers(1, 1025)),
+                                        "bf16" if r.random() < 0.6 else "f32"))
+
+
+@pytest.mark.parametrize("t,k,dtype", SWEEP_SUBLN, ids=[f"T{t}_K{k}_{d}" for t, k, d in SWEEP_SUBLN])
+def test_sweep_subln(bl, t, k, dtype):
+    xref, xin, g = _subln_inputs(t, k, dtype, 9800 + t + k)
+    q_ref, scale_ref, rs_ref, a_ref = oracle.subln_quant_act(xref, g)
+    xq, scale, rowsum = bl.subln_quant_act(xin, dev(g))
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(rowsum), rs_ref)
+    sc = host(scale).astype(np.float64)
+    zero = a_ref == 0
+    assert np.all(sc[zero] == 0.0)
+    rel = np.abs(sc[~zero] - scale_ref[~zero]) / scale_ref[~zero]
+    assert rel.size == 0 or float(rel.max()) <= 2.5e-7, f"scale off by {rel.max():.3g}"
