@@ -318,10 +318,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   } else {
     const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
     const int nvec = T * K / (MODE == kBf16 ? 8 : 4);
-    // wave 0 fetches the whole raw rows, ahead of every weight load of the
-    // block: shared out over the waves, the last share would queue behind the
-    // other waves' weight loads, and the prologue waits for all of it
-    // (measured: the 2B decode layer 871 -> 923 GB/s)
+    // wave 0 fetches the whole raw rows (the barrier below puts them ahead
+    // of every weight load of the block): shared out over the waves, the
+    // fetch takes more instructions and the prologue still waits for all of
+    // it (measured: the 2B decode layer 871 -> 923 GB/s before the barrier)
     if (wave == 0) {
       for (int base = 0; base < nvec; base += 64)
         if (base + lane < nvec)
@@ -332,6 +332,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   const float g = pr.gamma[0];
   float g2 = 0.0f;
   if constexpr (GATED) g2 = pr.gamma2[0];
+  // A block barrier here, before any weight load, puts every activation
+  // load of the block ahead of every weight load of the block in the CU's
+  // memory queue, whose loads come back roughly in issue order: the
+  // activations, needed first, are no longer stuck behind other waves'
+  // weights (measured: the 2B decode layer 920 -> 1005 GB/s, 28672 -> 8192 at
+  // one int8 token 15.5 -> 14.4 us).  A wave reaches it as soon as its
+  // activation loads are issued; after the weight loads it would wait until
+  // all of those are issued, which stalls while the CU's queue is full.  The
+  // same barrier orders the header clearing before the tile adds.
+  for (int i = threadIdx.x; i < 16 + 256 + 1 + 16; i += nthreads) zero[i] = 0;
+  lds_sync();
   // ... and last every weight chunk of this wave; slots past cnt repeat the
   // row's last chunk and meet a zero B operand below.
   uint4 buf[CPW];
@@ -341,11 +352,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     buf[i] = wrow[(size_t)c * 4];
   }
 
-  for (int i = threadIdx.x; i < 16 + 256 + 1 + 16; i += nthreads) zero[i] = 0;
   int qsum = 0;     // sum of q over this wave's k run, token of lane l: l & 15
   float a_t = am;   // absmax of the token whose outputs lane l writes (l >> 4)
   if constexpr (MODE == kInt8) {
-    lds_sync();                                     // header cleared (the waves arrive together)
     wait_vmem<CPW>();                               // this wave's activation run landed
     for (int t = 0; t < T; ++t) {
       const uint4* xt = reinterpret_cast<const uint4*>(xs8 + t * tstride + run0);
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     // Step A1 in the block.  The absmax of each token (T <= 4) over all of
     // K, from every wave's share of the raw rows ...
     wait_vmem<CPW>();                               // wave 0: the raw rows landed
-    lds_sync();                                     // ... for every wave; header cleared
+    lds_sync();                                     // ... for every wave
     constexpr int E = MODE == kBf16 ? 8 : 4;        // elements per 16 bytes
     const int per_tok = K / E, nvec = T * per_tok;
     const uint4* raw4 = reinterpret_cast<const uint4*>(raw);
