@@ -610,10 +610,13 @@ void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
 namespace {
 
 #ifndef BL_GEMV_DEC_RESIDENT
-#define BL_GEMV_DEC_RESIDENT 8192   // waves resident at once (8 per SIMD, 1024 SIMDs)
+#define BL_GEMV_DEC_RESIDENT 16384  // most waves per launch (two rounds of 8 per SIMD on 1024 SIMDs)
 #endif
 #ifndef BL_GEMV_DEC_MAXW
-#define BL_GEMV_DEC_MAXW 8          // waves per block, unless K needs more (8 chunks each)
+#define BL_GEMV_DEC_MAXW 8          // waves per block, unless K needs more (8 chunks each) ...
+#endif
+#ifndef BL_GEMV_DEC_MAXW_SHORT
+#define BL_GEMV_DEC_MAXW_SHORT 16   // ... or this many give every wave BL_GEMV_DEC_CPW chunks
 #endif
 #ifndef BL_GEMV_DEC_CPW
 #define BL_GEMV_DEC_CPW 2           // chunks per wave aimed for
@@ -635,21 +638,29 @@ namespace {
 // whose widest K is kmax: nw waves per block, each owning at most cpw
 // (a template size: 2, 4 or 8) consecutive 256-k chunks.  A block's time is
 // mostly latency plus the work its waves do one after another on the SIMDs,
-// so: about BL_GEMV_DEC_CPW chunks per wave, at most BL_GEMV_DEC_MAXW waves
-// per block and no more waves than fit on the chip at once, but never more
-// than 8 chunks per wave (K <= 32768, 128 chunks, keeps nw <= 16).
+// so: about BL_GEMV_DEC_CPW chunks per wave (up to BL_GEMV_DEC_MAXW_SHORT
+// waves per block when that is enough, else at most BL_GEMV_DEC_MAXW), no
+// more than BL_GEMV_DEC_RESIDENT waves in all, never more than 8 chunks per
+// wave (K <= 32768, 128 chunks, keeps nw <= 16) and no wave without chunks.
+// Measured on the 2B layer and the 70B shapes after the block barrier moved
+// ahead of the weight loads: 14 waves of 2 chunks for K = 6912 (+0.6% on the
+// layer against 8 of 4); 8 of 4 for K = 8192 at 1792 blocks (the fused
+// launch 16.8 -> 15.8 us against 4 of 8); 14 of 8 for K = 28672 (16 of 7:
+// 15.1 against 14.5 us).
 struct DecShape {
   int nw, cpw;
 };
 DecShape dec_shape(int64_t blocks, int64_t kmax) {
   const int nchunks = (int)(kmax / 256);
   int nw = (nchunks + BL_GEMV_DEC_CPW - 1) / BL_GEMV_DEC_CPW;
-  if (nw > BL_GEMV_DEC_MAXW) nw = BL_GEMV_DEC_MAXW;
+  const int maxw = nw <= BL_GEMV_DEC_MAXW_SHORT ? BL_GEMV_DEC_MAXW_SHORT : BL_GEMV_DEC_MAXW;
+  if (nw > maxw) nw = maxw;
   const int64_t fit = BL_GEMV_DEC_RESIDENT / blocks;
   if (nw > fit) nw = (int)(fit > 1 ? fit : 1);
   const int least = (nchunks + 7) / 8;
   if (nw < least) nw = least;
   const int per = (nchunks + nw - 1) / nw;
+  nw = (nchunks + per - 1) / per;   // the same chunks per wave, no wave left without
   return DecShape{nw, per <= 2 ? 2 : per <= 4 ? 4 : 8};
 }
 
