@@ -204,8 +204,11 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
 // A decode launch moves a few MB, so its time is mostly latency:
 //  - a block's problem is blockIdx.y, known before the first load, and all
 //    arguments arrive in one batch;
-//  - the activations go from global memory straight into LDS (no registers
-//    held while the weights are in flight), issued before the weights;
+//  - the activations are issued first and a block barrier follows before
+//    any weight load, so all of a block's activation loads reach memory
+//    ahead of all its weight loads (int8 input: global -> LDS directly;
+//    one raw token: into registers, four values per lane per chunk; more
+//    raw tokens: wave 0 stages the rows in LDS);
 //  - wave w owns a contiguous run of at most CPW chunks of its 16 rows and
 //    issues all of their loads at once: one memory round trip per wave;
 //  - the block barriers wait for LDS traffic only, so the weight loads stay
@@ -307,6 +310,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   // the wave's base + 16 l): int8 input, this wave's own k run; raw input
   // (step A1 fused), the whole rows, shared by the block ...
   const int run0 = c0 * 256, runb = cnt > 0 ? cnt * 256 : 0;   // this wave's k run
+  uint4 xraw[ONE && MODE != kInt8 ? CPW : 1];                  // one-token raw units
   if constexpr (MODE == kInt8) {
     const int8_t* x8 = static_cast<const int8_t*>(pr.x);
     for (int t = 0; t < T; ++t)
@@ -315,6 +319,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
           __builtin_amdgcn_global_load_lds(
               (dec_glb_t)(x8 + (int64_t)t * K + run0 + base + 16 * lane),
               (dec_lds_t)(xs8 + t * tstride + run0 + base), 16, 0, 0);
+  } else if constexpr (ONE) {
+    // one token: each lane loads, into registers, the four raw activations
+    // it will quantise in each chunk of this wave's run (elements 4l .. 4l+3
+    // of the chunk); slots past cnt repeat the row's last chunk and feed
+    // only the absmax, where a repeat changes nothing
+    const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int k0 = min(c0 + u, nchunks - 1) * 256 + 4 * lane;
+      if constexpr (MODE == kBf16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
+        xraw[u] = make_uint4(v.x, v.y, 0u, 0u);
+      } else {
+        xraw[u] = *reinterpret_cast<const uint4*>(xr + 4 * k0);
+      }
+    }
   } else {
     const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
     const int nvec = T * K / (MODE == kBf16 ? 8 : 4);
@@ -369,6 +389,63 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
       const int sum = wave_sum_i(part);
       if (r == t) qsum = sum;
     }
+  } else if constexpr (ONE) {
+    // Step A1 in the block, one token, from registers: the absmax over this
+    // wave's run (its repeats included), then over the block through LDS ...
+    wait_vmem<CPW>();                               // this lane's raw activations landed
+    uint32_t mx = 0;                                // magnitude bit patterns
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const uint4 v = xraw[u];
+      if constexpr (MODE == kBf16) {
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        const uint32_t m = 0x7fff7fffu;
+        const us2 h = __builtin_elementwise_max(__builtin_bit_cast(us2, v.x & m),
+                                                __builtin_bit_cast(us2, v.y & m));
+        mx = max(mx, (uint32_t)max(h.x, h.y) << 16);
+      } else {
+        mx = max(mx, max(max(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
+                         max(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
+      }
+    }
+    const int wm = wave_max_nonneg((int)mx);        // non-negative patterns order as values
+    if (lane == 0) atomicMax(&amax[0], wm);
+    lds_sync();
+    // ... then scale, round half to even and clip this lane's units into the
+    // int8 row (read back only by this wave: no barrier), summing q.  Block 0
+    // of the problem also stores the int8 activations and the absmax.
+    const float a = __uint_as_float((uint32_t)amax[0]);
+    const float s = kQb / fmaxf(a, kEps);
+    a_t = a;
+    const bool first = blockIdx.x == 0;
+    int tsum = 0;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      if (u >= cnt) break;                          // wave-uniform
+      const int k0 = run0 + u * 256 + 4 * lane;
+      const uint4 v = xraw[u];
+      float f[4];
+      if constexpr (MODE == kBf16) {
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+      } else {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+      }
+      int q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        q[e] = (int)fminf(fmaxf(rintf(f[e] * s), -kQb), kQb);   // one binary32 product
+      const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x04000c0cu);
+      const uint32_t word = lo | hi;
+      tsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, tsum, false);
+      *reinterpret_cast<uint32_t*>(xs8 + k0) = word;
+      if (first && pr.xq_out) *reinterpret_cast<uint32_t*>(pr.xq_out + k0) = word;
+    }
+    const int sum = wave_sum_i(tsum);
+    if (r == 0) qsum = sum;
+    if (first && wave == 0 && pr.absmax_out && lane == 0) pr.absmax_out[0] = a;
   } else {
     // Step A1 in the block.  The absmax of each token (T <= 4) over all of
     // K, from every wave's share of the raw rows ...
@@ -665,11 +742,12 @@ DecShape dec_shape(int64_t blocks, int64_t kmax) {
 }
 
 // Shapes the decode kernel takes: raw_bytes is 0 for int8 activations, else
-// the size of one raw activation (step A1 fused, at most 4 tokens).
+// the size of one raw activation (step A1 fused, at most 4 tokens; one token
+// keeps its raw activations in registers, more are staged in LDS).
 bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
   if ((k % 256) != 0 || t * k > BL_GEMV_DEC_XLDS) return false;
   if (raw_bytes == 0) return t <= 16;
-  return t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
+  return t == 1 || (t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS);
 }
 
 // Fused launches redo the token absmax in every block: worth it while that
@@ -681,7 +759,8 @@ bool fuse_work_ok(int64_t t, int64_t work) {
 }
 
 size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes) {
-  return kDecHead + (size_t)t * (kmax + 16) + (size_t)t * kmax * raw_bytes;
+  const size_t staged = t == 1 ? 0 : (size_t)t * kmax * raw_bytes;   // raw rows, T > 1
+  return kDecHead + (size_t)t * (kmax + 16) + staged;
 }
 
 template <int MODE, bool ONE, bool GATED>

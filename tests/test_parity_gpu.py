@@ -368,8 +368,10 @@ GROUPS = {
     "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(16384, 300)]),
     # many row blocks: fused at one token (8.4M staged elements, under 16M)
     "t1_bf16_many_blocks": (1, "bf16", [(8192, 8200), (8192, 8200)]),
-    # one token whose raw row does not fit the staging limit: act-quant runs separately
-    "t1_k28672_unfused": (1, "bf16", [(28672, 100)]),
+    # one token, K = 28672: fused, the raw row held in registers (14 waves of 8 chunks)
+    "t1_k28672_fused": (1, "bf16", [(28672, 100)]),
+    # one token whose int8 row does not fit the LDS limit: act-quant runs separately
+    "t1_k33024_unfused": (1, "bf16", [(33024, 100)]),
     # two tokens over the two-token work limit (4M): act-quant runs separately
     "t2_bf16_many_blocks": (2, "bf16", [(8192, 8200)]),
 }
