@@ -236,6 +236,7 @@ struct DecProblem {
   uint16_t* h;            // gated: [T, N / 2] bfloat16 out (then y is not written)
   int N, K;
   int per;                // chunks per wave: ceil((K / 256) / nw) <= CPW
+  int ldy;                // row stride of y and acc (N, or more for a row range of a wider problem)
 };
 constexpr int kMaxGroup = 8;
 struct DecGroup {
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   // fetches them in dependent rounds around the early exit below.
   __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
                    "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
-                   "s"(pr.per), "s"(T), "s"(nwaves));
+                   "s"(pr.per), "s"(pr.ldy), "s"(T), "s"(nwaves));
   if constexpr (GATED) __asm__ volatile("" ::"s"(pr.gamma2), "s"(pr.h));
   const int N = pr.N, K = pr.K, per = pr.per;
   const int n0 = (int)blockIdx.x * 16;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   if (ticket != nwaves - 1) return;
   if constexpr (GATED) {
     // rows 2i (gate) and 2i + 1 (up) of the tile make output n0 / 2 + i
-    const int half = N >> 1;
+    const int ldy = pr.ldy, half = ldy >> 1;
     for (int idx = lane; idx < 8 * T; idx += 64) {
       const int i = idx & 7, tl = idx >> 3;
       const int nn = n0 + 2 * i;
@@ -620,8 +621,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
       const int su = __hip_atomic_load(&tile[tl * 16 + 2 * i + 1], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
       if (pr.acc) {
-        pr.acc[(int64_t)tl * N + nn] = sg;
-        pr.acc[(int64_t)tl * N + nn + 1] = su;
+        pr.acc[(int64_t)tl * ldy + nn] = sg;
+        pr.acc[(int64_t)tl * ldy + nn + 1] = su;
       }
       float a;
       if constexpr (MODE == kInt8) a = idx < 64 ? am : pr.absmax[tl];
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     const int nn = n0 + i;
     if (nn >= N) continue;
     const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const int64_t o = (int64_t)tl * N + nn;
+    const int64_t o = (int64_t)tl * pr.ldy + nn;
     if (pr.acc) pr.acc[o] = sum;
     float sc = MODE == kInt8 ? out_scale(g, am) : osc;
     if (idx >= 64) {   // T > 4: tokens past lane 63's
@@ -778,7 +779,10 @@ template <int MODE>
 hipError_t run_dec(DecGroup& grp, int count, int bx, const DecShape& sh, size_t lds,
                    hipStream_t stream) {
   grp.nw = sh.nw;
-  for (int i = 0; i < count; ++i) grp.p[i].per = (grp.p[i].K / 256 + sh.nw - 1) / sh.nw;
+  for (int i = 0; i < count; ++i) {
+    grp.p[i].per = (grp.p[i].K / 256 + sh.nw - 1) / sh.nw;
+    if (grp.p[i].ldy == 0) grp.p[i].ldy = grp.p[i].N;
+  }
   const dim3 grid((unsigned)bx, (unsigned)count);
   bool one = false;   // single-token specialisation of the fused prologue
   if constexpr (MODE != kInt8) one = grp.T == 1;
@@ -840,23 +844,47 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
     }
     return hipSuccess;
   }
+  // The grid is (most blocks of a problem) x (problems), so blocks past a
+  // narrower problem's rows only launch and exit, and they delay the
+  // dispatch of the problems after them.  When the problems' block counts
+  // differ, each wider one is cut into row ranges of about the narrowest
+  // one's count (problems of their own, writing rows row0 .. of y with y's
+  // full row stride) while at most kMaxGroup of them result.
+  int64_t bmin = INT64_MAX, kmax = 0, blocks = 0;
+  int pieces = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t b = (probs[i].N + 15) / 16;
+    bmin = b < bmin ? b : bmin;
+    kmax = probs[i].K > kmax ? probs[i].K : kmax;
+    blocks += b;
+  }
+  for (int i = 0; i < count; ++i) pieces += (int)(((probs[i].N + 15) / 16 + bmin - 1) / bmin);
+  const bool cut = pieces <= kMaxGroup;
   DecGroup grp = {};
   grp.T = (int)t;
-  int64_t bx = 0, blocks = 0, kmax = 0;
+  int np = 0;
+  int64_t bx = 0;
   for (int i = 0; i < count; ++i) {
     const bl_linear& q = probs[i];
-    grp.p[i] = DecProblem{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr,
-                          q.y, q.acc, q.xq, q.absmax, nullptr, nullptr, (int)q.N, (int)q.K, 0};
-    const int64_t b = (q.N + 15) / 16;
-    blocks += b;
-    if (b > bx) bx = b;
-    if (q.K > kmax) kmax = q.K;
+    const int64_t step = cut ? bmin * 16 : q.N;    // rows per piece
+    for (int64_t row0 = 0; row0 < q.N; row0 += step) {
+      const int64_t rows = q.N - row0 < step ? q.N - row0 : step;
+      const bool head = row0 == 0;                 // writes the int8 activations and absmax
+      grp.p[np] = DecProblem{reinterpret_cast<const uint32_t*>(q.packed) + row0 * (q.K / 16),
+                             q.gamma, q.x, nullptr, q.y + row0,
+                             q.acc ? q.acc + row0 : nullptr, head ? q.xq : nullptr,
+                             head ? q.absmax : nullptr, nullptr, nullptr, (int)rows, (int)q.K, 0,
+                             (int)q.N};
+      const int64_t pb = (rows + 15) / 16;
+      bx = pb > bx ? pb : bx;
+      ++np;
+    }
   }
   // one block shape for the group: sized for the widest K
   const DecShape sh = dec_shape(blocks, kmax);
   const size_t lds = dec_lds(t, kmax, rb);
-  return bf16 ? run_dec<kBf16>(grp, count, (int)bx, sh, lds, stream)
-              : run_dec<kF32>(grp, count, (int)bx, sh, lds, stream);
+  return bf16 ? run_dec<kBf16>(grp, np, (int)bx, sh, lds, stream)
+              : run_dec<kF32>(grp, np, (int)bx, sh, lds, stream);
 }
 
 namespace {

@@ -356,6 +356,10 @@ GROUPS = {
     "layer_qkv_t1_bf16": (1, "bf16", [(2560, 2560), (2560, 640), (2560, 640)]),
     "layer_gateup_t1_bf16": (1, "bf16", [(2560, 6912), (2560, 6912)]),
     "layer_down_t1_bf16": (1, "bf16", [(6912, 2560)]),
+    # unequal problems cut into row pieces of the narrowest one's block count
+    # (ragged last pieces, int32 sums and y written through the row stride)
+    "t1_bf16_cut_ragged": (1, "bf16", [(2560, 100), (2560, 37)]),
+    "t3_f32_cut": (3, "f32", [(1024, 300), (1024, 64), (512, 70)]),
     "t4_f32_ragged": (4, "f32", [(256, 37), (512, 100), (768, 1)]),
     "t3_bf16_mixed_k": (3, "bf16", [(2048, 50), (256, 17)]),
     "t2_k28672": (2, "bf16", [(28672, 64)]),
