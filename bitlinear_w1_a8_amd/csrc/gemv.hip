@@ -244,10 +244,18 @@ struct DecGroup {
   int T, nw;              // tokens; waves per block (the block has 64 * nw threads)
 };
 
-// LDS header of the decode kernel: 64 zero bytes, the 16 x 16 int32 tile
-// (token-major), the finishing counter and 16 absmax bit patterns.
-constexpr int kDecHead = 64 + 256 * 4 + 4 + 16 * 4 + 12;   // padded to 16 bytes
-static_assert(kDecHead % 16 == 0, "LDS header alignment");
+// LDS header of the decode kernel: 64 zero bytes, the 16-token x 16 RT-row
+// int32 tile (token-major), the finishing counter and 16 absmax bit patterns
+// (padded to 16 bytes).
+constexpr int dec_head(int rt) { return 64 + 256 * rt * 4 + 4 + 16 * 4 + 12; }
+static_assert(dec_head(1) % 16 == 0 && dec_head(2) % 16 == 0, "LDS header alignment");
+
+// Waves per SIMD the decode kernel is compiled for: eight with int8 input on
+// one row tile (64 VGPRs), fewer where the raw activations or a second row
+// tile's weights take registers.
+constexpr int dec_waves_per_eu(int cpw, int mode, int rt) {
+  return rt == 1 ? (mode == 0 ? 8 : 6) : (cpw == 8 ? 4 : cpw == 4 ? 5 : 6);
+}
 
 typedef __attribute__((address_space(3))) void* dec_lds_t;
 typedef __attribute__((address_space(1))) void* dec_glb_t;
@@ -263,8 +271,9 @@ __device__ __forceinline__ float raw_elem(const uint4& v, int e) {
   }
 }
 
-template <int CPW, int MODE, bool ONE, bool GATED>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kInt8 ? 8 : 6))) void k_gemv_dec(const DecGroup grp) {
+template <int CPW, int MODE, bool ONE, bool GATED, int RT>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu(CPW, MODE, RT)))) void k_gemv_dec(const DecGroup grp) {
+  constexpr int kRows = 16 * RT;                    // weight rows of a block (RT tiles of 16)
   extern __shared__ __align__(16) unsigned char smem[];
   const DecProblem pr = grp.p[blockIdx.y];
   const int T = ONE ? 1 : grp.T, nwaves = grp.nw;
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
                    "s"(pr.per), "s"(pr.ldy), "s"(T), "s"(nwaves));
   if constexpr (GATED) __asm__ volatile("" ::"s"(pr.gamma2), "s"(pr.h));
   const int N = pr.N, K = pr.K, per = pr.per;
-  const int n0 = (int)blockIdx.x * 16;
+  const int n0 = (int)blockIdx.x * kRows;
   if (n0 >= N) return;                              // the grid spans the widest problem
 
   const int lane = threadIdx.x & 63, nthreads = nwaves * 64;
@@ -292,21 +301,25 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   const int tstride = K + 16;
   int* zero = reinterpret_cast<int*>(smem);                    // 16 ints of zeros
   int* tile = zero + 16;                                       // [token][row]
-  int* counter = tile + 256;
+  int* counter = tile + 256 * RT;
   int* amax = counter + 1;
-  unsigned char* xs8 = smem + kDecHead;
+  unsigned char* xs8 = smem + dec_head(RT);
   unsigned char* raw = xs8 + T * tstride;
 
-  int n = n0 + r;
-  n = n < N ? n : N - 1;                            // rows past N are computed, never stored
-  const uint4* wrow = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
+  const uint4* wrow[RT];                            // row r of each 16-row tile
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int n = n0 + 16 * rt + r;
+    n = n < N ? n : N - 1;                          // rows past N are computed, never stored
+    wrow[rt] = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
+  }
 
   // Issue order matters: vector memory operations retire in order, so what
   // is waited on first goes first.  The token absmax (int8 input) ...
   // (gated outputs: token l >> 3 of lane l, eight outputs per token)
   constexpr bool gated = GATED;
   float am = 0.0f;
-  if constexpr (MODE == kInt8) am = pr.absmax[min(gated ? lane >> 3 : lane >> 4, T - 1)];
+  if constexpr (MODE == kInt8) am = pr.absmax[min(lane / (gated ? kRows / 2 : kRows), T - 1)];
   // ... then the activations, straight into LDS (lane l's 16 bytes land at
   // the wave's base + 16 l): int8 input, this wave's own k run; raw input
   // (step A1 fused), the whole rows, shared by the block ...
@@ -362,21 +375,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   // activation loads are issued; after the weight loads it would wait until
   // all of those are issued, which stalls while the CU's queue is full.  The
   // same barrier orders the header clearing before the tile adds.
-  for (int i = threadIdx.x; i < 16 + 256 + 1 + 16; i += nthreads) zero[i] = 0;
+  for (int i = threadIdx.x; i < 16 + 256 * RT + 1 + 16; i += nthreads) zero[i] = 0;
   lds_sync();
   // ... and last every weight chunk of this wave; slots past cnt repeat the
   // row's last chunk and meet a zero B operand below.
-  uint4 buf[CPW];
+  uint4 buf[RT][CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int c = min(c0 + i, nchunks - 1);
-    buf[i] = wrow[(size_t)c * 4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) buf[rt][i] = wrow[rt][(size_t)c * 4];
   }
 
   int qsum = 0;     // sum of q over this wave's k run, token of lane l: l & 15
-  float a_t = am;   // absmax of the token whose outputs lane l writes (l >> 4)
+  float a_t = 0.0f; // one raw token: its absmax
   if constexpr (MODE == kInt8) {
-    wait_vmem<CPW>();                               // this wave's activation run landed
+    wait_vmem<RT * CPW>();                               // this wave's activation run landed
     for (int t = 0; t < T; ++t) {
       const uint4* xt = reinterpret_cast<const uint4*>(xs8 + t * tstride + run0);
       int part = 0;
@@ -393,7 +407,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   } else if constexpr (ONE) {
     // Step A1 in the block, one token, from registers: the absmax over this
     // wave's run (its repeats included), then over the block through LDS ...
-    wait_vmem<CPW>();                               // this lane's raw activations landed
+    wait_vmem<RT * CPW>();                               // this lane's raw activations landed
     uint32_t mx = 0;                                // magnitude bit patterns
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -450,7 +464,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   } else {
     // Step A1 in the block.  The absmax of each token (T <= 4) over all of
     // K, from every wave's share of the raw rows ...
-    wait_vmem<CPW>();                               // wave 0: the raw rows landed
+    wait_vmem<RT * CPW>();                               // wave 0: the raw rows landed
     lds_sync();                                     // ... for every wave
     constexpr int E = MODE == kBf16 ? 8 : 4;        // elements per 16 bytes
     const int per_tok = K / E, nvec = T * per_tok;
@@ -496,7 +510,6 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
 #pragma unroll
     for (int tt = 0; tt < (ONE ? 1 : 4); ++tt)
       sc[tt] = tt < T ? kQb / fmaxf(__uint_as_float((uint32_t)amax[tt]), kEps) : 0.0f;
-    a_t = __uint_as_float((uint32_t)amax[ONE ? 0 : min(lane >> 4, T - 1)]);
     const bool first = blockIdx.x == 0;
     const int ru = runb / 4;                        // 4-element units per token in the run
     int tsum[4] = {0, 0, 0, 0};
@@ -548,15 +561,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     if (first && wave == 0 && pr.absmax_out && lane < T)
       pr.absmax_out[lane] = __uint_as_float((uint32_t)amax[lane]);
   }
-  // lane l's output scale (token l >> 4); with int8 input it waits for the epilogue
-  float osc = 0.0f;
-  if constexpr (MODE != kInt8) osc = out_scale(g, a_t);
 
   // B operands of slot i: this token's 64 bytes of chunk c0 + i (four
   // 16-byte vectors; slice j takes dword j of each), or zeros for tokens past
   // T and for the repeated slots past cnt
   const unsigned char* xrow = xs8 + (r < T ? r : 0) * tstride + qg * 64;
-  v4i a1 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0}, a16 = {0, 0, 0, 0};
+  v4i a1[RT], a4[RT], a16[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) a1[rt] = a4[rt] = a16[rt] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const uint32_t* xc = (r < T && i < cnt)
@@ -564,43 +576,75 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
                              : reinterpret_cast<const uint32_t*>(zero);
     // slice j: dword j of each 16-byte vector (two ds_read2_b32 each)
     auto xs = [&](int j) { return v4i{(int)xc[j], (int)xc[4 + j], (int)xc[8 + j], (int)xc[12 + j]}; };
-    const uint4 w4 = buf[i];
-    if constexpr (CPW < 8) {
-      // fields masked in place: c, 4c and 16c per byte, three accumulators
-      a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-          (v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u), (int)(w4.z & 0x03030303u),
-               (int)(w4.w & 0x03030303u)}),
-          xs(0), a1, 0, 0, 0);
-      a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-          (v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu), (int)(w4.z & 0x0C0C0C0Cu),
-               (int)(w4.w & 0x0C0C0C0Cu)}),
-          xs(1), a4, 0, 0, 0);
-      a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-          (v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u), (int)(w4.z & 0x30303030u),
-               (int)(w4.w & 0x30303030u)}),
-          xs(2), a16, 0, 0, 0);
-    } else {
-      // eight chunks in flight leave no room for three accumulators: every
-      // field is shifted down to c and summed in one
+    if constexpr (RT == 1) {
+      const uint4 w4 = buf[0][i];
+      if constexpr (CPW < 8) {
+        // fields masked in place: c, 4c and 16c per byte, three accumulators
+        a1[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            (v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u), (int)(w4.z & 0x03030303u),
+                 (int)(w4.w & 0x03030303u)}),
+            xs(0), a1[0], 0, 0, 0);
+        a4[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            (v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu), (int)(w4.z & 0x0C0C0C0Cu),
+                 (int)(w4.w & 0x0C0C0C0Cu)}),
+            xs(1), a4[0], 0, 0, 0);
+        a16[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            (v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u), (int)(w4.z & 0x30303030u),
+                 (int)(w4.w & 0x30303030u)}),
+            xs(2), a16[0], 0, 0, 0);
+      } else {
+        // eight chunks in flight leave no room for three accumulators: every
+        // field is shifted down to c and summed in one
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            (v4i{(int)codes_of(w4.x, j), (int)codes_of(w4.y, j), (int)codes_of(w4.z, j),
-                 (int)codes_of(w4.w, j)}),
-            xs(j), a1, 0, 0, 0);
+        for (int j = 0; j < 3; ++j)
+          a1[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              (v4i{(int)codes_of(w4.x, j), (int)codes_of(w4.y, j), (int)codes_of(w4.z, j),
+                   (int)codes_of(w4.w, j)}),
+              xs(j), a1[0], 0, 0, 0);
+      }
+      a1[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
+               (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)}),
+          xs(3), a1[0], 0, 0, 0);
+    } else {
+      // two row tiles: the same, slice by slice, one B slice serving both
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i b = xs(j);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint4 w4 = buf[rt][i];
+          v4i a;
+          if (j == 3) {
+            a = v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
+                    (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)};
+          } else if constexpr (CPW < 8) {
+            const uint32_t m = j == 0 ? 0x03030303u : j == 1 ? 0x0C0C0C0Cu : 0x30303030u;
+            a = v4i{(int)(w4.x & m), (int)(w4.y & m), (int)(w4.z & m), (int)(w4.w & m)};
+          } else {
+            a = v4i{(int)codes_of(w4.x, j), (int)codes_of(w4.y, j), (int)codes_of(w4.z, j),
+                    (int)codes_of(w4.w, j)};
+          }
+          if (CPW < 8 && j == 1)
+            a4[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, a4[rt], 0, 0, 0);
+          else if (CPW < 8 && j == 2)
+            a16[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, a16[rt], 0, 0, 0);
+          else
+            a1[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, a1[rt], 0, 0, 0);
+        }
+      }
     }
-    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        (v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
-             (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)}),
-        xs(3), a1, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);   // one chunk's operands live at a time
   }
 
-  // lane (qg, r) holds rows 4qg + v of token column r
+  // lane (qg, r) holds rows 16 rt + 4qg + v of token column r
   if (r < T) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      atomicAdd(&tile[r * 16 + 4 * qg + v], a1[v] + (a4[v] >> 2) + (a16[v] >> 4) - qsum);
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        atomicAdd(&tile[r * kRows + 16 * rt + 4 * qg + v],
+                  a1[rt][v] + (a4[rt][v] >> 2) + (a16[rt][v] >> 4) - qsum);
   }
   // The last wave to add its tile writes the block's outputs; the others are
   // done.  The counter's release/acquire orders the tile adds before it.
@@ -612,13 +656,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
   if constexpr (GATED) {
     // rows 2i (gate) and 2i + 1 (up) of the tile make output n0 / 2 + i
     const int ldy = pr.ldy, half = ldy >> 1;
-    for (int idx = lane; idx < 8 * T; idx += 64) {
-      const int i = idx & 7, tl = idx >> 3;
+    for (int idx = lane; idx < kRows / 2 * T; idx += 64) {
+      const int i = idx % (kRows / 2), tl = idx / (kRows / 2);
       const int nn = n0 + 2 * i;
       if (nn >= N) continue;
-      const int sg = __hip_atomic_load(&tile[tl * 16 + 2 * i], __ATOMIC_RELAXED,
+      const int sg = __hip_atomic_load(&tile[tl * kRows + 2 * i], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
-      const int su = __hip_atomic_load(&tile[tl * 16 + 2 * i + 1], __ATOMIC_RELAXED,
+      const int su = __hip_atomic_load(&tile[tl * kRows + 2 * i + 1], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
       if (pr.acc) {
         pr.acc[(int64_t)tl * ldy + nn] = sg;
@@ -632,18 +676,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(MODE == kI
     }
     return;
   }
-  for (int idx = lane; idx < 16 * T; idx += 64) {
-    const int i = idx & 15, tl = idx >> 4;
+  for (int idx = lane; idx < kRows * T; idx += 64) {
+    const int i = idx % kRows, tl = idx / kRows;
     const int nn = n0 + i;
     if (nn >= N) continue;
     const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int64_t o = (int64_t)tl * pr.ldy + nn;
     if (pr.acc) pr.acc[o] = sum;
-    float sc = MODE == kInt8 ? out_scale(g, am) : osc;
-    if (idx >= 64) {   // T > 4: tokens past lane 63's
-      sc = out_scale(g, MODE == kInt8 ? pr.absmax[tl] : __uint_as_float((uint32_t)amax[tl]));
-    }
-    pr.y[o] = (float)sum * sc;
+    float a;                                        // the token's absmax (int8: lane's own first)
+    if constexpr (MODE == kInt8) a = idx < 64 ? am : pr.absmax[tl];
+    else a = ONE ? a_t : __uint_as_float((uint32_t)amax[tl]);
+    pr.y[o] = (float)sum * out_scale(g, a);
   }
 }
 
@@ -696,6 +739,12 @@ namespace {
 #ifndef BL_GEMV_DEC_MAXW_SHORT
 #define BL_GEMV_DEC_MAXW_SHORT 16   // ... or this many give every wave BL_GEMV_DEC_CPW chunks
 #endif
+#ifndef BL_GEMV_DEC_RT2_MIN_TILES
+#define BL_GEMV_DEC_RT2_MIN_TILES 512   // 16-row tiles from which a block takes two ...
+#endif
+#ifndef BL_GEMV_DEC_RT2_MAX_CHUNKS
+#define BL_GEMV_DEC_RT2_MAX_CHUNKS 16   // ... of rows of at most this many 256-k chunks
+#endif
 #ifndef BL_GEMV_DEC_CPW
 #define BL_GEMV_DEC_CPW 2           // chunks per wave aimed for
 #endif
@@ -726,10 +775,18 @@ namespace {
 // launch 16.8 -> 15.8 us against 4 of 8); 14 of 8 for K = 28672 (16 of 7:
 // 15.1 against 14.5 us).
 struct DecShape {
-  int nw, cpw;
+  int nw, cpw, rt;          // waves per block, chunks per wave (template), 16-row tiles per block
 };
-DecShape dec_shape(int64_t blocks, int64_t kmax) {
+DecShape dec_shape(int64_t tiles, int64_t kmax) {
+  // Two row tiles per block for short rows once that still leaves a block
+  // for every CU: the block's activations (fetched and, fused, quantised once
+  // per block) then serve 32 rows, and half as many blocks are launched.
+  // Measured: the 2B gate/up launch (K = 2560, 864 tiles) gains, the layer
+  // 1167 -> 1184 GB/s; 70B rows (K = 8192, 28672) lose 2 us, their waves
+  // then holding twice the weights at half the occupancy.
   const int nchunks = (int)(kmax / 256);
+  const int rt = tiles >= BL_GEMV_DEC_RT2_MIN_TILES && nchunks <= BL_GEMV_DEC_RT2_MAX_CHUNKS ? 2 : 1;
+  const int64_t blocks = (tiles + rt - 1) / rt;
   int nw = (nchunks + BL_GEMV_DEC_CPW - 1) / BL_GEMV_DEC_CPW;
   const int maxw = nw <= BL_GEMV_DEC_MAXW_SHORT ? BL_GEMV_DEC_MAXW_SHORT : BL_GEMV_DEC_MAXW;
   if (nw > maxw) nw = maxw;
@@ -739,7 +796,7 @@ DecShape dec_shape(int64_t blocks, int64_t kmax) {
   if (nw < least) nw = least;
   const int per = (nchunks + nw - 1) / nw;
   nw = (nchunks + per - 1) / per;   // the same chunks per wave, no wave left without
-  return DecShape{nw, per <= 2 ? 2 : per <= 4 ? 4 : 8};
+  return DecShape{nw, per <= 2 ? 2 : per <= 4 ? 4 : 8, rt};
 }
 
 // Shapes the decode kernel takes: raw_bytes is 0 for int8 activations, else
@@ -759,29 +816,41 @@ bool fuse_work_ok(int64_t t, int64_t work) {
   return work <= (t == 1 ? BL_GEMV_FUSE_MAX_WORK_T1 : BL_GEMV_FUSE_MAX_WORK);
 }
 
-size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes) {
+size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes, int rt) {
   const size_t staged = t == 1 ? 0 : (size_t)t * kmax * raw_bytes;   // raw rows, T > 1
-  return kDecHead + (size_t)t * (kmax + 16) + staged;
+  return dec_head(rt) + (size_t)t * (kmax + 16) + staged;
+}
+
+template <int MODE, bool ONE, bool GATED, int RT>
+void launch_dec_rt(const DecGroup& grp, dim3 grid, const DecShape& sh, size_t lds,
+                   hipStream_t stream) {
+  if (sh.cpw == 2)
+    k_gemv_dec<2, MODE, ONE, GATED, RT><<<grid, sh.nw * 64, lds, stream>>>(grp);
+  else if (sh.cpw == 4)
+    k_gemv_dec<4, MODE, ONE, GATED, RT><<<grid, sh.nw * 64, lds, stream>>>(grp);
+  else
+    k_gemv_dec<8, MODE, ONE, GATED, RT><<<grid, sh.nw * 64, lds, stream>>>(grp);
 }
 
 template <int MODE, bool ONE, bool GATED>
 void launch_dec(const DecGroup& grp, dim3 grid, const DecShape& sh, size_t lds,
                 hipStream_t stream) {
-  if (sh.cpw == 2)
-    k_gemv_dec<2, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
-  else if (sh.cpw == 4)
-    k_gemv_dec<4, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
+  if (sh.rt == 2)
+    launch_dec_rt<MODE, ONE, GATED, 2>(grp, grid, sh, lds, stream);
   else
-    k_gemv_dec<8, MODE, ONE, GATED><<<grid, sh.nw * 64, lds, stream>>>(grp);
+    launch_dec_rt<MODE, ONE, GATED, 1>(grp, grid, sh, lds, stream);
 }
 
 template <int MODE>
-hipError_t run_dec(DecGroup& grp, int count, int bx, const DecShape& sh, size_t lds,
+hipError_t run_dec(DecGroup& grp, int count, const DecShape& sh, size_t lds,
                    hipStream_t stream) {
   grp.nw = sh.nw;
+  int bx = 0;   // blocks of the problem with the most rows
   for (int i = 0; i < count; ++i) {
     grp.p[i].per = (grp.p[i].K / 256 + sh.nw - 1) / sh.nw;
     if (grp.p[i].ldy == 0) grp.p[i].ldy = grp.p[i].N;
+    const int b = (grp.p[i].N + 16 * sh.rt - 1) / (16 * sh.rt);
+    bx = b > bx ? b : bx;
   }
   const dim3 grid((unsigned)bx, (unsigned)count);
   bool one = false;   // single-token specialisation of the fused prologue
@@ -813,7 +882,8 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
                         nullptr, nullptr, gamma2, h, n, k, 0};
   const int blocks = (n + 15) / 16;
-  return run_dec<kInt8>(grp, 1, blocks, dec_shape(blocks, k), dec_lds(t, k, 0), stream);
+  const DecShape sh = dec_shape(blocks, k);
+  return run_dec<kInt8>(grp, 1, sh, dec_lds(t, k, 0, sh.rt), stream);
 }
 
 }  // namespace
@@ -844,29 +914,35 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
     }
     return hipSuccess;
   }
+  // one block shape for the group: sized for the widest K and all 16-row tiles
+  int64_t tiles = 0, kmax = 0;
+  for (int i = 0; i < count; ++i) {
+    tiles += (probs[i].N + 15) / 16;
+    kmax = probs[i].K > kmax ? probs[i].K : kmax;
+  }
+  const DecShape sh = dec_shape(tiles, kmax);
+  const size_t lds = dec_lds(t, kmax, rb, sh.rt);
   // The grid is (most blocks of a problem) x (problems), so blocks past a
   // narrower problem's rows only launch and exit, and they delay the
   // dispatch of the problems after them.  When the problems' block counts
   // differ, each wider one is cut into row ranges of about the narrowest
   // one's count (problems of their own, writing rows row0 .. of y with y's
   // full row stride) while at most kMaxGroup of them result.
-  int64_t bmin = INT64_MAX, kmax = 0, blocks = 0;
-  int pieces = 0;
+  const int64_t brows = 16 * sh.rt;                 // weight rows per block
+  int64_t bmin = INT64_MAX;
   for (int i = 0; i < count; ++i) {
-    const int64_t b = (probs[i].N + 15) / 16;
+    const int64_t b = (probs[i].N + brows - 1) / brows;
     bmin = b < bmin ? b : bmin;
-    kmax = probs[i].K > kmax ? probs[i].K : kmax;
-    blocks += b;
   }
-  for (int i = 0; i < count; ++i) pieces += (int)(((probs[i].N + 15) / 16 + bmin - 1) / bmin);
+  int pieces = 0;
+  for (int i = 0; i < count; ++i) pieces += (int)(((probs[i].N + brows - 1) / brows + bmin - 1) / bmin);
   const bool cut = pieces <= kMaxGroup;
   DecGroup grp = {};
   grp.T = (int)t;
   int np = 0;
-  int64_t bx = 0;
   for (int i = 0; i < count; ++i) {
     const bl_linear& q = probs[i];
-    const int64_t step = cut ? bmin * 16 : q.N;    // rows per piece
+    const int64_t step = cut ? bmin * brows : q.N;  // rows per piece
     for (int64_t row0 = 0; row0 < q.N; row0 += step) {
       const int64_t rows = q.N - row0 < step ? q.N - row0 : step;
       const bool head = row0 == 0;                 // writes the int8 activations and absmax
@@ -875,16 +951,11 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
                              q.acc ? q.acc + row0 : nullptr, head ? q.xq : nullptr,
                              head ? q.absmax : nullptr, nullptr, nullptr, (int)rows, (int)q.K, 0,
                              (int)q.N};
-      const int64_t pb = (rows + 15) / 16;
-      bx = pb > bx ? pb : bx;
       ++np;
     }
   }
-  // one block shape for the group: sized for the widest K
-  const DecShape sh = dec_shape(blocks, kmax);
-  const size_t lds = dec_lds(t, kmax, rb);
-  return bf16 ? run_dec<kBf16>(grp, np, (int)bx, sh, lds, stream)
-              : run_dec<kF32>(grp, np, (int)bx, sh, lds, stream);
+  return bf16 ? run_dec<kBf16>(grp, np, sh, lds, stream)
+              : run_dec<kF32>(grp, np, sh, lds, stream);
 }
 
 namespace {
@@ -940,9 +1011,9 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
     grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma_gate, x, nullptr,
                           nullptr, acc, xq, absmax, gamma_up, h, (int)n, (int)k, 0};
     const DecShape sh = dec_shape(blocks, k);
-    const size_t lds = dec_lds(t, k, rb);
-    return bf16 ? run_dec<kBf16>(grp, 1, (int)blocks, sh, lds, stream)
-                : run_dec<kF32>(grp, 1, (int)blocks, sh, lds, stream);
+    const size_t lds = dec_lds(t, k, rb, sh.rt);
+    return bf16 ? run_dec<kBf16>(grp, 1, sh, lds, stream)
+                : run_dec<kF32>(grp, 1, sh, lds, stream);
   }
   hipError_t e = launch_quant(x, bf16, t, k, xq, absmax, nullptr, stream);
   if (e != hipSuccess) return e;
