@@ -221,6 +221,20 @@ def test_forward_shapes(bl, t, n, k, algo):
                   tern, q, gamma, absmax, algo)
 
 
+# prefill-sized problems on the 128 x 512 tiles: ragged T and N (partial
+# tiles in both directions), K steps 1, 4 and 5 (a whole three-stage cycle,
+# one and two steps past it)
+WIDE_SHAPES = [(2085, 6976, 512), (2048, 6500, 640), (2304, 6400, 128)]
+
+
+@pytest.mark.parametrize("algo", ["gemm", "auto"])
+@pytest.mark.parametrize("t,n,k", WIDE_SHAPES, ids=[f"T{t}_N{n}_K{k}" for t, n, k in WIDE_SHAPES])
+def test_forward_wide_tiles_ragged(bl, t, n, k, algo):
+    tern, q, absmax, gamma = _forward_inputs(t, n, k, 7 * t + n + k)
+    check_forward(bl, dev(oracle.pack_ternary(tern)), dev(np.array([gamma])), dev(q), dev(absmax),
+                  tern, q, gamma, absmax, algo)
+
+
 def test_forward_extremes(bl):
     """All q = +-127 against all-ones rows: the largest sums the contraction makes."""
     t, n, k = 3, 48, 4096
