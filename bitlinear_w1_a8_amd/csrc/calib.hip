@@ -1,5 +1,5 @@
 // Measurement helpers, not part of the forward: the ceilings that the
-// forward's kernels are judged against, measured on the device at hand
+// forward's kernels are compared with, measured on the device at hand
 // rather than taken from the data sheet.
 //
 //  - an empty kernel: the launch floor a short kernel cannot go below;

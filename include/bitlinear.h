@@ -306,7 +306,7 @@ int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
 
 /* ------------------------------------------------------------------------
  * Measurement helpers.  Not part of the forward: they measure, on the device
- * at hand, the ceilings that the forward's kernels are judged against (the
+ * at hand, the ceilings that the forward's kernels are compared with (the
  * launch floor, the HBM read stream, the int8 matrix-core rate).  Errors as
  * for every call above; they touch no memory but their own arguments.
  * ------------------------------------------------------------------------ */
