@@ -214,7 +214,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ 
 //     column) over the banks;
 //   packed weights: 1 KiB = 32 rows x 32 bytes (8 words = 128 k), row-major.
 // Each wave reads its four weight words per fragment with one 16-byte LDS
-// read and expands them in registers, as in the kernel above.
+// read.  Two-bit weights go to the MFMA as their codes c = t + 1 in {0, 1, 2}
+// (one or two VALU operations per four weights, no byte-permute), so the
+// contraction yields sum c*q = sum t*q + sum q; each wave sums the q of the
+// activation chunks it loaded itself (one LDS read and four dot4 operations
+// per 1 KiB chunk and K step), and the epilogue subtracts each token's total
+// over the block's K range.  All of it is integer arithmetic: the result is
+// the same exact int32 sum.  (Measured against the byte-permute expansion:
+// T = 2048 prefill and 70B T = 256 4-8% faster.)
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -273,6 +280,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
   __shared__ float scale2[GATED ? BM : 1];
+  __shared__ int rsum[WBITS == 2 ? BM : 1];   // two-bit weights: each token's sum of q
   auto abuf = [&](auto st) -> unsigned char* {
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return A0;
@@ -377,6 +385,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
+  int qpart[kAChunks];   // per lane: sum of q over its 16-byte pieces of chunk i
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) qpart[i] = 0;
+
   const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : K / BK;   // >= 1 (host)
   constexpr int kLoads = kAChunks + kBChunks;     // this wave's loads per tile
   static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
@@ -406,6 +418,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
     const unsigned char* Bt =
         bbuf(stage_c) + (wn * 32 * WNF + m) * kBRow + (WBITS == 2 ? 16 * h : 0);
+    if constexpr (WBITS == 2) {
+      // this wave's own activation chunks of the step (rows 8c .. 8c + 7,
+      // 16 bytes per lane, slot order irrelevant to a sum): sum of q
+#pragma unroll
+      for (int i = 0; i < kAChunks; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(abuf(stage_c) +
+                                                        (wave * kAChunks + i) * 1024 + 16 * lane);
+        int p = qpart[i];
+        p = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, p, false);
+        p = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, p, false);
+        p = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, p, false);
+        qpart[i] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, p, false);
+      }
+    }
     uint4 bw[WNF];
 #pragma unroll
     for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * kBRow);
@@ -424,8 +450,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
         const uint32_t w = s == 0 ? bw[j].x : s == 1 ? bw[j].y : s == 2 ? bw[j].z : bw[j].w;
         v4i b;
         if constexpr (WBITS == 2) {
-          b = v4i{(int)signed_codes(w, 0), (int)signed_codes(w, 1), (int)signed_codes(w, 2),
-                  (int)signed_codes(w, 3)};
+          // codes c = t + 1 as they are: sum c * q = sum t * q + sum q
+          b = v4i{(int)codes_of(w, 0), (int)codes_of(w, 1), (int)codes_of(w, 2),
+                  (int)codes_of(w, 3)};
         } else {
           const uint32_t wh = w >> (4 * h);
           b = v4i{(int)signed_bits(wh, 0), (int)signed_bits(wh, 1), (int)signed_bits(wh, 2),
@@ -463,6 +490,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   if constexpr (STAGES == 4)
     if (kt + 2 < nk) step(I2{}, kt + 2);
   wait_vmem<0>();   // no load may land in LDS after the block has finished
+  if constexpr (WBITS == 2) {
+    // eight lanes hold the pieces of one row of a chunk: their total is the
+    // token's sum of q over this block's K range
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      int v = qpart[i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      if ((lane & 7) == 0) rsum[8 * (wave * kAChunks + i) + (lane >> 3)] = v;
+    }
+    lds_sync();
+  }
 
   if constexpr (GATED) {
     const int half = N >> 1;
@@ -473,10 +513,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
         const int r = wm * 32 * WMF + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
         const int tok = m0 + r;
         const float sg = scale[r], su = scale2[r];
+        const int qs = rsum[r];
 #pragma unroll
         for (int j = 0; j < WNF; ++j) {
           const int n = n0 + wn * 32 * WNF + j * 32 + m;
-          const int sv = acc[i][j][v];
+          const int sv = acc[i][j][v] - qs;
           // every lane takes part: lane l gets lane l ^ 1's sum
           const int other = __builtin_amdgcn_update_dpp(0, sv, 0xB1, 0xF, 0xF, false);
           if (tok >= T || n >= N) continue;
@@ -497,12 +538,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       const int tok = m0 + r;
       if (tok >= T) continue;
       const float sc = scale[r];
+      const int qs = WBITS == 2 ? rsum[r] : 0;
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
         const int n = n0 + wn * 32 * WNF + j * 32 + m;
         if (n >= N) continue;
         const int64_t o = (int64_t)tok * N + n;
-        const int sv = acc[i][j][v];
+        const int sv = acc[i][j][v] - qs;
         if constexpr (SPLIT) {
           // K split: exact int32 partial sums meet in y (zeroed beforehand,
           // read as int32 until the finishing pass rescales it in place)
