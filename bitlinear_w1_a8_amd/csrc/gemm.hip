@@ -38,11 +38,11 @@ __device__ __forceinline__ uint32_t signed_codes(uint32_t word, int j) {
   return __builtin_amdgcn_perm(kTernTable, kTernTable, codes_of(word, j));
 }
 
-// One-bit weights (bit 1 = +1, 0 = -1): bits j of the four bytes of a word are
-// four consecutive k; byte-permute them through {-1, +1}.
-constexpr uint32_t kBinTable = 0x000001FFu;   // bytes {0xFF, 0x01}
-__device__ __forceinline__ uint32_t signed_bits(uint32_t word, int j) {
-  return __builtin_amdgcn_perm(kBinTable, kBinTable, (word >> j) & 0x01010101u);
+// One-bit weights (bit u = 1 for +1, 0 for -1): bits j of the four bytes of a
+// word are four consecutive k, taken as bytes u in {0, 1}; with t = 2u - 1,
+// sum t*q = 2 * sum u*q - sum q.
+__device__ __forceinline__ uint32_t bits_of(uint32_t word, int j) {
+  return (word >> j) & 0x01010101u;
 }
 
 template <int WMF, int WNF>
@@ -219,9 +219,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint32_t* __restrict__ 
 // contraction yields sum c*q = sum t*q + sum q; each wave sums the q of the
 // activation chunks it loaded itself (one LDS read and four dot4 operations
 // per 1 KiB chunk and K step), and the epilogue subtracts each token's total
-// over the block's K range.  All of it is integer arithmetic: the result is
-// the same exact int32 sum.  (Measured against the byte-permute expansion:
-// T = 2048 prefill and 70B T = 256 4-8% faster.)
+// over the block's K range (one-bit weights likewise go in as their bits u,
+// and the epilogue forms 2 * sum u*q - sum q).  All of it is integer
+// arithmetic: the result is the same exact int32 sum.  (Measured against the
+// byte-permute expansion: T = 2048 prefill and 70B T = 256 4-8% faster.)
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -232,6 +233,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 #ifndef BL_GEMM_GROUP_M
 #define BL_GEMM_GROUP_M 4   // row blocks per group of the tile order
 #endif
+
+// The exact sum from the contraction of the weight codes and the token's sum
+// of q: two-bit codes c = t + 1 give sum t*q = acc - sum q, one-bit codes
+// u = (t + 1) / 2 give sum t*q = 2 acc - sum q.
+template <int WBITS>
+__device__ __forceinline__ int exact_sum(int acc, int qsum) {
+  return (WBITS == 2 ? acc : 2 * acc) - qsum;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
   __shared__ float scale2[GATED ? BM : 1];
-  __shared__ int rsum[WBITS == 2 ? BM : 1];   // two-bit weights: each token's sum of q
+  __shared__ int rsum[BM];   // each token's sum of q over the block's K range
   auto abuf = [&](auto st) -> unsigned char* {
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return A0;
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
     const unsigned char* Bt =
         bbuf(stage_c) + (wn * 32 * WNF + m) * kBRow + (WBITS == 2 ? 16 * h : 0);
-    if constexpr (WBITS == 2) {
+    {
       // this wave's own activation chunks of the step (rows 8c .. 8c + 7,
       // 16 bytes per lane, slot order irrelevant to a sum): sum of q
 #pragma unroll
@@ -455,8 +464,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
                   (int)codes_of(w, 3)};
         } else {
           const uint32_t wh = w >> (4 * h);
-          b = v4i{(int)signed_bits(wh, 0), (int)signed_bits(wh, 1), (int)signed_bits(wh, 2),
-                  (int)signed_bits(wh, 3)};
+          b = v4i{(int)bits_of(wh, 0), (int)bits_of(wh, 1), (int)bits_of(wh, 2),
+                  (int)bits_of(wh, 3)};
         }
 #pragma unroll
         for (int i = 0; i < WMF; ++i)
@@ -490,7 +499,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   if constexpr (STAGES == 4)
     if (kt + 2 < nk) step(I2{}, kt + 2);
   wait_vmem<0>();   // no load may land in LDS after the block has finished
-  if constexpr (WBITS == 2) {
+  {
     // eight lanes hold the pieces of one row of a chunk: their total is the
     // token's sum of q over this block's K range
 #pragma unroll
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
         for (int j = 0; j < WNF; ++j) {
           const int n = n0 + wn * 32 * WNF + j * 32 + m;
-          const int sv = acc[i][j][v] - qs;
+          const int sv = exact_sum<WBITS>(acc[i][j][v], qs);
           // every lane takes part: lane l gets lane l ^ 1's sum
           const int other = __builtin_amdgcn_update_dpp(0, sv, 0xB1, 0xF, 0xF, false);
           if (tok >= T || n >= N) continue;
@@ -538,13 +547,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       const int tok = m0 + r;
       if (tok >= T) continue;
       const float sc = scale[r];
-      const int qs = WBITS == 2 ? rsum[r] : 0;
+      const int qs = rsum[r];
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
         const int n = n0 + wn * 32 * WNF + j * 32 + m;
         if (n >= N) continue;
         const int64_t o = (int64_t)tok * N + n;
-        const int sv = acc[i][j][v] - qs;
+        const int sv = exact_sum<WBITS>(acc[i][j][v], qs);
         if constexpr (SPLIT) {
           // K split: exact int32 partial sums meet in y (zeroed beforehand,
           // read as int32 until the finishing pass rescales it in place)
