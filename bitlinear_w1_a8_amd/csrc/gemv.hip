@@ -697,6 +697,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 #ifndef BL_GEMV_MAXW
 #define BL_GEMV_MAXW 8       // most waves per block (they split K)
 #endif
+#ifndef BL_GEMV_RT2_MIN_BLOCKS
+#define BL_GEMV_RT2_MIN_BLOCKS 128   // 32-row blocks for 16 < T <= 64 from this many on
+#endif
 
 template <int VEC, int RT, int NTT, int U>
 void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
@@ -719,7 +722,16 @@ void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
                 const float* gamma2, uint16_t* h, hipStream_t stream) {
   if (t <= 16)
     run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
-  else if (t <= 32)
+  else if (n < 32 * BL_GEMV_RT2_MIN_BLOCKS) {
+    // two-tile blocks would leave most CUs idle: one tile per block, twice
+    // the blocks (measured at 6912 -> 2560: T = 32 14.0 -> 11.4 us, T = 64
+    // 21.5 -> 17.7 us; at 2560 -> 6912, 216 two-tile blocks, one tile loses)
+    if (t <= 32)
+      run<VEC, 1, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                      gamma2, h, stream);
+    else
+      run<VEC, 1, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
+  } else if (t <= 32)
     run<VEC, 2, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
                                                     gamma2, h, stream);
   else
