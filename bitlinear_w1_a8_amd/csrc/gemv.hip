@@ -754,6 +754,9 @@ namespace {
 #ifndef BL_GEMV_DEC_RT2_MIN_TILES
 #define BL_GEMV_DEC_RT2_MIN_TILES 512   // 16-row tiles from which a block takes two ...
 #endif
+#ifndef BL_GEMV_DEC_RT2_MIN_TILES_MULTI
+#define BL_GEMV_DEC_RT2_MIN_TILES_MULTI 256   // ... or this many when T > 1 ...
+#endif
 #ifndef BL_GEMV_DEC_RT2_MAX_CHUNKS
 #define BL_GEMV_DEC_RT2_MAX_CHUNKS 16   // ... of rows of at most this many 256-k chunks
 #endif
@@ -789,15 +792,19 @@ namespace {
 struct DecShape {
   int nw, cpw, rt;          // waves per block, chunks per wave (template), 16-row tiles per block
 };
-DecShape dec_shape(int64_t tiles, int64_t kmax) {
+DecShape dec_shape(int64_t tiles, int64_t kmax, int64_t t) {
   // Two row tiles per block for short rows once that still leaves a block
   // for every CU: the block's activations (fetched and, fused, quantised once
   // per block) then serve 32 rows, and half as many blocks are launched.
   // Measured: the 2B gate/up launch (K = 2560, 864 tiles) gains, the layer
   // 1167 -> 1184 GB/s; 70B rows (K = 8192, 28672) lose 2 us, their waves
   // then holding twice the weights at half the occupancy.
+  // Several tokens stage T times the activations per block, so two tiles
+  // pay from fewer tiles on (measured: 2560 -> 6912 at T = 8, 432 tiles,
+  // 6.1 -> 5.7 us; at T = 1 the same change costs 1.5%).
   const int nchunks = (int)(kmax / 256);
-  const int rt = tiles >= BL_GEMV_DEC_RT2_MIN_TILES && nchunks <= BL_GEMV_DEC_RT2_MAX_CHUNKS ? 2 : 1;
+  const int64_t min_tiles = t > 1 ? BL_GEMV_DEC_RT2_MIN_TILES_MULTI : BL_GEMV_DEC_RT2_MIN_TILES;
+  const int rt = tiles >= min_tiles && nchunks <= BL_GEMV_DEC_RT2_MAX_CHUNKS ? 2 : 1;
   const int64_t blocks = (tiles + rt - 1) / rt;
   int nw = (nchunks + BL_GEMV_DEC_CPW - 1) / BL_GEMV_DEC_CPW;
   const int maxw = nw <= BL_GEMV_DEC_MAXW_SHORT ? BL_GEMV_DEC_MAXW_SHORT : BL_GEMV_DEC_MAXW;
@@ -894,7 +901,7 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
                         nullptr, nullptr, gamma2, h, n, k, 0};
   const int blocks = (n + 15) / 16;
-  const DecShape sh = dec_shape(blocks, k);
+  const DecShape sh = dec_shape(blocks, k, t);
   return run_dec<kInt8>(grp, 1, sh, dec_lds(t, k, 0, sh.rt), stream);
 }
 
@@ -932,7 +939,7 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
     tiles += (probs[i].N + 15) / 16;
     kmax = probs[i].K > kmax ? probs[i].K : kmax;
   }
-  const DecShape sh = dec_shape(tiles, kmax);
+  const DecShape sh = dec_shape(tiles, kmax, t);
   const size_t lds = dec_lds(t, kmax, rb, sh.rt);
   // The grid is (most blocks of a problem) x (problems), so blocks past a
   // narrower problem's rows only launch and exit, and they delay the
@@ -1022,7 +1029,7 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
     grp.T = (int)t;
     grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma_gate, x, nullptr,
                           nullptr, acc, xq, absmax, gamma_up, h, (int)n, (int)k, 0};
-    const DecShape sh = dec_shape(blocks, k);
+    const DecShape sh = dec_shape(blocks, k, t);
     const size_t lds = dec_lds(t, k, rb, sh.rt);
     return bf16 ? run_dec<kBf16>(grp, 1, sh, lds, stream)
                 : run_dec<kF32>(grp, 1, sh, lds, stream);
