@@ -197,7 +197,9 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # ragged T and N; the 128 x 256 tiles; the 128 x 512 tiles
               (200, 1500, 28672), (1100, 3800, 512), (1500, 8100, 256),
               # table-lookup kernel: 4-wave blocks with word loads and a short last chunk
-              (40, 900, 3088)]
+              (40, 900, 3088),
+              # decode kernel, several int8 tokens, 257 row tiles: two per block
+              (9, 4100, 1024)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
@@ -392,6 +394,10 @@ GROUPS = {
     "t1_k33024_unfused": (1, "bf16", [(33024, 100)]),
     # two tokens over the two-token work limit (4M): act-quant runs separately
     "t2_bf16_many_blocks": (2, "bf16", [(8192, 8200)]),
+    # several tokens, at least 256 row tiles of short rows: two tiles per
+    # block in the fused kernel (ragged last block, a cut narrow problem)
+    "t3_bf16_two_tiles_ragged": (3, "bf16", [(2560, 4100), (2560, 37)]),
+    "t4_f32_two_tiles": (4, "f32", [(1024, 4096)]),
 }
 
 
