@@ -692,7 +692,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 
 // Launch-shape tunables (compile-time so variants can be built and compared).
 #ifndef BL_GEMV_U
-#define BL_GEMV_U 4          // chunks whose loads a wave issues together
+#define BL_GEMV_U 2          // chunks whose loads a wave issues together (6912 -> 2560
+                             // at T = 8: 6.0 us with 4, 5.7 with 2, 6.3 with 8)
 #endif
 #ifndef BL_GEMV_MAXW
 #define BL_GEMV_MAXW 8       // most waves per block (they split K)
