@@ -54,6 +54,7 @@ SIGNATURES["bitlinear_gated_relu2"] = (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_
                                                 _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp])
 SIGNATURES["bitlinear_linear_grouped"] = (_c_int, [ctypes.POINTER(BlLinear), _c_int, _c_i64,
                                                    _c_int, _c_vp])
+SIGNATURES["bitlinear_pack_weights_noalloc"] = (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp])
 SIGNATURES["bitlinear_calib_sink_len"] = (_c_i64, [])
 SIGNATURES["bitlinear_calib_empty"] = (_c_int, [_c_vp])
 SIGNATURES["bitlinear_calib_read"] = (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp])
@@ -139,6 +140,29 @@ def pack_weights(w):
     ws = torch.empty(wsb, dtype=torch.uint8, device=w.device)
     _check(lib.bitlinear_pack_weights(_ptr(w), n, k, _ptr(packed), _ptr(gamma), _ptr(ws), wsb,
                                       _stream(w.device)))
+    return packed, gamma
+
+
+def pack_weights_noalloc(w, packed=None, gamma=None):
+    """Step A0 through the library's own device buckets (no workspace): the
+    same results as pack_weights.  ``packed`` and ``gamma`` may be passed in
+    (preallocated outputs); otherwise they are allocated here."""
+    lib = load()
+    _need_cuda(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    if packed is None:
+        packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    _need_cuda(packed, "packed", torch.uint8)
+    _need_cuda(gamma, "gamma", torch.float32)
+    _need_shape(packed, "packed", (n, k // 4))
+    _need_shape(gamma, "gamma", (1,))
+    _same_device("pack_weights_noalloc", w, packed, gamma)
+    _check(lib.bitlinear_pack_weights_noalloc(_ptr(w), n, k, _ptr(packed), _ptr(gamma),
+                                              _stream(w.device)))
     return packed, gamma
 
 

@@ -77,6 +77,24 @@ int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed
                                       static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                   float* gamma, void* stream) {
+  const char* fn = "bitlinear_pack_weights_noalloc";
+  if (!w || !packed || !gamma) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+  if (int rc = check_k(fn, K)) return rc;
+  if (N < 1 || N > kMaxN || N * K > kMaxNK)
+    return fail(BL_ERR_SHAPE, "%s: N=%lld, K=%lld: N*K above 2^38 would overflow the %d "
+                "fixed buckets", fn, (long long)N, (long long)K, bl::kGammaBuckets);
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4))
+    return fail(BL_ERR_ALIGN, "%s: w and packed need 16-byte, gamma 4-byte alignment", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long* buckets = nullptr;
+  const hipError_t e = bl::scratch_buckets(s, &buckets);
+  if (e != hipSuccess)
+    return fail(BL_ERR_HIP, "%s: device scratch lookup failed: %s", fn, hipGetErrorString(e));
+  return launched(fn, bl::launch_pack(w, N, K, packed, gamma, buckets, s));
+}
+
 int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
                         float* absmax, int32_t* rowsum, void* stream) {
   const char* fn = "bitlinear_quant_act";

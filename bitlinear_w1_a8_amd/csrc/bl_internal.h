@@ -37,6 +37,10 @@ constexpr size_t kPackWorkspaceBytes = kGammaBuckets * sizeof(unsigned long long
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
                        unsigned long long* buckets, hipStream_t stream);
 
+// Device address of the library's own kGammaBuckets buckets on the device of
+// `stream` (the current device for the null stream), looked up once per device.
+hipError_t scratch_buckets(hipStream_t stream, unsigned long long** out);
+
 // gamma = mean |W| alone (exact sum, one rounding), shared by both weight formats.
 hipError_t launch_gamma(const float* w, int64_t n, int64_t k, float* gamma,
                         unsigned long long* buckets, hipStream_t stream);

@@ -12,9 +12,19 @@
 // of < 2^24 each stay below 2^64), the 254 bucket sums are combined into one
 // 384-bit integer, and that is rounded once to binary64, divided by N*K in
 // binary64 and rounded to binary32.
+#include <mutex>
+
 #include "bl_internal.h"
 
 namespace bl {
+
+// Device-resident buckets of bitlinear_pack_weights_noalloc, for callers that
+// cannot allocate: one copy per device, held until the process ends.  In host
+// code this name is only a stand-in for the symbol; the device address comes
+// from hipGetSymbolAddress (scratch_buckets below) and is the only form ever
+// passed to a kernel or a copy.
+static __device__ __align__(256) unsigned long long scratch[kGammaBuckets];
+
 namespace {
 
 constexpr int kHistThreads = 256;
@@ -179,6 +189,37 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, fl
   k_ternarize_pack<<<grid_for(nwords, 256, 65536), 256, 0, stream>>>(
       reinterpret_cast<const float4*>(w), nwords, gamma, reinterpret_cast<uint32_t*>(packed));
   return hipGetLastError();
+}
+
+hipError_t scratch_buckets(hipStream_t stream, unsigned long long** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // Looked up once per device, with that device current.
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = static_cast<unsigned long long*>(addr[dev]);
+  return hipSuccess;
 }
 
 hipError_t launch_interleave(const uint8_t* a, const uint8_t* b, int64_t n, int64_t k,

@@ -24,7 +24,9 @@
  * --------------------------------
  * - Tensor pointers are DEVICE pointers into row-major buffers that the
  *   caller allocates and owns; outputs are written in place.  The library
- *   keeps no state between calls and never allocates device memory.
+ *   keeps no state between calls and never allocates device memory; its one
+ *   piece of device memory is the fixed 2 KiB array that
+ *   bitlinear_pack_weights_noalloc uses in place of a workspace.
  * - `stream` is a hipStream_t passed as void*; NULL selects the null stream.
  *   Every call only enqueues work on `stream`: it never synchronises the host.
  * - Arguments are validated on the host before any HIP call.  A failed check
@@ -125,6 +127,23 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
                            float* gamma, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* bitlinear_pack_weights without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The same kernels and results as
+ * bitlinear_pack_weights; the gamma buckets live in a fixed 2 KiB array in the
+ * library's device memory (256 x uint64, one copy per device, kept until the
+ * process ends).  The call allocates nothing.  Every call on one device shares
+ * that array and clears it first, so calls that overlap on one device (on
+ * different streams, or from different threads without ordering) race and
+ * may return a wrong gamma; calls on one stream are ordered and safe.
+ *
+ *   w, N, K, packed, gamma   as bitlinear_pack_weights; N*K <= 2^38, the most
+ *            that the fixed buckets sum exactly (larger matrices: BL_ERR_SHAPE).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP (also when the
+ * array's device address cannot be looked up). */
+int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                   float* gamma, void* stream);
 
 /* Step A1: per-token absmax quantisation of activations to int8.
  * Follows "BitNet解读", activation quantisation (each token scaled into

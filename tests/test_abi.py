@@ -37,7 +37,7 @@ def lib(built_lib):
 
 def test_header_symbols_exported(lib):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
 
@@ -73,6 +73,21 @@ def test_pack_errors(lib):
     assert f(A16, 16, 64, A16, A16, A16 + 4, 4096, None) == BL_ERR_ALIGN
     assert f(A16, 16, 64, A16, A16, A16, 2047, None) == BL_ERR_WORKSPACE
     assert "2048" in _err(lib)
+
+
+def test_pack_noalloc_errors(lib):
+    f = lib.bitlinear_pack_weights_noalloc
+    assert f(None, 16, 64, A16, A16, None) == BL_ERR_NULL
+    assert f(A16, 16, 64, None, A16, None) == BL_ERR_NULL
+    assert f(A16, 16, 64, A16, None, None) == BL_ERR_NULL
+    assert f(A16, 16, 40, A16, A16, None) == BL_ERR_SHAPE
+    assert f(A16, 0, 64, A16, A16, None) == BL_ERR_SHAPE
+    # the fixed buckets sum at most 2^38 weights exactly
+    assert f(A16, 1 << 26, 8192, A16, A16, None) == BL_ERR_SHAPE
+    assert "2^38" in _err(lib)
+    assert f(A_ODD, 16, 64, A16, A16, None) == BL_ERR_ALIGN
+    assert f(A16, 16, 64, A16 + 8, A16, None) == BL_ERR_ALIGN
+    assert f(A16, 16, 64, A16, A16 + 2, None) == BL_ERR_ALIGN
 
 
 def test_quant_errors(lib):
