@@ -20,9 +20,11 @@ from .bitlinear_ref import (  # noqa: F401
 )
 from .subln_ref import (  # noqa: F401
     EPS_N,
+    normalise,
     rms_factor,
     subln_plain,
     subln_quant_act,
+    sum_squares,
 )
 from .ffn_ref import (  # noqa: F401
     bf16_rne,

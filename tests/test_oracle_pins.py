@@ -7,6 +7,7 @@ per-matrix scale, a transposed or truncated contraction, ...) and checks that
 at least one pin fails, so each pin set is shown to be able to see it.
 """
 
+import math
 import types
 
 import numpy as np
@@ -149,24 +150,56 @@ def _rescale_no_floor(acc, gamma, absmax):
     return np.asarray(acc, np.float64) * np.float64(gamma) * m[:, None] / 127.0
 
 
-def _subln(x, gain, eps_n=oracle.EPS_N, *, use_gain=True, rms_of="x", eps=True, scale_op="mul",
-           gain_in_codes=True, mean_abs=False):
+def _subln(x, gain, eps_n=oracle.EPS_N, *, use_gain=True, rms_of="x", eps=True, sum_mode="exact",
+           r_mode="steps", order="gain_first", codes_of_u=False, scale_of_u=False, mean_abs=False):
     x = np.asarray(x)
     if x.dtype == np.uint16:
         x = oracle.widen_bf16(x)
     x = np.asarray(x, np.float32)
     g = np.asarray(gain, np.float32)
+    k = x.shape[1]
     u = x * g[None, :] if use_gain else x
-    q, a, rowsum = oracle.quant_act(u if gain_in_codes else x)
-    if not gain_in_codes:
-        a = np.max(np.abs(u), axis=1).astype(np.float32)
     src = (u if rms_of == "u" else x).astype(np.float64)
-    ms = np.mean(np.abs(src), axis=1) if mean_abs else np.mean(src * src, axis=1)
-    r = 1.0 / (ms + (eps_n if eps else 0.0)) if mean_abs else 1.0 / np.sqrt(ms + (eps_n if eps else 0.0))
+    sq = np.abs(src) if mean_abs else src * src
+    if sum_mode == "exact":
+        s = np.array([math.fsum(row.tolist()) for row in sq])
+    elif sum_mode == "seq":
+        s = np.zeros(x.shape[0])
+        for j in range(k):
+            s = s + sq[:, j]
+    elif sum_mode == "np":
+        s = np.sum(sq, axis=1)
+    else:                                    # a binary32 running sum
+        s32 = np.zeros(x.shape[0], np.float32)
+        for j in range(k):
+            s32 = s32 + sq[:, j].astype(np.float32)
+        s = s32.astype(np.float64)
+    ms64 = s / k
+    e = np.float32(eps_n) if eps else np.float32(0.0)
     with np.errstate(all="ignore"):
-        scale = a.astype(np.float64) * r if scale_op == "mul" else (
-            a.astype(np.float64) / r if scale_op == "div" else a.astype(np.float64))
-    return q, scale, rowsum, a
+        if r_mode == "f64":
+            r64 = 1.0 / (ms64 + float(e)) if mean_abs else 1.0 / np.sqrt(ms64 + float(e))
+            r = r64.astype(np.float32)
+        elif r_mode == "one_rounding":
+            v = ms64.astype(np.float32) + e
+            r = (1.0 / np.sqrt(v.astype(np.float64))).astype(np.float32)
+        else:
+            v = ms64.astype(np.float32) + e
+            r = np.float32(1.0) / (v if mean_abs else np.sqrt(v))
+    if codes_of_u:
+        # quantise x * g and hand on r * max|x * g| as the scale
+        q, a, rowsum = oracle.quant_act(u)
+        return q, (a.astype(np.float64) * r.astype(np.float64)).astype(np.float32), rowsum, r
+    if r_mode == "f64":
+        xh = (u.astype(np.float64) * r64[:, None]).astype(np.float32)
+    elif order == "gain_first":
+        xh = u * r[:, None]
+    else:
+        xh = (x * r[:, None]) * g[None, :]
+    q, a, rowsum = oracle.quant_act(xh)
+    if scale_of_u:
+        a = np.max(np.abs(u), axis=1).astype(np.float32)
+    return q, a, rowsum, r
 
 
 def _subln_mutant(**kw):
@@ -258,12 +291,17 @@ MUTANTS = {
     "gated_gate_up_swapped": dict(gated_relu2=_gated_mutant(swap=True)),
     "bf16_truncate": dict(bf16_rne=_bf16_trunc),
     "bf16_half_away": dict(bf16_rne=_bf16_half_away),
+    "subln_codes_of_x_times_g": dict(subln_quant_act=_subln_mutant(codes_of_u=True)),
     "subln_no_gain": dict(subln_quant_act=_subln_mutant(use_gain=False)),
     "subln_rms_of_x_times_g": dict(subln_quant_act=_subln_mutant(rms_of="u")),
     "subln_no_eps": dict(subln_quant_act=_subln_mutant(eps=False)),
-    "subln_scale_without_rms": dict(subln_quant_act=_subln_mutant(scale_op="none")),
-    "subln_scale_divided_by_rms": dict(subln_quant_act=_subln_mutant(scale_op="div")),
-    "subln_gain_only_in_scale": dict(subln_quant_act=_subln_mutant(gain_in_codes=False)),
+    "subln_sum_running_binary64": dict(subln_quant_act=_subln_mutant(sum_mode="seq")),
+    "subln_sum_numpy_pairwise": dict(subln_quant_act=_subln_mutant(sum_mode="np")),
+    "subln_sum_binary32": dict(subln_quant_act=_subln_mutant(sum_mode="f32")),
+    "subln_r_in_binary64": dict(subln_quant_act=_subln_mutant(r_mode="f64")),
+    "subln_r_one_rounding": dict(subln_quant_act=_subln_mutant(r_mode="one_rounding")),
+    "subln_norm_before_gain": dict(subln_quant_act=_subln_mutant(order="norm_first")),
+    "subln_scale_is_max_x_times_g": dict(subln_quant_act=_subln_mutant(scale_of_u=True)),
     "subln_mean_abs_not_rms": dict(subln_quant_act=_subln_mutant(mean_abs=True)),
     "gamma_per_row": dict(absmean_gamma=_per_row_gamma),
     "gamma_f32_running_sum": dict(absmean_gamma=_f32_sum_gamma),
