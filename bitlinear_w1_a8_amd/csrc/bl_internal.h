@@ -162,11 +162,79 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));   // lgkmcnt, expcnt: no wait
 }
 
+// Exact non-negative integers in L little-endian 32-bit limbs (the exact
+// sums of gamma and of the SubLN squares), used by one thread.
+//
+// limbs_add: add v * 2^off (off >= 0); the caller guarantees that the sum fits.
+template <int L>
+__device__ __forceinline__ void limbs_add(uint32_t (&limb)[L], unsigned long long v, int off) {
+  if (!v) return;
+  const int l0 = off >> 5, o = off & 31;
+  const unsigned long long lo = v << o;
+  const uint32_t part[3] = {(uint32_t)lo, (uint32_t)(lo >> 32), o ? (uint32_t)(v >> (64 - o)) : 0u};
+  unsigned long long carry = 0;
+  for (int i = l0; i < L; ++i) {
+    const int pi = i - l0;
+    const unsigned long long s = (unsigned long long)limb[i] + carry + (pi < 3 ? part[pi] : 0u);
+    limb[i] = (uint32_t)s;
+    carry = s >> 32;
+    if (pi >= 2 && !carry) break;
+  }
+}
+
+// limbs_to_f64: the integer times 2^scale, rounded once to binary64 (nearest,
+// ties to even); the result must lie in the normal binary64 range or be 0.
+template <int L>
+__device__ __forceinline__ double limbs_to_f64(const uint32_t (&limb)[L], int scale) {
+  int top = -1;
+  for (int i = L - 1; i >= 0 && top < 0; --i)
+    if (limb[i]) top = i * 32 + (31 - __builtin_clz(limb[i]));
+  if (top < 0) return 0.0;
+  if (top <= 52) {
+    const unsigned long long x = ((unsigned long long)limb[1] << 32) | limb[0];
+    return ldexp((double)x, scale);
+  }
+  auto bit = [&](int i) -> uint32_t { return (limb[i >> 5] >> (i & 31)) & 1u; };
+  unsigned long long m = 0;
+  for (int i = top; i >= top - 52; --i) m = (m << 1) | bit(i);
+  const uint32_t rnd = bit(top - 53);
+  uint32_t sticky = 0;
+  for (int i = top - 54; i >= 0 && !sticky; --i) sticky |= bit(i);
+  int e = top - 52;
+  if (rnd && (sticky || (m & 1ull))) {
+    ++m;
+    if (m == (1ull << 53)) { m >>= 1; ++e; }
+  }
+  return ldexp((double)m, e + scale);
+}
+
+// gamma * max(absmax, eps), exact in binary64 (two 24-bit significands).
+__device__ __forceinline__ double gamma_m(float gamma, float absmax) {
+  return (double)gamma * (double)fmaxf(absmax, kEps);
+}
+
+// Step A3 in binary64, rounded to binary32: RN32(RN64(RN64(acc * gamma * m) / 127)),
+// the oracle's rescale of the sum, with gm = gamma * m from gamma_m.  acc * gm
+// is one rounding of the exact product (acc * gamma is exact in binary64).
+// The division by 127 is a product with RN64(1/127), then a correction by
+// the exact remainder (one fused multiply-add), which is correctly rounded
+// here: t / 127 of a 53-bit t is never a binary64 midpoint and lies at least
+// ulp/254 from one, far more than the error of the corrected quotient.
+__device__ __forceinline__ float a3_f32(int acc, double gm) {
+  constexpr double kInv = 1.0 / 127.0;          // RN64(1/127)
+  const double t = (double)acc * gm;
+  const double q0 = t * kInv;
+  const double rem = fma(-q0, 127.0, t);        // exact: q0 is within one ulp of t / 127
+  return (float)fma(rem, kInv, q0);
+}
+
 // Gated ReLU^2 of one output pair, rounded to bfloat16 (nearest, ties to
-// even): g = acc_g * sg and u = acc_u * su (binary32), h = (max(g, 0)^2) * u
-// with the two products in that order.
-__device__ __forceinline__ uint16_t gated_relu2_bf16(int acc_g, int acc_u, float sg, float su) {
-  const float g = (float)acc_g * sg, u = (float)acc_u * su;
+// even): g and u are the binary32 roundings of step A3's binary64 value
+// (a3_f32, gm_g and gm_u from gamma_m), h = (max(g, 0)^2) * u with the two
+// binary32 products in that order.
+__device__ __forceinline__ uint16_t gated_relu2_bf16(int acc_g, int acc_u, double gm_g,
+                                                     double gm_u) {
+  const float g = a3_f32(acc_g, gm_g), u = a3_f32(acc_u, gm_u);
   const float r = fmaxf(g, 0.0f);
   const float h = (r * r) * u;
   uint32_t b = __float_as_uint(h);

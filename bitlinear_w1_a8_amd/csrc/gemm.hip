@@ -288,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   __shared__ __align__(16) unsigned char B2[STAGES > 2 ? kBBuf : 16];
   __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
   __shared__ float scale[BM];
-  __shared__ float scale2[GATED ? BM : 1];
+  __shared__ double gm_gate[GATED ? BM : 1], gm_up[GATED ? BM : 1];   // gamma * m, binary64
   __shared__ int rsum[BM];   // each token's sum of q over the block's K range
   auto abuf = [&](auto st) -> unsigned char* {
     constexpr int S = decltype(st)::value;
@@ -335,15 +335,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   // per-token output scale first: its loads retire before the pipeline starts
   {
     const float g = gamma[0];
-    for (int r = tid; r < BM; r += NT) {
-      const int tok = m0 + r;
-      scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
-    }
     if constexpr (GATED) {
       const float g2 = gamma2[0];
       for (int r = tid; r < BM; r += NT) {
         const int tok = m0 + r;
-        scale2[r] = tok < T ? out_scale(g2, absmax[tok]) : 0.0f;
+        const float a = tok < T ? absmax[tok] : 0.0f;
+        gm_gate[r] = gamma_m(g, a);
+        gm_up[r] = gamma_m(g2, a);
+      }
+    } else {
+      for (int r = tid; r < BM; r += NT) {
+        const int tok = m0 + r;
+        scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
       }
     }
   }
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 32 * WMF + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
         const int tok = m0 + r;
-        const float sg = scale[r], su = scale2[r];
+        const double gg = gm_gate[r], gu = gm_up[r];
         const int qs = rsum[r];
 #pragma unroll
         for (int j = 0; j < WNF; ++j) {
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
           const int64_t o = (int64_t)tok * N + n;
           if (acc_out) acc_out[o] = sv;
           if ((m & 1) == 0)
-            h_out[(int64_t)tok * half + (n >> 1)] = gated_relu2_bf16(sv, other, sg, su);
+            h_out[(int64_t)tok * half + (n >> 1)] = gated_relu2_bf16(sv, other, gg, gu);
         }
       }
     }

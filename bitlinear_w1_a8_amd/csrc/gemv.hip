@@ -175,7 +175,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
         acc_out[o + 1] = su;
       }
       const float a = absmax[tl];
-      h[(int64_t)tl * half + (n >> 1)] = gated_relu2_bf16(sg, su, out_scale(g, a), out_scale(g2, a));
+      h[(int64_t)tl * half + (n >> 1)] = gated_relu2_bf16(sg, su, gamma_m(g, a), gamma_m(g2, a));
     }
     return;
   }
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
       if constexpr (MODE == kInt8) a = idx < 64 ? am : pr.absmax[tl];
       else a = __uint_as_float((uint32_t)amax[tl]);
       pr.h[(int64_t)tl * half + (nn >> 1)] =
-          gated_relu2_bf16(sg, su, out_scale(g, a), out_scale(g2, a));
+          gated_relu2_bf16(sg, su, gamma_m(g, a), gamma_m(g2, a));
     }
     return;
   }

@@ -77,46 +77,8 @@ __global__ void k_gamma_finalize(const unsigned long long* __restrict__ buckets,
   constexpr int kLimbs = 12;  // 384 bits > 253 + 64 + 8
   uint32_t limb[kLimbs];
   for (int i = 0; i < kLimbs; ++i) limb[i] = 0;
-  for (int b = 1; b < 255; ++b) {
-    const unsigned long long v = buckets[b];
-    if (!v) continue;
-    const int sh = b - 1;          // value = v * 2^(b-1) * 2^-149
-    const int l0 = sh >> 5, o = sh & 31;
-    const unsigned long long lo = v << o;
-    const uint32_t part[3] = {(uint32_t)lo, (uint32_t)(lo >> 32),
-                              o ? (uint32_t)(v >> (64 - o)) : 0u};
-    unsigned long long carry = 0;
-    for (int i = l0; i < kLimbs; ++i) {
-      const int pi = i - l0;
-      unsigned long long s = (unsigned long long)limb[i] + carry + (pi < 3 ? part[pi] : 0u);
-      limb[i] = (uint32_t)s;
-      carry = s >> 32;
-      if (pi >= 2 && !carry) break;
-    }
-  }
-  int top = -1;
-  for (int i = kLimbs - 1; i >= 0 && top < 0; --i)
-    if (limb[i]) top = i * 32 + (31 - __builtin_clz(limb[i]));
-  double sum;
-  if (top < 0) {
-    sum = 0.0;
-  } else if (top <= 52) {
-    const unsigned long long x = ((unsigned long long)limb[1] << 32) | limb[0];
-    sum = ldexp((double)x, -149);
-  } else {
-    auto bit = [&](int i) -> uint32_t { return (limb[i >> 5] >> (i & 31)) & 1u; };
-    unsigned long long m = 0;
-    for (int i = top; i >= top - 52; --i) m = (m << 1) | bit(i);
-    const uint32_t rnd = bit(top - 53);
-    uint32_t sticky = 0;
-    for (int i = top - 54; i >= 0 && !sticky; --i) sticky |= bit(i);
-    int e = top - 52;
-    if (rnd && (sticky || (m & 1ull))) {
-      ++m;
-      if (m == (1ull << 53)) { m >>= 1; ++e; }
-    }
-    sum = ldexp((double)m, e - 149);
-  }
+  for (int b = 1; b < 255; ++b) limbs_add(limb, buckets[b], b - 1);  // v * 2^(b-1) * 2^-149
+  const double sum = limbs_to_f64(limb, -149);
   const double mean = sum / (double)count;
   gamma[0] = (float)mean;
 }

@@ -10,13 +10,10 @@
 // operations inside each wave and across waves through LDS, and the same
 // registers are then scaled, rounded, clipped and stored as int8.
 //
-// With the sub-layer norm in front (SubLN, read as an RMS norm with a
+// The sub-layer norm in front of it (SubLN, read as an RMS norm with a
 // per-feature gain g and no bias: 2B4T report section 2, the explainer's
-// component table): the per-token absmax scale cancels the per-token RMS
-// factor r = 1 / sqrt(mean(x^2) + eps_n), so the codes are those of
-// u = x * g (one binary32 product per element) and the token's scale handed
-// to the rescale is r * max|u|.  The sum of squares is taken in binary64,
-// where every x^2 is exact.
+// component table) runs in its own kernel, k_subln_quant: normalise, then
+// quantise the normalised row, with the sum of squares taken exactly.
 #include "bl_internal.h"
 
 namespace bl {
@@ -79,29 +76,27 @@ template <> struct In<1> {
   }
 };
 
-// Elements e of a 16-byte vector, widened exactly to binary32, times the gain
-// (the sub-layer norm) or as they are.
-template <int BF16, bool NORM>
-__device__ __forceinline__ void elems(const uint4& v, const float* g, float (&f)[In<BF16>::E]) {
+// Elements of a 16-byte vector, widened exactly to binary32.
+template <int BF16>
+__device__ __forceinline__ void elems(const uint4& v, float (&f)[In<BF16>::E]) {
 #pragma unroll
   for (int e = 0; e < In<BF16>::E; ++e) f[e] = In<BF16>::get(v, e);
-  if constexpr (NORM) {
-    const float4* g4 = reinterpret_cast<const float4*>(g);
-#pragma unroll
-    for (int w = 0; w < In<BF16>::E / 4; ++w) {
-      const float4 gv = g4[w];
-      f[4 * w] *= gv.x;
-      f[4 * w + 1] *= gv.y;
-      f[4 * w + 2] *= gv.z;
-      f[4 * w + 3] *= gv.w;
-    }
-  }
 }
 
-__device__ __forceinline__ double vec_sumsq(const float* f, int n) {
-  double s = 0.0;
-  for (int e = 0; e < n; ++e) s += (double)f[e] * (double)f[e];
-  return s;
+// The same elements times the gain (one binary32 product each): u = x * g.
+template <int BF16>
+__device__ __forceinline__ void elems_gain(const uint4& v, const float* g,
+                                           float (&f)[In<BF16>::E]) {
+  elems<BF16>(v, f);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+#pragma unroll
+  for (int w = 0; w < In<BF16>::E / 4; ++w) {
+    const float4 gv = g4[w];
+    f[4 * w] *= gv.x;
+    f[4 * w + 1] *= gv.y;
+    f[4 * w + 2] *= gv.z;
+    f[4 * w + 3] *= gv.w;
+  }
 }
 
 __device__ __forceinline__ int quant1(float x, float s) {
@@ -109,12 +104,9 @@ __device__ __forceinline__ int quant1(float x, float s) {
   return (int)fminf(fmaxf(rintf(v), -kQb), kQb);
 }
 
-template <int BF16, bool NORM>
-__device__ __forceinline__ void quant_store(const uint4& v, const float* g, float s, int8_t* dst,
-                                            int& sum) {
-  constexpr int E = In<BF16>::E;
-  float f[E];
-  elems<BF16, NORM>(v, g, f);
+// Codes of E values, stored as E bytes at dst (8-byte or 4-byte aligned).
+template <int E>
+__device__ __forceinline__ void quant_store_f(const float (&f)[E], float s, int8_t* dst, int& sum) {
   uint32_t out[E / 4];
 #pragma unroll
   for (int w = 0; w < E / 4; ++w) {
@@ -134,38 +126,38 @@ __device__ __forceinline__ void quant_store(const uint4& v, const float* g, floa
   }
 }
 
-// absmax bits of the vector's elements (times the gain); with the norm, also
-// adds the squares of the raw elements to ss
-template <int BF16, bool NORM>
-__device__ __forceinline__ int vec_absmax_bits(const uint4& v, const float* g, double& ss) {
-  constexpr int E = In<BF16>::E;
-  float f[E];
-  elems<BF16, false>(v, g, f);
-  if constexpr (NORM) ss += vec_sumsq(f, E);
-  elems<BF16, NORM>(v, g, f);
+template <int BF16>
+__device__ __forceinline__ void quant_store(const uint4& v, float s, int8_t* dst, int& sum) {
+  float f[In<BF16>::E];
+  elems<BF16>(v, f);
+  quant_store_f(f, s, dst, sum);
+}
+
+// Largest |f| of the E values as a binary32 bit pattern (non-negative
+// patterns order like their values).
+template <int E>
+__device__ __forceinline__ int absmax_bits(const float (&f)[E]) {
   int m = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) m = max(m, (int)(__float_as_uint(f[i]) & 0x7fffffffu));
-  return m;  // non-negative binary32 bit patterns order like their values
+  return m;
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+template <int BF16>
+__device__ __forceinline__ int vec_absmax_bits(const uint4& v) {
+  float f[In<BF16>::E];
+  elems<BF16>(v, f);
+  return absmax_bits(f);
 }
 
-template <int BF16, bool NORM>
+template <int BF16>
 __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x, int k,
                                                     int8_t* __restrict__ xq,
                                                     float* __restrict__ absmax,
-                                                    int32_t* __restrict__ rowsum,
-                                                    const float* __restrict__ gain,
-                                                    float eps_n) {
+                                                    int32_t* __restrict__ rowsum) {
   constexpr int E = In<BF16>::E;
   __shared__ int red[kMaxWaves];
   __shared__ int red2[kMaxWaves];
-  __shared__ double redss[kMaxWaves];
   const int nvec = k / E;
   const int64_t row = blockIdx.x;
   const uint4* xr = x + row * (int64_t)nvec;
@@ -175,24 +167,19 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 
   uint4 v[kMaxVec];
   int m = 0;
-  double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < kMaxVec; ++i) {
     const int idx = tid + i * nthr;
     if (idx < nvec) {
       v[i] = xr[idx];
-      m = max(m, vec_absmax_bits<BF16, NORM>(v[i], gain + idx * E, ss));
+      m = max(m, vec_absmax_bits<BF16>(v[i]));
     }
   }
   for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr)
-    m = max(m, vec_absmax_bits<BF16, NORM>(xr[idx], gain + idx * E, ss));
+    m = max(m, vec_absmax_bits<BF16>(xr[idx]));
 
   m = wave_max_u(m);
   if (lane == 0) red[wave] = m;
-  if constexpr (NORM) {
-    ss = wave_sum_f64(ss);
-    if (lane == 0) redss[wave] = ss;
-  }
   __syncthreads();
   int mb = red[0];
   for (int wv = 1; wv < nwaves; ++wv) mb = max(mb, red[wv]);
@@ -203,10 +190,10 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < kMaxVec; ++i) {
     const int idx = tid + i * nthr;
-    if (idx < nvec) quant_store<BF16, NORM>(v[i], gain + idx * E, s, qr + (int64_t)idx * E, sum);
+    if (idx < nvec) quant_store<BF16>(v[i], s, qr + (int64_t)idx * E, sum);
   }
   for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr)
-    quant_store<BF16, NORM>(xr[idx], gain + idx * E, s, qr + (int64_t)idx * E, sum);
+    quant_store<BF16>(xr[idx], s, qr + (int64_t)idx * E, sum);
 
   if (rowsum) {
     sum = wave_sum(sum);
@@ -218,55 +205,273 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
       rowsum[row] = t;
     }
   }
+  if (tid == 0) absmax[row] = a;
+}
+
+// ------------------------------------------------------------------ SubLN + A1
+//
+// Per token: S = sum_k x^2 exactly (rounded once to binary64), ms =
+// RN32(RN64(S / K)), r = RN32(1 / RN32(sqrt(RN32(ms + eps_n)))), x_hat =
+// RN32(RN32(x * g) * r), then step A1 on x_hat; scale[t] = max |x_hat|.
+//
+// The exact sum: with x = m * 2^(e-150) (24-bit m; e = 1 and no hidden bit
+// for subnormals), x^2 = m^2 * 2^(2e-300) with m^2 < 2^48.  Each wave takes
+// the exponent E of its largest |x| and adds m^2 << (2(e - E) + 62) into a
+// 128-bit integer per lane (no carry-out: fewer than 2^17 terms of < 2^110).
+// That is exact for every element within 31 binades of the wave's largest;
+// a smaller one (none in ordinary data) sets a flag, and then the block
+// sums those elements into per-exponent LDS buckets instead.  One thread
+// adds the waves' 128-bit sums and the buckets into a 576-bit integer in
+// units of 2^-298 and rounds it once to binary64.
+//
+// max |x_hat| is RN32(max |u| * r): rounding is monotonic, so the largest
+// |u| gives the largest |x_hat|.
+
+constexpr int kSqShift = 62;       // bit of m^2 for an element at the wave's exponent
+constexpr int kSqLimbs = 18;       // 576 bits: sums below 2^17 * 2^256 in units of 2^-298
+
+struct U128 {
+  unsigned long long lo, hi;
+};
+
+__device__ __forceinline__ void u128_add(U128& a, unsigned long long lo, unsigned long long hi) {
+  const unsigned long long l = a.lo + lo;
+  a.hi += hi + (l < lo ? 1ull : 0ull);
+  a.lo = l;
+}
+
+// Significand and effective exponent of |x| (subnormals: e = 1, no hidden bit).
+__device__ __forceinline__ void split_f32(float x, uint32_t& m, int& e) {
+  const uint32_t b = __float_as_uint(x) & 0x7fffffffu;
+  e = (int)(b >> 23);
+  m = b & 0x7fffffu;
+  if (e) m |= 0x800000u; else e = 1;
+}
+
+// Adds x^2 to the lane's sum at the wave's exponent ew; returns false (and
+// adds nothing) for an element too small for the 128-bit window.
+__device__ __forceinline__ bool add_square(U128& acc, float x, int ew) {
+  uint32_t m;
+  int e;
+  split_f32(x, m, e);
+  if (!m) return true;
+  const int sh = 2 * (e - ew) + kSqShift;
+  if (sh < 0) return false;
+  const unsigned long long sq = (unsigned long long)m * m;
+  u128_add(acc, sq << sh, (sq >> 1) >> (63 - sh));
+  return true;
+}
+
+__device__ __forceinline__ U128 wave_sum_u128(U128 a) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long lo = __shfl_xor(a.lo, o), hi = __shfl_xor(a.hi, o);
+    u128_add(a, lo, hi);
+  }
+  return a;
+}
+
+template <int BF16>
+__global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ x, int k,
+                                                      const float* __restrict__ gain,
+                                                      float eps_n, int8_t* __restrict__ xq,
+                                                      float* __restrict__ scale,
+                                                      int32_t* __restrict__ rowsum) {
+  constexpr int E = In<BF16>::E;
+  __shared__ unsigned long long red_lo[kMaxWaves], red_hi[kMaxWaves];
+  __shared__ int red_e[kMaxWaves], red_umax[kMaxWaves], red_far[kMaxWaves], red2[kMaxWaves];
+  __shared__ float sh_r, sh_s;
+  __shared__ unsigned long long far_hist[2][256];   // buckets of the small elements (rare)
+  const int nvec = k / E;
+  const int64_t row = blockIdx.x;
+  const uint4* xr = x + row * (int64_t)nvec;
+  int8_t* qr = xq + row * (int64_t)k;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+
+  // 1. the row in registers; largest |x| and |u| = |x * g|
+  uint4 v[kMaxVec];
+  int mx = 0, mu = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int idx = tid + i * nthr;
+    if (idx < nvec) {
+      v[i] = xr[idx];
+      float f[E];
+      elems<BF16>(v[i], f);
+      mx = max(mx, absmax_bits(f));
+      elems_gain<BF16>(v[i], gain + idx * E, f);
+      mu = max(mu, absmax_bits(f));
+    }
+  }
+  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+    float f[E];
+    elems<BF16>(xr[idx], f);
+    mx = max(mx, absmax_bits(f));
+    elems_gain<BF16>(xr[idx], gain + idx * E, f);
+    mu = max(mu, absmax_bits(f));
+  }
+  const int ew = max(wave_max_u(mx) >> 23, 1);   // exponent of the wave's largest |x|
+  mu = wave_max_u(mu);
+
+  // 2. exact sum of squares, per lane at the wave's exponent
+  U128 acc = {0ull, 0ull};
+  bool fits = true;
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int idx = tid + i * nthr;
+    if (idx < nvec) {
+      float f[E];
+      elems<BF16>(v[i], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) fits &= add_square(acc, f[e], ew);
+    }
+  }
+  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+    float f[E];
+    elems<BF16>(xr[idx], f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) fits &= add_square(acc, f[e], ew);
+  }
+  acc = wave_sum_u128(acc);
+  const bool wave_far = __ballot(!fits) != 0;
+  if (lane == 0) {
+    red_lo[wave] = acc.lo;
+    red_hi[wave] = acc.hi;
+    red_e[wave] = ew;
+    red_umax[wave] = mu;
+    red_far[wave] = wave_far;
+  }
+  __syncthreads();
+  bool far = false;
+  for (int wv = 0; wv < nwaves; ++wv) far |= red_far[wv] != 0;
+
+  if (far) {   // block-uniform: some element lay more than 31 binades below its wave's largest
+    for (int j = tid; j < 512; j += nthr) (&far_hist[0][0])[j] = 0ull;
+    __syncthreads();
+    // the same elements per thread as above, read again (this path is rare)
+    for (int idx = tid; idx < nvec; idx += nthr) {
+      float f[E];
+      elems<BF16>(xr[idx], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        uint32_t m;
+        int ex;
+        split_f32(f[e], m, ex);
+        if (m && 2 * (ex - ew) + kSqShift < 0) {
+          const unsigned long long sq = (unsigned long long)m * m;
+          atomicAdd(&far_hist[0][ex], sq >> 24);
+          atomicAdd(&far_hist[1][ex], sq & 0xffffffull);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. one thread: the exact sum, r, the absmax of x_hat and the step-A1 scale
   if (tid == 0) {
-    if constexpr (NORM) {
-      double t = redss[0];
-      for (int wv = 1; wv < nwaves; ++wv) t += redss[wv];
-      const double r = 1.0 / sqrt(t / (double)k + (double)eps_n);
-      absmax[row] = (float)((double)a * r);
-    } else {
-      absmax[row] = a;
+    uint32_t limb[kSqLimbs];
+    for (int i = 0; i < kSqLimbs; ++i) limb[i] = 0;
+    int um = 0;
+    for (int wv = 0; wv < nwaves; ++wv) {
+      // the wave's sum is in units of 2^(2 ew - 362) = 2^(2 ew - 64) * 2^-298
+      unsigned long long lo = red_lo[wv], hi = red_hi[wv];
+      const int off = 2 * red_e[wv] - 64;
+      if (off < 0) {     // exact: every term's lowest set bit is at or above -off
+        const int sft = -off;
+        lo = (lo >> sft) | (hi << (64 - sft));
+        hi >>= sft;
+        limbs_add(limb, lo, 0);
+        limbs_add(limb, hi, 64);
+      } else {
+        limbs_add(limb, lo, off);
+        limbs_add(limb, hi, off + 64);
+      }
+      um = max(um, red_umax[wv]);
+    }
+    if (far) {
+      for (int ex = 1; ex < 255; ++ex) {   // m^2 = hi * 2^24 + lo, at 2^(2 ex - 300)
+        limbs_add(limb, far_hist[0][ex], 2 * ex + 22);
+        limbs_add(limb, far_hist[1][ex], 2 * ex - 2);
+      }
+    }
+    const double ssum = limbs_to_f64(limb, -298);
+    const float ms = (float)(ssum / (double)k);   // binary64 mean, one rounding to binary32
+    const float root = sqrtf(ms + eps_n);          // binary32 add; correctly rounded root
+    const float r = 1.0f / root;                   // IEEE binary32 division
+    const float a = __uint_as_float((uint32_t)um) * r;   // = max |x_hat|
+    sh_r = r;
+    sh_s = kQb / fmaxf(a, kEps);
+    scale[row] = a;
+  }
+  __syncthreads();
+  const float r = sh_r, s = sh_s;
+
+  // 4. x_hat = RN32(u * r), quantised with step A1's scale
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int idx = tid + i * nthr;
+    if (idx < nvec) {
+      float f[E];
+      elems_gain<BF16>(v[i], gain + idx * E, f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] *= r;
+      quant_store_f(f, s, qr + (int64_t)idx * E, sum);
+    }
+  }
+  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+    float f[E];
+    elems_gain<BF16>(xr[idx], gain + idx * E, f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] *= r;
+    quant_store_f(f, s, qr + (int64_t)idx * E, sum);
+  }
+  if (rowsum) {
+    sum = wave_sum(sum);
+    if (lane == 0) red2[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int wv = 0; wv < nwaves; ++wv) t += red2[wv];
+      rowsum[row] = t;
     }
   }
 }
 
-hipError_t launch_quant_impl(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
-                             float* absmax, int32_t* rowsum, const float* gain, float eps_n,
-                             hipStream_t stream) {
-  const int e = bf16 ? 8 : 4;
+// Enough threads that each holds at most kMaxVec vectors, in whole waves.
+dim3 row_block(int64_t k, int e) {
   const int64_t nvec = k / e;
-  // enough threads that each holds at most kMaxVec vectors, in whole waves
   int64_t thr = (nvec + kMaxVec - 1) / kMaxVec;
   thr = ((thr + 63) / 64) * 64;
   if (thr < 64) thr = 64;
   if (thr > 64 * kMaxWaves) thr = 64 * kMaxWaves;
-  const dim3 grid((unsigned)t), block((unsigned)thr);
-  const uint4* xv = static_cast<const uint4*>(x);
-  if (gain) {
-    if (bf16)
-      k_act_quant<1, true><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum, gain, eps_n);
-    else
-      k_act_quant<0, true><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum, gain, eps_n);
-  } else {
-    if (bf16)
-      k_act_quant<1, false><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum, gain, eps_n);
-    else
-      k_act_quant<0, false><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum, gain, eps_n);
-  }
-  return hipGetLastError();
+  return dim3((unsigned)thr);
 }
 
 }  // namespace
 
 hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
                         float* absmax, int32_t* rowsum, hipStream_t stream) {
-  return launch_quant_impl(x, bf16, t, k, xq, absmax, rowsum, nullptr, 0.0f, stream);
+  const dim3 grid((unsigned)t), block = row_block(k, bf16 ? 8 : 4);
+  const uint4* xv = static_cast<const uint4*>(x);
+  if (bf16)
+    k_act_quant<1><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum);
+  else
+    k_act_quant<0><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum);
+  return hipGetLastError();
 }
 
 hipError_t launch_subln_quant(const void* x, int bf16, const float* gain, float eps_n, int64_t t,
                               int64_t k, int8_t* xq, float* scale, int32_t* rowsum,
                               hipStream_t stream) {
-  return launch_quant_impl(x, bf16, t, k, xq, scale, rowsum, gain, eps_n, stream);
+  const dim3 grid((unsigned)t), block = row_block(k, bf16 ? 8 : 4);
+  const uint4* xv = static_cast<const uint4*>(x);
+  if (bf16)
+    k_subln_quant<1><<<grid, block, 0, stream>>>(xv, (int)k, gain, eps_n, xq, scale, rowsum);
+  else
+    k_subln_quant<0><<<grid, block, 0, stream>>>(xv, (int)k, gain, eps_n, xq, scale, rowsum);
+  return hipGetLastError();
 }
 
 }  // namespace bl

@@ -47,6 +47,9 @@
  *   binary64 and rounded to binary32, so it does not depend on any order.
  * - y = acc * gamma * max(absmax, eps) / 127, computed in binary32 (within
  *   1e-5 relative of the binary64 value; y is +0 exactly where acc is 0).
+ *   Where a later binary32 step depends on y's bits (the gated ReLU^2 below),
+ *   y is instead the binary64 value ((acc * gamma) * m) / 127, one rounding
+ *   per operation, rounded to binary32.
  *
  * Packed weight layout (the pages fix only "four weights per byte"):
  *   code c = t + 1 in {0, 1, 2} (3 never occurs).  Row n of the N x K matrix
@@ -165,15 +168,17 @@ int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t
  * (section 2) puts subln before the quantised projections and drops every
  * bias; the explainer's component table lists it in place of RMSNorm /
  * LayerNorm.  No page gives its formula; it is taken here as an RMS norm with
- * a per-feature gain g and no bias:
- *   x_hat[t,k] = x[t,k] * g[k] / sqrt(mean_k x[t,k]^2 + eps_n).
- * Per-token absmax quantisation cancels the positive per-token factor
- * r = 1 / sqrt(mean_k x^2 + eps_n), so the result is step A1 applied to
- * u = x * g (one binary32 product per element), with the token's scale
- * r * max_k |u| in place of the absmax:
- *   xq[t,k]  = clamp(round_half_even(u * (127 / max(max|u|, eps))), -127, 127),
- *   scale[t] = r * max_k |u[t,k]|  (sum of squares in binary64; binary32 out).
- * scale takes the place of absmax in bitlinear_forward.
+ * a per-feature gain g and no bias, applied first, its output then quantised
+ * by step A1.  Per token, in this order and precision:
+ *   S        = sum_k x[t,k]^2, exact, rounded once to binary64 (no order of
+ *              summation matters),
+ *   ms       = RN32(RN64(S / K)),
+ *   r        = RN32(1 / RN32(sqrt(RN32(ms + eps_n)))),
+ *   x_hat    = RN32(RN32(x * g) * r),
+ *   scale[t] = max_k |x_hat[t,k]|  (exact),
+ *   xq[t,k]  = clamp(round_half_even(x_hat * RN32(127 / max(scale, eps))), -127, 127).
+ * scale takes the place of absmax in bitlinear_forward.  Rows whose mean
+ * square exceeds the binary32 range are outside the domain.
  *
  *   x        [T, K] activations of dtype x_dtype (BL_F32 or BL_BF16), 16-byte aligned.
  *   gain     [K] float32 per-feature gain (device), 16-byte aligned.
@@ -297,8 +302,9 @@ int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int
  * squared-ReLU activation that the 2B4T report (section 2) puts in the
  * feed-forward sublayer, read as a gated unit and written as bfloat16 for the
  * down projection:
- *   g = y_gate[t,n], u = y_up[t,n]  (binary32, exactly as bitlinear_forward
- *       computes them: acc * (gamma * max(absmax, eps) / 127)),
+ *   g, u = step A3 of the gate and up sums in binary64, ((acc * gamma) * m)
+ *       / 127 with m = max(absmax, eps), one rounding per operation, rounded
+ *       to binary32,
  *   h[t,n] = bf16_round_nearest_even((max(g, 0) * max(g, 0)) * u)
  *       (two binary32 products in that order).
  * The activations are quantised once (step A1) and shared by both

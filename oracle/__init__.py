@@ -27,11 +27,10 @@ from .subln_ref import (  # noqa: F401
     sum_squares,
 )
 from .ffn_ref import (  # noqa: F401
+    a3_f32,
     bf16_rne,
     gated_relu2,
     gated_relu2_plain,
-    out_scale_f32,
-    y_f32,
 )
 from .binary_ref import (  # noqa: F401
     binarize,

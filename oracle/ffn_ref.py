@@ -13,36 +13,28 @@ the decode workload).
 Reading (stated): the activation that feeds the down projection is
 h = ReLU(g)^2 * u, with g and u the outputs of the gate and up BitLinear
 layers on the same input, stored as bfloat16 (the activation dtype of the
-workloads).  Because the result is rounded to bfloat16 and must be the same
-bits on every side, the binary32 order of evaluation is part of the
-definition:
+workloads).  g and u are step A3's values as this oracle defines them (the
+binary64 rescale of ``bitlinear_ref.rescale``), rounded once to binary32;
+because h is rounded to bfloat16 and must be the same bits on every side, the
+binary32 order of what follows is part of the definition:
 
-    s_p = RN32(RN32(gamma_p * max(absmax, eps)) / 127)     (p = gate, up)
-    g   = RN32(acc_gate * s_gate),  u = RN32(acc_up * s_up)
-    r   = max(g, 0)
-    h   = bf16_rne(RN32(RN32(r * r) * u))
+    g = RN32(A3(acc_gate)),  u = RN32(A3(acc_up))
+    r = max(g, 0)
+    h = bf16_rne(RN32(RN32(r * r) * u))
 
-(acc are the exact int32 sums, converted exactly to binary32 since
-|acc| < 2^24).  ``gated_relu2_plain`` evaluates ReLU(g)^2 * u in binary64 from
-the binary64 outputs of step A3, for the pins to check the binary32 route.
+``gated_relu2_plain`` evaluates ReLU(g)^2 * u in binary64 from the binary64
+outputs of step A3, for a pin that bounds how far the binary32 route may
+stray from it.
 """
 
 import numpy as np
 
-from .bitlinear_ref import EPS_A, QB, _check_finite
+from .bitlinear_ref import EPS_A, QB, _check_finite, rescale
 
 
-def out_scale_f32(gamma, absmax):
-    """s = RN32(RN32(gamma * max(absmax, eps)) / 127) per token, binary32."""
-    m = np.maximum(np.asarray(absmax, np.float32), EPS_A)
-    return (np.float32(gamma) * m) / np.float32(QB)
-
-
-def y_f32(acc, gamma, absmax):
-    """The binary32 output of step A3: RN32(acc * s)."""
-    acc = np.asarray(acc)
-    assert np.all(np.abs(acc) < 2 ** 24)
-    return acc.astype(np.float32) * out_scale_f32(gamma, absmax)[:, None]
+def a3_f32(acc, gamma, absmax):
+    """Step A3 rounded to binary32: RN32 of the binary64 rescale."""
+    return rescale(acc, gamma, absmax).astype(np.float32)
 
 
 def bf16_rne(x):
@@ -56,8 +48,8 @@ def bf16_rne(x):
 
 def gated_relu2(acc_gate, acc_up, gamma_gate, gamma_up, absmax):
     """h = bf16_rne(RN32(RN32(max(g, 0)^2) * u)) as uint16 bfloat16 bits [T, N]."""
-    g = y_f32(acc_gate, gamma_gate, absmax)
-    u = y_f32(acc_up, gamma_up, absmax)
+    g = a3_f32(acc_gate, gamma_gate, absmax)
+    u = a3_f32(acc_up, gamma_up, absmax)
     _check_finite(g, "gate output")
     _check_finite(u, "up output")
     r = np.maximum(g, np.float32(0))

@@ -545,17 +545,16 @@ def _bf16_torch(v):
 
 
 def _gated_scalar(ag, au, gg, gu, a):
-    # the defined binary32 route, one operation at a time: each step in
-    # binary64 on binary32 operands, rounded once to binary32 (exact for +,
-    # -, *, / since 53 >= 2*24 + 2)
-    r32 = lambda v: float(np.float32(v))
-    m = r32(max(float(np.float32(a)), F32_EPS))
-    sg = r32(r32(float(np.float32(gg)) * m) / 127.0)
-    su = r32(r32(float(np.float32(gu)) * m) / 127.0)
-    g = r32(float(ag) * sg)
-    u = r32(float(au) * su)
-    r = max(g, 0.0)
-    return r32(r32(r * r) * u)
+    # the defined route in exact rationals: g and u are step A3's binary64
+    # evaluation ((acc * gamma) * m) / 127, one rounding per operation,
+    # rounded to binary32; then two binary32 products
+    m = max(Fraction(float(np.float32(a))), Fraction(F32_EPS))
+    def a3(acc, gamma):
+        t = _rn64(_rn64(acc * Fraction(float(np.float32(gamma)))) * m)
+        return _rn32(_rn64(t / 127))
+    g, u = a3(int(ag), gg), a3(int(au), gu)
+    r = max(g, Fraction(0))
+    return float(_rn32(_rn32(r * r) * u))
 
 
 def pin_e7_gated_relu2(o):
@@ -566,12 +565,13 @@ def pin_e7_gated_relu2(o):
 
 
 def pin_gated_route(o):
-    # inputs where the order of the two products and a binary64 output scale
-    # change the bfloat16 bits (found by search); expected values from the
-    # scalar route above and torch's rounding
+    # inputs where a binary32 output scale RN32(RN32(gamma * m) / 127), or
+    # the other order of the two products, changes the bfloat16 bits (found
+    # by search); expected values from the exact-rational route above and
+    # torch's rounding
     gg, gu, a = 0.0173, 0.0291, 3.7
-    ag = np.array([[2483, 2106, 2483, 320, 1280, 1587, 7, 0, 1000]])
-    au = np.array([[-481, 2789, 962, -905, 905, -1840, 5, 100, -1]])
+    ag = np.array([[3962, 9049, 15404, 7127, 8976, 2483, 320, 7, 0, 1000]])
+    au = np.array([[-4705, 8931, 9021, -14946, 2615, -481, -905, 5, 100, -1]])
     h = o.gated_relu2(ag, au, gg, gu, np.array([a], np.float32))
     want = _bf16_torch([_gated_scalar(x, y, gg, gu, a) for x, y in zip(ag[0], au[0])])
     assert np.array_equal(h.ravel(), want)

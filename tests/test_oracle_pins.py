@@ -216,16 +216,19 @@ def _bf16_half_away(x):
 
 
 def _gated(acc_gate, acc_up, gamma_gate, gamma_up, absmax, *, relu=True, square=True, relu_up=False,
-           order="rr_u", scale64=False, rounder=None, swap=False):
+           order="rr_u", scale32=False, rounder=None, swap=False):
     if swap:
         acc_gate, acc_up, gamma_gate, gamma_up = acc_up, acc_gate, gamma_up, gamma_gate
-    if scale64:
-        m = np.maximum(np.asarray(absmax, np.float32), oracle.EPS_A).astype(np.float64)
-        g = (np.asarray(acc_gate, np.float64) * (float(np.float32(gamma_gate)) * m / 127)[:, None]).astype(np.float32)
-        u = (np.asarray(acc_up, np.float64) * (float(np.float32(gamma_up)) * m / 127)[:, None]).astype(np.float32)
+    if scale32:
+        # a binary32 scale RN32(RN32(gamma * m) / 127) applied to the sum
+        m = np.maximum(np.asarray(absmax, np.float32), oracle.EPS_A)
+        sg = (np.float32(gamma_gate) * m) / np.float32(127)
+        su = (np.float32(gamma_up) * m) / np.float32(127)
+        g = np.asarray(acc_gate).astype(np.float32) * sg[:, None]
+        u = np.asarray(acc_up).astype(np.float32) * su[:, None]
     else:
-        g = oracle.y_f32(acc_gate, gamma_gate, absmax)
-        u = oracle.y_f32(acc_up, gamma_up, absmax)
+        g = oracle.a3_f32(acc_gate, gamma_gate, absmax)
+        u = oracle.a3_f32(acc_up, gamma_up, absmax)
     r = np.maximum(g, np.float32(0)) if relu else g
     if relu_up:
         u = np.maximum(u, np.float32(0))
@@ -285,7 +288,7 @@ MUTANTS = {
     "gated_not_squared": dict(gated_relu2=_gated_mutant(square=False)),
     "gated_relu_on_up_too": dict(gated_relu2=_gated_mutant(relu_up=True)),
     "gated_other_product_order": dict(gated_relu2=_gated_mutant(order="r_ru")),
-    "gated_binary64_scale": dict(gated_relu2=_gated_mutant(scale64=True)),
+    "gated_binary32_scale": dict(gated_relu2=_gated_mutant(scale32=True)),
     "gated_bf16_truncate": dict(gated_relu2=_gated_mutant(rounder=_bf16_trunc)),
     "gated_bf16_half_away": dict(gated_relu2=_gated_mutant(rounder=_bf16_half_away)),
     "gated_gate_up_swapped": dict(gated_relu2=_gated_mutant(swap=True)),

@@ -336,20 +336,67 @@ def _subln_inputs(t, k, dtype, seed):
     return x, dev(x), g
 
 
-@pytest.mark.parametrize("t,k,dtype", SUBLN_CASES, ids=[f"T{t}_K{k}_{d}" for t, k, d in SUBLN_CASES])
-def test_subln_quant(bl, t, k, dtype):
-    xref, xin, g = _subln_inputs(t, k, dtype, 900 + t + k)
-    q_ref, scale_ref, rs_ref, a_ref = oracle.subln_quant_act(xref, g)
+def check_subln(bl, xref, xin, g):
+    """Codes, the scale (absmax of x_hat) and row sums, all bit for bit."""
+    q_ref, a_ref, rs_ref, _ = oracle.subln_quant_act(xref, g)
     xq, scale, rowsum = bl.subln_quant_act(xin, dev(g))
     q = host(xq)
     bad = int(np.count_nonzero(q != q_ref))
     assert bad == 0, f"{bad} of {q.size} int8 activations differ"
     assert np.array_equal(host(rowsum), rs_ref)
-    sc = host(scale).astype(np.float64)
-    zero = a_ref == 0
-    assert np.all(sc[zero] == 0.0)
-    rel = np.abs(sc[~zero] - scale_ref[~zero]) / scale_ref[~zero]
-    assert rel.size == 0 or float(rel.max()) <= 2.5e-7, f"scale off by {rel.max():.3g}"
+    sc = host(scale)
+    bad = np.flatnonzero(sc.view(np.uint32) != a_ref.view(np.uint32))
+    assert bad.size == 0, f"scale differs on tokens {bad[:8]}: {sc[bad[:4]]} vs {a_ref[bad[:4]]}"
+    return xq, scale, q_ref, a_ref
+
+
+@pytest.mark.parametrize("t,k,dtype", SUBLN_CASES, ids=[f"T{t}_K{k}_{d}" for t, k, d in SUBLN_CASES])
+def test_subln_quant(bl, t, k, dtype):
+    xref, xin, g = _subln_inputs(t, k, dtype, 900 + t + k)
+    check_subln(bl, xref, xin, g)
+
+
+def _subln_special_rows(k, seed):
+    """Rows that take every branch of the exact sum of squares: elements far
+    below their wave's largest (the per-exponent buckets), a row of
+    subnormals (the sum shifted down), zeros, a constant row, one huge entry
+    among ones, and the worked example's values tiled."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((8, k), np.float32)
+    x[0] = rng.standard_normal(k) * 10.0 ** rng.uniform(-30, 17, k)
+    x[1] = rng.standard_normal(k) * np.float32(1e-39)
+    x[2] = 0.0
+    x[3] = -0.375
+    x[4] = 1.0
+    x[4, k // 3] = np.float32(2.0 ** 60)
+    x[5] = rng.standard_normal(k)
+    x[5, ::37] *= np.float32(1e-13)
+    x[6] = np.tile(np.float32([-1.0, -1.0, 4.0, 2.0]), k // 4)
+    x[7] = rng.standard_normal(k) * np.float32(1e-30)
+    x[7, 5] = np.float32(3e-3)
+    g = (1.0 + 0.5 * rng.standard_normal(k)).astype(np.float32)
+    g[:4] = [1.0, 0.5, 0.25, 0.5]
+    return x, g
+
+
+@pytest.mark.parametrize("k,dtype", [(4096, "f32"), (4096, "bf16"), (64, "f32"), (131072, "f32")],
+                         ids=["K4096_f32", "K4096_bf16", "K64_f32", "K131072_f32"])
+def test_subln_special(bl, k, dtype):
+    x, g = _subln_special_rows(k, 970 + k)
+    if dtype == "bf16":
+        bits = wl.bf16_bits(x)
+        check_subln(bl, bits, dev_bf16(bits), g)
+    else:
+        check_subln(bl, x, dev(x), g)
+
+
+def test_subln_worked_example(bl):
+    # E6: normalising first gives the code -63 where quantising x * g would
+    # give the tie 63.5 -> -64 (K padded to 16 with the same four values)
+    x = np.tile(np.float32([-1.0, -1.0, 4.0, 2.0]), 4)[None, :]
+    g = np.tile(np.float32([1.0, 0.5, 0.25, 0.5]), 4)
+    xq, scale, q_ref, _ = check_subln(bl, x, dev(x), g)
+    assert host(xq)[0, :4].tolist() == [-127, -63, 127, 127]
 
 
 def test_subln_then_forward(bl):
@@ -358,12 +405,11 @@ def test_subln_then_forward(bl):
     packed, gamma, _, gamma_ref = check_pack(bl, w)
     tern = oracle.ternarize(w, gamma_ref)
     xref, xin, g = _subln_inputs(t, k, "bf16", 952)
-    q_ref, scale_ref, _, _ = oracle.subln_quant_act(xref, g)
-    xq, scale, _ = bl.subln_quant_act(xin, dev(g))
+    xq, scale, q_ref, a_ref = check_subln(bl, xref, xin, g)
     y, acc = bl.forward(packed, gamma, xq, scale, n, want_acc=True)
     acc_ref = oracle.contract(q_ref, tern)
     assert np.array_equal(host(acc), acc_ref)
-    check_y(host(y), acc_ref, gamma_ref, scale_ref.astype(np.float32))
+    check_y(host(y), acc_ref, gamma_ref, a_ref)
 
 
 # ------------------------------------------------------------------ grouped A1-A3
@@ -453,7 +499,11 @@ GATED_CASES = [(1, 6912, 2560, "bf16"), (3, 100, 512, "f32"), (4, 37, 256, "bf16
                (70, 64, 320, "f32"), (130, 300, 1040, "bf16"), (300, 500, 2560, "bf16"),
                (1024, 6144, 512, "bf16"), (2, 8200, 8192, "bf16"), (1, 28672, 8192, "bf16"),
                # gated MFMA kernel on 64 x 256 and 128 x 256 tiles
-               (1100, 1900, 512, "bf16"), (256, 14336, 1024, "bf16")]
+               (1100, 1900, 512, "bf16"), (256, 14336, 1024, "bf16"),
+               # two row tiles per block with several tokens: the int8 decode
+               # kernel (T = 8, 864 tiles), the fused one (T = 3, 2 * 2100
+               # rows), the 64-token kernel (T = 32)
+               (8, 6912, 2560, "bf16"), (3, 2100, 1024, "f32"), (32, 2100, 512, "bf16")]
 
 
 def _gated_inputs(bl, t, n, k, dtype, seed):
@@ -505,16 +555,13 @@ def test_gated_relu2(bl, t, n, k, dtype):
     assert np.array_equal(_bits(h2), _bits(h))
 
 
-def test_gated_relu2_prefill_full_size_sampled(bl):
-    """The 2B gate/up projections at T = 2048 (128 x 512 tiles), checked on
-    sampled tokens, the zero token among them."""
+def test_gated_relu2_prefill_full_size(bl):
+    """The 2B gate/up projections at T = 2048 (128 x 512 tiles), every token
+    (the zero token among them) checked."""
     t, n, k = 2048, 6912, 2560
     pgu, gg, gu, xin, xref, tg, tu, gg_ref, gu_ref = _gated_inputs(bl, t, n, k, "bf16", 7100)
     h, xq, absmax, acc = bl.gated_relu2(xin, pgu, gg, gu, want_acc=True)
-    rows = np.sort(np.concatenate([[0, 1, 127, 128, t - 1],
-                                   np.random.default_rng(7101).choice(t, 27, replace=False)]))
-    rows = np.unique(rows)
-    _check_gated(_bits(h), host(xq), host(absmax), host(acc), xref, tg, tu, gg_ref, gu_ref, rows)
+    _check_gated(_bits(h), host(xq), host(absmax), host(acc), xref, tg, tu, gg_ref, gu_ref)
 
 
 def test_gated_relu2_then_down(bl):
@@ -767,12 +814,4 @@ SWEEP_SUBLN = _draw(9105, 6, lambda r: (int(r.choice([1, 2, 5, 64, 300])), 16 * 
 @pytest.mark.parametrize("t,k,dtype", SWEEP_SUBLN, ids=[f"T{t}_K{k}_{d}" for t, k, d in SWEEP_SUBLN])
 def test_sweep_subln(bl, t, k, dtype):
     xref, xin, g = _subln_inputs(t, k, dtype, 9800 + t + k)
-    q_ref, scale_ref, rs_ref, a_ref = oracle.subln_quant_act(xref, g)
-    xq, scale, rowsum = bl.subln_quant_act(xin, dev(g))
-    assert np.array_equal(host(xq), q_ref)
-    assert np.array_equal(host(rowsum), rs_ref)
-    sc = host(scale).astype(np.float64)
-    zero = a_ref == 0
-    assert np.all(sc[zero] == 0.0)
-    rel = np.abs(sc[~zero] - scale_ref[~zero]) / scale_ref[~zero]
-    assert rel.size == 0 or float(rel.max()) <= 2.5e-7, f"scale off by {rel.max():.3g}"
+    check_subln(bl, xref, xin, g)
