@@ -111,14 +111,14 @@ class Calls:
     def __init__(self, lib):
         self.lib = lib
 
-    def quant(self, x, xq, absmax, t, k, stream):
-        rc = self.lib.bitlinear_quant_act(x, 1, t, k, xq, absmax, None, stream)
+    def quant(self, x, xq, absmax, t, k, stream, rowsum=None):
+        rc = self.lib.bitlinear_quant_act(x, 1, t, k, xq, absmax, rowsum, stream)
         if rc:
             raise RuntimeError(self.lib.bitlinear_last_error().decode())
 
-    def forward(self, packed, gamma, xq, absmax, t, n, k, y, algo, stream):
-        rc = self.lib.bitlinear_forward_algo(packed, gamma, xq, absmax, t, n, k, y, None, algo,
-                                             stream)
+    def forward(self, packed, gamma, xq, absmax, t, n, k, y, algo, stream, rowsum=None):
+        rc = self.lib.bitlinear_forward_algo(packed, gamma, xq, absmax, rowsum, t, n, k, y, None,
+                                             algo, stream)
         if rc:
             raise RuntimeError(self.lib.bitlinear_last_error().decode())
 
@@ -346,6 +346,7 @@ def big_extra(torch, binding, wl, dev, stream):
             x = torch.randn((t, m.k), device=dev, generator=xg).to(torch.bfloat16)
             xq = torch.empty((t, m.k), dtype=torch.int8, device=dev)
             am = torch.empty(t, dtype=torch.float32, device=dev)
+            rs = torch.empty(t, dtype=torch.int32, device=dev)
             y = torch.empty((t, m.n), dtype=torch.float32, device=dev)
             descs = []
             for c in copies:
@@ -357,10 +358,17 @@ def big_extra(torch, binding, wl, dev, stream):
             us_grp = rotated_time_us(
                 torch, lambda s, i: calls.grouped(descs[i], t, ctypes.c_void_p(s.cuda_stream)),
                 len(copies), stream)
-            calls.quant(ptr(x), ptr(xq), ptr(am), t, m.k, ctypes.c_void_p(stream.cuda_stream))
+            calls.quant(ptr(x), ptr(xq), ptr(am), t, m.k, ctypes.c_void_p(stream.cuda_stream),
+                        ptr(rs))
             us_fwd = rotated_time_us(
                 torch, lambda s, i: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), t, m.n, m.k,
                                                   ptr(y), 0, ctypes.c_void_p(s.cuda_stream)),
+                len(copies), stream)
+            # the same with the tokens' row sums handed in (no sum-of-q pass in the kernel)
+            us_rs = rotated_time_us(
+                torch, lambda s, i: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), t, m.n, m.k,
+                                                  ptr(y), 0, ctypes.c_void_p(s.cuda_stream),
+                                                  ptr(rs)),
                 len(copies), stream)
             if t == 1:
                 rec["t1_act_quant_plus_forward_us"] = round(us_grp, 2)
@@ -368,12 +376,14 @@ def big_extra(torch, binding, wl, dev, stream):
                 rec["t1_forward_us"] = round(us_fwd, 2)
                 rec["t1_forward_gb_s"] = round(gemv_bytes(1, m.n, m.k) / us_fwd / 1e3, 1)
                 rec["t1_forward_frac_of_hbm_peak"] = round(gemv_bytes(1, m.n, m.k) / us_fwd / 1e3 / HBM_PEAK_GBS, 4)
+                rec["t1_forward_rowsum_given_us"] = round(us_rs, 2)
             else:
                 ops = 2.0 * t * m.n * m.k
                 rec["t256_act_quant_plus_forward_us"] = round(us_grp, 2)
                 rec["t256_forward_us"] = round(us_fwd, 2)
                 rec["t256_forward_tops"] = round(ops / us_fwd / 1e6, 1)
                 rec["t256_forward_frac_of_int8_peak"] = round(ops / us_fwd / 1e6 / INT8_PEAK_TOPS, 4)
+                rec["t256_forward_rowsum_given_us"] = round(us_rs, 2)
         out[f"{m.k}->{m.n}"] = rec
         del copies, packed
         torch.cuda.empty_cache()

@@ -32,9 +32,9 @@ SIGNATURES = {
     "bitlinear_quant_act": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
     "bitlinear_subln_quant_act": (_c_int, [_c_vp, _c_int, _c_vp, ctypes.c_float, _c_i64, _c_i64,
                                            _c_vp, _c_vp, _c_vp, _c_vp]),
-    "bitlinear_forward": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp,
-                                   _c_vp, _c_vp]),
-    "bitlinear_forward_algo": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+    "bitlinear_forward": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                   _c_vp, _c_vp, _c_vp]),
+    "bitlinear_forward_algo": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                                         _c_vp, _c_vp, _c_int, _c_vp]),
 }
 
@@ -213,8 +213,12 @@ def subln_quant_act(x, gain, eps_n=1e-5, with_rowsum=True):
     return xq, scale, rowsum
 
 
-def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None, acc_out=None):
-    """Steps A2 + A3 on the GPU: -> y float32[T, N] (and acc int32[T, N] if want_acc)."""
+def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None, acc_out=None,
+            rowsum=None):
+    """Steps A2 + A3 on the GPU: -> y float32[T, N] (and acc int32[T, N] if want_acc).
+
+    ``rowsum`` (int32[T], the row sums quant_act returns) lets the kernels
+    take each token's sum of q instead of deriving it."""
     lib = load()
     _need_cuda(packed, "packed", torch.uint8)
     _need_cuda(gamma, "gamma", torch.float32)
@@ -226,6 +230,9 @@ def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None,
     _need_shape(packed, "packed", (n, k // 4))
     _need_shape(gamma, "gamma", (1,))
     _need_shape(absmax, "absmax", (t,))
+    if rowsum is not None:
+        _need_cuda(rowsum, "rowsum", torch.int32)
+        _need_shape(rowsum, "rowsum", (t,))
     if out is not None:
         _need_cuda(out, "out", torch.float32)
         _need_shape(out, "out", (t, n))
@@ -236,16 +243,17 @@ def forward(packed, gamma, xq, absmax, n, algo="auto", want_acc=False, out=None,
         _need_shape(acc, "acc_out", (t, n))
     if want_acc and acc is None:
         acc = torch.empty((t, n), dtype=torch.int32, device=xq.device)
-    _same_device("forward", packed, gamma, xq, absmax, y, acc)
-    _check(lib.bitlinear_forward_algo(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax), t, n, k,
-                                      _ptr(y), _ptr(acc), ALGOS[algo], _stream(xq.device)))
+    _same_device("forward", packed, gamma, xq, absmax, y, acc, rowsum)
+    _check(lib.bitlinear_forward_algo(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(absmax),
+                                      _ptr(rowsum), t, n, k, _ptr(y), _ptr(acc), ALGOS[algo],
+                                      _stream(xq.device)))
     return (y, acc) if want_acc else y
 
 
 def bitlinear(x, packed, gamma, n, algo="auto"):
     """Quantise x and run the forward: y = BitLinear(x) with pre-packed weights."""
-    xq, absmax, _ = quant_act(x, with_rowsum=False)
-    return forward(packed, gamma, xq, absmax, n, algo=algo)
+    xq, absmax, rowsum = quant_act(x)
+    return forward(packed, gamma, xq, absmax, n, algo=algo, rowsum=rowsum)
 
 
 def linear_grouped(xs, weights, want_acc=False):

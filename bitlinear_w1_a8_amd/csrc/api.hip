@@ -19,7 +19,7 @@ constexpr int64_t kMaxNK = int64_t(1) << 38;  // keeps every gamma bucket below 
 constexpr int64_t kMaxTN = int64_t(1) << 36;  // y up to 256 GiB
 constexpr int64_t kMaxBinaryK = 32768;         // int8 rows of the binary decode kernel fit LDS
 
-int fail(int code, const char* fmt, ...) {
+bl_status fail(bl_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -31,14 +31,14 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_k(const char* fn, int64_t k) {
+bl_status check_k(const char* fn, int64_t k) {
   if (k < 16 || k > BITLINEAR_MAX_K || k % 16 != 0)
     return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 16 in [16, %d]", fn,
                 (long long)k, BITLINEAR_MAX_K);
   return BL_OK;
 }
 
-int launched(const char* fn, hipError_t e) {
+bl_status launched(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(BL_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   g_last_error.clear();
   return BL_OK;
@@ -60,11 +60,11 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
   return bl::kPackWorkspaceBytes;
 }
 
-int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+bl_status bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "bitlinear_pack_weights";
   if (!w || !packed || !gamma || !workspace) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (N < 1 || N > kMaxN || N * K > kMaxNK)
     return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 8))
@@ -77,11 +77,11 @@ int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed
                                       static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
-                                   float* gamma, void* stream) {
+bl_status bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                         float* gamma, void* stream) {
   const char* fn = "bitlinear_pack_weights_noalloc";
   if (!w || !packed || !gamma) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (N < 1 || N > kMaxN || N * K > kMaxNK)
     return fail(BL_ERR_SHAPE, "%s: N=%lld, K=%lld: N*K above 2^38 would overflow the %d "
                 "fixed buckets", fn, (long long)N, (long long)K, bl::kGammaBuckets);
@@ -95,13 +95,13 @@ int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t
   return launched(fn, bl::launch_pack(w, N, K, packed, gamma, buckets, s));
 }
 
-int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
-                        float* absmax, int32_t* rowsum, void* stream) {
+bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
+                              float* absmax, int32_t* rowsum, void* stream) {
   const char* fn = "bitlinear_quant_act";
   if (!x || !xq || !absmax) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (x_dtype != BL_F32 && x_dtype != BL_BF16)
     return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(absmax, 4) || (rowsum && !aligned(rowsum, 4)))
     return fail(BL_ERR_ALIGN, "%s: x and xq need 16-byte, absmax and rowsum 4-byte alignment", fn);
@@ -109,16 +109,16 @@ int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t
                                        static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
-                              int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
-                              void* stream) {
+bl_status bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
+                                    int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
+                                    void* stream) {
   const char* fn = "bitlinear_subln_quant_act";
   if (!x || !gain || !xq || !scale) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (x_dtype != BL_F32 && x_dtype != BL_BF16)
     return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
   if (!(eps_n > 0.0f) || !std::isfinite(eps_n))
     return fail(BL_ERR_ARG, "%s: eps_n must be finite and > 0", fn);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
   if (!aligned(x, 16) || !aligned(gain, 16) || !aligned(xq, 16) || !aligned(scale, 4) ||
       (rowsum && !aligned(rowsum, 4)))
@@ -128,25 +128,25 @@ int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, flo
                                              rowsum, static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                           const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                           int32_t* acc, int algo, void* stream) {
+bl_status bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                                 const float* absmax, const int32_t* rowsum, int64_t T, int64_t N,
+                                 int64_t K, float* y, int32_t* acc, int algo, void* stream) {
   const char* fn = "bitlinear_forward";
   if (!packed || !gamma || !xq || !absmax || !y)
     return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
   if (N < 1 || N > kMaxN || T * N > kMaxTN)
     return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
   if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
-      !aligned(y, 4) || (acc && !aligned(acc, 4)))
+      !aligned(y, 4) || (acc && !aligned(acc, 4)) || (rowsum && !aligned(rowsum, 4)))
     return fail(BL_ERR_ALIGN, "%s: packed and xq need 16-byte, the others 4-byte alignment", fn);
-  if (algo == BL_ALGO_AUTO) algo = T <= bl::kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
+  if (algo == BL_ALGO_AUTO) algo = bl::auto_algo(T, N, K);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (algo == BL_ALGO_GEMV)
-    return launched(fn, bl::launch_gemv(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+    return launched(fn, bl::launch_gemv(packed, gamma, xq, absmax, rowsum, T, N, K, y, acc, s));
   if (algo == BL_ALGO_GEMM)
-    return launched(fn, bl::launch_gemm(packed, gamma, xq, absmax, T, N, K, y, acc, s));
+    return launched(fn, bl::launch_gemm(packed, gamma, xq, absmax, rowsum, T, N, K, y, acc, s));
   if (algo == BL_ALGO_LUT)
     return launched(fn, bl::launch_gemv_lut(packed, gamma, xq, absmax, T, N, K, y, acc, s));
   if (algo == BL_ALGO_DOT4)
@@ -154,8 +154,8 @@ int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8
   return fail(BL_ERR_ARG, "%s: unknown algo %d", fn, algo);
 }
 
-int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
-                             void* stream) {
+bl_status bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
+                                   void* stream) {
   const char* fn = "bitlinear_linear_grouped";
   if (!problems) return fail(BL_ERR_NULL, "%s: NULL problems array", fn);
   if (count < 1 || count > 8) return fail(BL_ERR_ARG, "%s: count=%d must be in [1, 8]", fn, count);
@@ -166,7 +166,7 @@ int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, in
     const bl_linear& q = problems[i];
     if (!q.x || !q.packed || !q.gamma || !q.y || !q.xq || !q.absmax)
       return fail(BL_ERR_NULL, "%s: problem %d: NULL pointer argument", fn, i);
-    if (int rc = check_k(fn, q.K)) return rc;
+    if (bl_status rc = check_k(fn, q.K)) return rc;
     if (q.N < 1 || q.N > kMaxN || T * q.N > kMaxTN)
       return fail(BL_ERR_SHAPE, "%s: problem %d: N=%lld out of range", fn, i, (long long)q.N);
     if (!aligned(q.x, 16) || !aligned(q.packed, 16) || !aligned(q.xq, 16) ||
@@ -179,9 +179,9 @@ int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, in
                                               static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
-                                  float* gamma, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+bl_status bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                        float* gamma, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
   const char* fn = "bitlinear_pack_weights_binary";
   if (!w || !packed || !gamma || !workspace) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (K < 256 || K > kMaxBinaryK || K % 256 != 0)
@@ -199,9 +199,9 @@ int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t*
                                              static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                             const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                             int32_t* acc, int algo, void* stream) {
+bl_status bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                                   const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                                   int32_t* acc, int algo, void* stream) {
   const char* fn = "bitlinear_forward_binary";
   if (!packed || !gamma || !xq || !absmax || !y)
     return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
@@ -221,11 +221,11 @@ int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const in
                                                 static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
-                              uint8_t* out, void* stream) {
+bl_status bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
+                                    uint8_t* out, void* stream) {
   const char* fn = "bitlinear_interleave_rows";
   if (!a || !b || !out) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (N < 1 || 2 * N > kMaxN || 2 * N * K > kMaxNK)
     return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
   if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out, 4))
@@ -233,16 +233,16 @@ int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int
   return launched(fn, bl::launch_interleave(a, b, N, K, out, static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
-                          const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
-                          int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
-                          void* stream) {
+bl_status bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
+                                const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
+                                int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
+                                void* stream) {
   const char* fn = "bitlinear_gated_relu2";
   if (!x || !packed_gu || !gamma_gate || !gamma_up || !h || !xq || !absmax)
     return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (x_dtype != BL_F32 && x_dtype != BL_BF16)
     return fail(BL_ERR_DTYPE, "%s: unknown x_dtype %d", fn, x_dtype);
-  if (int rc = check_k(fn, K)) return rc;
+  if (bl_status rc = check_k(fn, K)) return rc;
   if (T < 1 || T > kMaxT) return fail(BL_ERR_SHAPE, "%s: T=%lld out of range", fn, (long long)T);
   if (N < 1 || 2 * N > kMaxN || T * 2 * N > kMaxTN)
     return fail(BL_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
@@ -255,19 +255,20 @@ int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
                                        static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                      const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                      int32_t* acc, void* stream) {
-  return bitlinear_forward_algo(packed, gamma, xq, absmax, T, N, K, y, acc, BL_ALGO_AUTO, stream);
+bl_status bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                            const float* absmax, const int32_t* rowsum, int64_t T, int64_t N,
+                            int64_t K, float* y, int32_t* acc, void* stream) {
+  return bitlinear_forward_algo(packed, gamma, xq, absmax, rowsum, T, N, K, y, acc, BL_ALGO_AUTO,
+                                stream);
 }
 
 int64_t bitlinear_calib_sink_len(void) { return bl::kCalibSinkLen; }
 
-int bitlinear_calib_empty(void* stream) {
+bl_status bitlinear_calib_empty(void* stream) {
   return launched("bitlinear_calib_empty", bl::launch_calib_empty(static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+bl_status bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   const char* fn = "bitlinear_calib_read";
   if (!buf || !sink) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40))
@@ -278,7 +279,7 @@ int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
   return launched(fn, bl::launch_calib_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream) {
+bl_status bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream) {
   const char* fn = "bitlinear_calib_mfma";
   if (!sink) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (iters < 1 || iters > (int64_t(1) << 20) || byte < -128 || byte > 127)

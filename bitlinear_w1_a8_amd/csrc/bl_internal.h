@@ -14,11 +14,13 @@ namespace bl {
 constexpr float kEps = 1e-5f;
 constexpr float kQb = 127.0f;
 
-// T at or below which the automatic choice takes the decode kernel: measured
-// on 2560->6912 and 6912->2560 against the tiled MFMA kernel with its tile
-// choice, the decode kernel is faster through T = 32 on both, within 5% at
-// T = 64 (faster on one, slower on the other) and twice as slow at T = 128.
+// Largest T that the automatic choice may send to the decode kernel; see
+// auto_algo for the rule per shape.
 constexpr int64_t kGemvMaxTokens = 64;
+
+// The automatic kernel choice of bitlinear_forward: BL_ALGO_GEMV (the decode
+// kernels) or BL_ALGO_GEMM (the tiled MFMA kernel), by shape (gemv.hip).
+int auto_algo(int64_t t, int64_t n, int64_t k);
 
 // Measurement helpers (calib.hip): the launch floor, the HBM read stream and
 // the int8 matrix-core rate of the device; the read writes kCalibReadBlocks
@@ -65,10 +67,11 @@ hipError_t launch_subln_quant(const void* x, int bf16, const float* gain, float 
                               int64_t k, int8_t* xq, float* scale, int32_t* rowsum,
                               hipStream_t stream);
 
-// Decode kernel: handles any T by taking tokens 64 at a time.
+// Decode kernel: handles any T by taking tokens 64 at a time.  rowsum (the
+// tokens' sums of q) may be NULL: the kernel then derives the sums itself.
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
-                       int32_t* acc, hipStream_t stream);
+                       const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
+                       int64_t k, float* y, int32_t* acc, hipStream_t stream);
 
 // Table-lookup decode kernel (comparison design), any T (one token per block row).
 hipError_t launch_gemv_lut(const uint8_t* packed, const float* gamma, const int8_t* xq,
@@ -84,9 +87,10 @@ hipError_t launch_gemv_dot4(const uint8_t* packed, const float* gamma, const int
 hipError_t launch_linear_group(const struct bl_linear* probs, int count, int64_t t, int bf16,
                                hipStream_t stream);
 
+// Tiled MFMA kernel, any T; rowsum as for launch_gemv.
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
-                       int32_t* acc, hipStream_t stream);
+                       const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
+                       int64_t k, float* y, int32_t* acc, hipStream_t stream);
 
 // Gate and up projections of one input with the gated ReLU^2 epilogue: the
 // packed matrix holds 2n rows, row 2i of the gate and row 2i+1 of the up

@@ -259,8 +259,10 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // GATED: the weight rows come in (gate, up) pairs, 2i and 2i + 1, which sit in
 // neighbouring lanes of a fragment; the even lane takes its neighbour's sum
 // and writes the bfloat16 gated ReLU^2 of output i to h (y is not used).
+// RS: each token's sum of q comes from rowsum[] (subtracted by the first K
+// part only) instead of being summed from the activation tiles in the loop.
 template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED,
-          int WBITS = 2>
+          int WBITS = 2, bool RS = false>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
                                                          const int8_t* __restrict__ xq,
@@ -270,8 +272,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
                                                          int32_t* __restrict__ acc_out,
                                                          int ksteps, int splits,
                                                          const float* __restrict__ gamma2,
-                                                         uint16_t* __restrict__ h_out) {
+                                                         uint16_t* __restrict__ h_out,
+                                                         const int32_t* __restrict__ rowsum) {
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
+  static_assert(!(RS && (GATED || WBITS != 2)), "rowsum: plain two-bit kernels only");
   static_assert(!(SPLIT && GATED), "the gated epilogue needs whole sums");
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       for (int r = tid; r < BM; r += NT) {
         const int tok = m0 + r;
         scale[r] = tok < T ? out_scale(g, absmax[tok]) : 0.0f;
+        if constexpr (RS) rsum[r] = tok < T && part == 0 ? rowsum[tok] : 0;
       }
     }
   }
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
     const unsigned char* Bt =
         bbuf(stage_c) + (wn * 32 * WNF + m) * kBRow + (WBITS == 2 ? 16 * h : 0);
-    {
+    if constexpr (!RS) {
       // this wave's own activation chunks of the step (rows 8c .. 8c + 7,
       // 16 bytes per lane, slot order irrelevant to a sum): sum of q
 #pragma unroll
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   if constexpr (STAGES == 4)
     if (kt + 2 < nk) step(I2{}, kt + 2);
   wait_vmem<0>();   // no load may land in LDS after the block has finished
-  {
+  if constexpr (!RS) {
     // eight lanes hold the pieces of one row of a chunk: their total is the
     // token's sum of q over this block's K range
 #pragma unroll
@@ -597,7 +602,8 @@ template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool GATED = fal
 hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
                    hipStream_t stream, int splits = 1, int ksteps = 0,
-                   const float* gamma2 = nullptr, uint16_t* h = nullptr) {
+                   const float* gamma2 = nullptr, uint16_t* h = nullptr,
+                   const int32_t* rowsum = nullptr) {
   // K parts of ksteps 128-wide steps each (the last may be shorter); the
   // caller sizes them so that every part has at least one step
   if (splits == 1) ksteps = (int)(k / BK);
@@ -609,6 +615,9 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>;
     else if constexpr (GATED)
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, true>;
+    else if (rowsum)
+      return splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false, 2, true>
+                        : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true>;
     else
       return splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false>
                         : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false>;
@@ -616,7 +625,7 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
   auto kern = pick();
   kern<<<dim3((unsigned)(tiles * splits)), WAVES * 64, 0, stream>>>(
       reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc,
-      ksteps, splits, gamma2, h);
+      ksteps, splits, gamma2, h, rowsum);
   return hipGetLastError();
 }
 
@@ -698,8 +707,8 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
-                       int32_t* acc, hipStream_t stream) {
+                       const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
+                       int64_t k, float* y, int32_t* acc, hipStream_t stream) {
   const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
   if (!lds_ok) {
     // K % 128 != 0 (or offsets beyond 32 bits): the register-staged kernel
@@ -710,13 +719,17 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
   }
   switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true)) {
     case Tiles::kWide:
-      return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+      return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
     case Tiles::kNarrow:
-      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W256:
-      return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+      return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W128:
-      return run_lds<4, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
+      return run_lds<4, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
     case Tiles::kSplit: {
       // 128 x 512 tiles, K in parts: y is cleared, takes the exact int32
       // partial sums by atomics and is rescaled in place
@@ -729,7 +742,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       k_clear_i32<<<(unsigned)std::min<int64_t>((total + 255) / 256, 4096), 256, 0, stream>>>(
           reinterpret_cast<int*>(y), total);
       hipError_t e = run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                         stream, (int)parts, (int)steps);
+                                                         stream, (int)parts, (int)steps, nullptr,
+                                                         nullptr, rowsum);
       if (e != hipSuccess) return e;
       const int col_blocks = (int)((n + 1023) / 1024);
       k_split_finish<<<(unsigned)(t * col_blocks), 256, 0, stream>>>(y, acc, gamma, absmax, (int)n,

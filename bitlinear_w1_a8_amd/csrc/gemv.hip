@@ -22,6 +22,9 @@
 // Work split: a block owns 16*RT weight rows; its waves split K into chunks of
 // 64*VEC k; partial 16x16 tiles are summed through LDS; the epilogue
 // multiplies by gamma * max(absmax, eps) / 127.
+#include <atomic>
+#include <type_traits>
+
 #include "bitlinear.h"
 #include "bl_internal.h"
 
@@ -38,8 +41,10 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
                                               int K, float* __restrict__ y,
                                               int32_t* __restrict__ acc_out,
                                               const float* __restrict__ gamma2,
-                                              uint16_t* __restrict__ h) {
+                                              uint16_t* __restrict__ h,
+                                              const int32_t* __restrict__ rowsum) {
   extern __shared__ int red[];  // [nwaves][RT*NTT*4][64]
+  const bool derive = rowsum == nullptr;   // sum q here, or take each token's total
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int qg = lane >> 4, r = lane & 15;
   const int K16 = K >> 4;                           // packed words per row
@@ -105,11 +110,13 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (derive) {
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
+        for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-        for (int d = 0; d < 4 * VEC; ++d)
-          qs[tt] = __builtin_amdgcn_sdot4((int)xv[u][tt][d], 0x01010101, qs[tt], false);
+          for (int d = 0; d < 4 * VEC; ++d)
+            qs[tt] = __builtin_amdgcn_sdot4((int)xv[u][tt][d], 0x01010101, qs[tt], false);
+      }
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
 #pragma unroll
@@ -128,7 +135,8 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
     }
   }
 
-  // sum of q over this wave's k for the token of column r: add the 4 lane groups
+  // sum of q over this wave's k for the token of column r: add the 4 lane
+  // groups (with rowsum given, qs is 0 and the total comes off at the end)
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     int s = qs[tt];
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint32_t* __restrict__ packe
     const int ln = (i >> 2) * 16 + j;
     int s = 0;
     for (int wv = 0; wv < nwaves; ++wv) s += red[(wv * kSlots + slot) * 64 + ln];
-    return s;
+    return derive ? s : s - rowsum[tl];
   };
   if (h) {
     // gated: rows 2i (gate) and 2i + 1 (up) make output n0 / 2 + i
@@ -237,6 +245,7 @@ struct DecProblem {
   int N, K;
   int per;                // chunks per wave: ceil((K / 256) / nw) <= CPW
   int ldy;                // row stride of y and acc (N, or more for a row range of a wider problem)
+  const int32_t* rowsum;  // kInt8: each token's sum of q, or NULL (each wave sums its own k run)
 };
 constexpr int kMaxGroup = 8;
 struct DecGroup {
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   // fetches them in dependent rounds around the early exit below.
   __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
                    "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
-                   "s"(pr.per), "s"(pr.ldy), "s"(T), "s"(nwaves));
+                   "s"(pr.per), "s"(pr.ldy), "s"(pr.rowsum), "s"(T), "s"(nwaves));
   if constexpr (GATED) __asm__ volatile("" ::"s"(pr.gamma2), "s"(pr.h));
   const int N = pr.N, K = pr.K, per = pr.per;
   const int n0 = (int)blockIdx.x * kRows;
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   float a_t = 0.0f; // one raw token: its absmax
   if constexpr (MODE == kInt8) {
     wait_vmem<RT * CPW>();                               // this wave's activation run landed
-    for (int t = 0; t < T; ++t) {
+    for (int t = 0; t < (pr.rowsum ? 0 : T); ++t) {     // with rowsum: the totals, at the end
       const uint4* xt = reinterpret_cast<const uint4*>(xs8 + t * tstride + run0);
       int part = 0;
       for (int i = lane; i < runb / 16; i += 64) {
@@ -660,10 +669,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
       const int i = idx % (kRows / 2), tl = idx / (kRows / 2);
       const int nn = n0 + 2 * i;
       if (nn >= N) continue;
+      const int qt = MODE == kInt8 && pr.rowsum ? pr.rowsum[tl] : 0;
       const int sg = __hip_atomic_load(&tile[tl * kRows + 2 * i], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                                       __HIP_MEMORY_SCOPE_WORKGROUP) - qt;
       const int su = __hip_atomic_load(&tile[tl * kRows + 2 * i + 1], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                                       __HIP_MEMORY_SCOPE_WORKGROUP) - qt;
       if (pr.acc) {
         pr.acc[(int64_t)tl * ldy + nn] = sg;
         pr.acc[(int64_t)tl * ldy + nn + 1] = su;
@@ -680,7 +690,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
     const int i = idx % kRows, tl = idx / kRows;
     const int nn = n0 + i;
     if (nn >= N) continue;
-    const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) -
+                    (MODE == kInt8 && pr.rowsum ? pr.rowsum[tl] : 0);
     const int64_t o = (int64_t)tl * pr.ldy + nn;
     if (pr.acc) pr.acc[o] = sum;
     float a;                                        // the token's absmax (int8: lane's own first)
@@ -704,8 +715,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 
 template <int VEC, int RT, int NTT, int U>
 void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* absmax,
-         int t, int n, int k, float* y, int32_t* acc, const float* gamma2, uint16_t* h,
-         hipStream_t stream) {
+         const int32_t* rowsum, int t, int n, int k, float* y, int32_t* acc, const float* gamma2,
+         uint16_t* h, hipStream_t stream) {
   const int k16 = k / 16;
   const int nchunks = (k16 + 4 * VEC - 1) / (4 * VEC);
   int nw = (nchunks + U - 1) / U;       // one pass of U chunks per wave where possible
@@ -714,29 +725,30 @@ void run(const uint8_t* packed, const float* gamma, const int8_t* xq, const floa
   const int grid = (n + 16 * RT - 1) / (16 * RT);
   const size_t lds = (size_t)nw * RT * NTT * 4 * 64 * sizeof(int);
   k_gemv<VEC, RT, NTT, U><<<grid, nw * 64, lds, stream>>>(
-      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc, gamma2, h);
+      reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, t, n, k, y, acc, gamma2, h,
+      rowsum);
 }
 
 template <int VEC>
 void run_tokens(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                const float* absmax, int t, int n, int k, float* y, int32_t* acc,
-                const float* gamma2, uint16_t* h, hipStream_t stream) {
+                const float* absmax, const int32_t* rs, int t, int n, int k, float* y,
+                int32_t* acc, const float* gamma2, uint16_t* h, hipStream_t stream) {
   if (t <= 16)
-    run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
+    run<VEC, 1, 1, BL_GEMV_U>(packed, gamma, xq, absmax, rs, t, n, k, y, acc, gamma2, h, stream);
   else if (n < 32 * BL_GEMV_RT2_MIN_BLOCKS) {
     // two-tile blocks would leave most CUs idle: one tile per block, twice
     // the blocks (measured at 6912 -> 2560: T = 32 14.0 -> 11.4 us, T = 64
     // 21.5 -> 17.7 us; at 2560 -> 6912, 216 two-tile blocks, one tile loses)
     if (t <= 32)
-      run<VEC, 1, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                      gamma2, h, stream);
+      run<VEC, 1, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, rs, t, n, k, y,
+                                                      acc, gamma2, h, stream);
     else
-      run<VEC, 1, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
+      run<VEC, 1, 4, 1>(packed, gamma, xq, absmax, rs, t, n, k, y, acc, gamma2, h, stream);
   } else if (t <= 32)
-    run<VEC, 2, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, t, n, k, y, acc,
+    run<VEC, 2, 2, (BL_GEMV_U > 2 ? 2 : BL_GEMV_U)>(packed, gamma, xq, absmax, rs, t, n, k, y, acc,
                                                     gamma2, h, stream);
   else
-    run<VEC, 2, 4, 1>(packed, gamma, xq, absmax, t, n, k, y, acc, gamma2, h, stream);
+    run<VEC, 2, 4, 1>(packed, gamma, xq, absmax, rs, t, n, k, y, acc, gamma2, h, stream);
 }
 
 }  // namespace
@@ -895,12 +907,12 @@ bool dec_ok(int64_t t, int64_t k, const void* packed, const void* xq) {
 }
 
 hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                        const float* absmax, int t, int n, int k, float* y, int32_t* acc,
-                        const float* gamma2, uint16_t* h, hipStream_t stream) {
+                        const float* absmax, const int32_t* rowsum, int t, int n, int k, float* y,
+                        int32_t* acc, const float* gamma2, uint16_t* h, hipStream_t stream) {
   DecGroup grp = {};
   grp.T = t;
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
-                        nullptr, nullptr, gamma2, h, n, k, 0};
+                        nullptr, nullptr, gamma2, h, n, k, 0, 0, rowsum};
   const int blocks = (n + 15) / 16;
   const DecShape sh = dec_shape(blocks, k, t);
   return run_dec<kInt8>(grp, 1, sh, dec_lds(t, k, 0, sh.rt), stream);
@@ -927,9 +939,11 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
       const bl_linear& q = probs[i];
       hipError_t e = launch_quant(q.x, bf16, t, q.K, q.xq, q.absmax, nullptr, stream);
       if (e != hipSuccess) return e;
-      e = t <= kGemvMaxTokens
-              ? launch_gemv(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream)
-              : launch_gemm(q.packed, q.gamma, q.xq, q.absmax, t, q.N, q.K, q.y, q.acc, stream);
+      e = auto_algo(t, q.N, q.K) == BL_ALGO_GEMV
+              ? launch_gemv(q.packed, q.gamma, q.xq, q.absmax, nullptr, t, q.N, q.K, q.y, q.acc,
+                            stream)
+              : launch_gemm(q.packed, q.gamma, q.xq, q.absmax, nullptr, t, q.N, q.K, q.y, q.acc,
+                            stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -982,40 +996,57 @@ namespace {
 
 // The int8-input decode kernels, plain (y) or gated (gamma2 and h given).
 hipError_t gemv_any(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                    const float* absmax, int64_t t, int64_t n, int64_t k, float* y, int32_t* acc,
-                    const float* gamma2, uint16_t* h, hipStream_t stream) {
+                    const float* absmax, const int32_t* rowsum, int64_t t, int64_t n, int64_t k,
+                    float* y, int32_t* acc, const float* gamma2, uint16_t* h,
+                    hipStream_t stream) {
   if (dec_ok(t, k, packed, xq))
-    return run_dec_int8(packed, gamma, xq, absmax, (int)t, (int)n, (int)k, y, acc, gamma2, h,
-                        stream);
+    return run_dec_int8(packed, gamma, xq, absmax, rowsum, (int)t, (int)n, (int)k, y, acc, gamma2,
+                        h, stream);
   const bool vec4 = (k % 64) == 0 && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
   for (int64_t t0 = 0; t0 < t; t0 += kGemvTokens) {
     const int tc = (int)(t - t0 < kGemvTokens ? t - t0 : kGemvTokens);
     const int8_t* xs = xq + t0 * k;
+    const int32_t* rs = rowsum ? rowsum + t0 : nullptr;
     float* ys = y ? y + t0 * n : nullptr;
     int32_t* as = acc ? acc + t0 * n : nullptr;
     uint16_t* hs = h ? h + t0 * (n / 2) : nullptr;
     if (vec4)
-      run_tokens<4>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, gamma2, hs, stream);
+      run_tokens<4>(packed, gamma, xs, absmax + t0, rs, tc, (int)n, (int)k, ys, as, gamma2, hs,
+                    stream);
     else
-      run_tokens<1>(packed, gamma, xs, absmax + t0, tc, (int)n, (int)k, ys, as, gamma2, hs, stream);
+      run_tokens<1>(packed, gamma, xs, absmax + t0, rs, tc, (int)n, (int)k, ys, as, gamma2, hs,
+                    stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+int auto_algo(int64_t t, int64_t n, int64_t k) {
+  // Measured against the tiled MFMA kernel with its own tile choice: the
+  // decode kernels win through T = 32 on the 2B shapes (2560 -> 6912 at
+  // T = 32: 8.4 against 12.1 us; 6912 -> 2560: 11.4 against 23.7); at T = 64
+  // they still win where the rows are long and few (6912 -> 2560: 17.7
+  // against 23.9 us) but not on wide, short rows (2560 -> 6912: 12.8
+  // against 12.4); from T = 128 on the MFMA kernel wins on both.
+  if (t <= 32) return BL_ALGO_GEMV;
+  if (t <= kGemvMaxTokens && n <= k) return BL_ALGO_GEMV;
+  return BL_ALGO_GEMM;
+}
+
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                       const float* absmax, int64_t t, int64_t n, int64_t k, float* y,
-                       int32_t* acc, hipStream_t stream) {
-  return gemv_any(packed, gamma, xq, absmax, t, n, k, y, acc, nullptr, nullptr, stream);
+                       const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
+                       int64_t k, float* y, int32_t* acc, hipStream_t stream) {
+  return gemv_any(packed, gamma, xq, absmax, rowsum, t, n, k, y, acc, nullptr, nullptr, stream);
 }
 
 hipError_t launch_gemv_gated(const uint8_t* packed, const float* gamma_gate,
                              const float* gamma_up, const int8_t* xq, const float* absmax,
                              int64_t t, int64_t n, int64_t k, uint16_t* h, int32_t* acc,
                              hipStream_t stream) {
-  return gemv_any(packed, gamma_gate, xq, absmax, t, n, k, nullptr, acc, gamma_up, h, stream);
+  return gemv_any(packed, gamma_gate, xq, absmax, nullptr, t, n, k, nullptr, acc, gamma_up, h,
+                  stream);
 }
 
 hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const float* gamma_gate,
@@ -1037,7 +1068,7 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
   }
   hipError_t e = launch_quant(x, bf16, t, k, xq, absmax, nullptr, stream);
   if (e != hipSuccess) return e;
-  return t <= kGemvMaxTokens
+  return auto_algo(t, n, k) == BL_ALGO_GEMV
              ? launch_gemv_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream)
              : launch_gemm_gated(packed, gamma_gate, gamma_up, xq, absmax, t, n, k, h, acc, stream);
 }

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 /* Largest K accepted: keeps every |acc| <= 127*K below 2^24, so the int32
  * sum converts to binary32 exactly. */
@@ -127,9 +127,9 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
  *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K)
  *             bytes, 8-byte aligned; its contents are overwritten.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
-int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
-                           float* gamma, void* workspace, size_t workspace_bytes,
-                           void* stream);
+bl_status bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                 float* gamma, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* bitlinear_pack_weights without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
@@ -145,8 +145,8 @@ int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed
  *            that the fixed buckets sum exactly (larger matrices: BL_ERR_SHAPE).
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP (also when the
  * array's device address cannot be looked up). */
-int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
-                                   float* gamma, void* stream);
+bl_status bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                         float* gamma, void* stream);
 
 /* Step A1: per-token absmax quantisation of activations to int8.
  * Follows "BitNet解读", activation quantisation (each token scaled into
@@ -161,8 +161,8 @@ int bitlinear_pack_weights_noalloc(const float* w, int64_t N, int64_t K, uint8_t
  *   absmax   [T] float32 output: a itself (not floored), 4-byte aligned.
  *   rowsum   [T] int32 output sum_k xq[t,k], or NULL to skip it.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_HIP. */
-int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
-                        float* absmax, int32_t* rowsum, void* stream);
+bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t* xq,
+                              float* absmax, int32_t* rowsum, void* stream);
 
 /* The sub-layer norm in front of step A1, fused with it.  The 2B4T report
  * (section 2) puts subln before the quantised projections and drops every
@@ -189,9 +189,9 @@ int bitlinear_quant_act(const void* x, int x_dtype, int64_t T, int64_t K, int8_t
  *   rowsum   [T] int32 output sum_k xq[t,k], or NULL.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_ARG
  * (eps_n), BL_ERR_HIP. */
-int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
-                              int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
-                              void* stream);
+bl_status bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, float eps_n,
+                                    int64_t T, int64_t K, int8_t* xq, float* scale, int32_t* rowsum,
+                                    void* stream);
 
 /* Steps A2 and A3: y[t, n] = (sum_k t[n,k] * xq[t,k]) * gamma * max(absmax[t], eps) / 127.
  * The contraction follows "BitNet解读", computational efficiency (ternary
@@ -199,24 +199,33 @@ int bitlinear_subln_quant_act(const void* x, int x_dtype, const float* gain, flo
  * the rescale follows the bitnet.cpp post, section 1.1 (the scale factor).
  * Dispatches on T (BL_ALGO_AUTO); see bitlinear_forward_algo.
  *
+ * The matrix-core kernels contract the stored codes c = t + 1 and remove
+ * sum_k xq[t,k] from each token's sums afterwards.  With `rowsum` given they
+ * take that sum from it, once per token; with NULL every kernel derives it
+ * from the activations it reads.
+ *
  *   packed   [N, K/4] uint8 from bitlinear_pack_weights, 16-byte aligned.
  *   gamma    [1] float32 (device) from bitlinear_pack_weights.
  *   xq       [T, K] int8 from bitlinear_quant_act, 16-byte aligned.
  *   absmax   [T] float32 from bitlinear_quant_act.
+ *   rowsum   [T] int32 sum_k xq[t,k] as bitlinear_quant_act writes it, 4-byte
+ *            aligned, or NULL.  Any other value gives wrong results (it is
+ *            not checked).
  *   T, N, K  1 <= T <= 2^24, 1 <= N <= 2^26, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
  *   y        [T, N] float32 output, 4-byte aligned.
  *   acc      [T, N] int32 output of the exact sums, or NULL to skip it.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
-int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                      const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                      int32_t* acc, void* stream);
+bl_status bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                            const float* absmax, const int32_t* rowsum, int64_t T, int64_t N,
+                            int64_t K, float* y, int32_t* acc, void* stream);
 
 /* bitlinear_forward with an explicit kernel choice (a bl_algo value); the
- * results are identical for every choice.  Errors as bitlinear_forward, plus
- * BL_ERR_ARG for an unknown algo. */
-int bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                           const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                           int32_t* acc, int algo, void* stream);
+ * results are identical for every choice (the table-lookup and packed-dot
+ * kernels work on signed weights and do not read rowsum).  Errors as
+ * bitlinear_forward, plus BL_ERR_ARG for an unknown algo. */
+bl_status bitlinear_forward_algo(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                                 const float* absmax, const int32_t* rowsum, int64_t T, int64_t N,
+                                 int64_t K, float* y, int32_t* acc, int algo, void* stream);
 
 /* One problem of bitlinear_linear_grouped: a whole BitLinear forward. */
 typedef struct bl_linear {
@@ -247,8 +256,8 @@ typedef struct bl_linear {
  *   x_dtype   BL_F32 or BL_BF16.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_ARG
  * (count out of range), BL_ERR_HIP. */
-int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
-                             void* stream);
+bl_status bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, int x_dtype,
+                                   void* stream);
 
 /* Step A0 for binary weights (+1 / -1, one bit each).  The original BitNet
  * has only these two values (the 2B4T explainer, section 2; "BitNet解读", on
@@ -264,9 +273,9 @@ int bitlinear_linear_grouped(const bl_linear* problems, int count, int64_t T, in
  *   gamma     [1] float32 output (device), 4-byte aligned.
  *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K) bytes.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
-int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
-                                  float* gamma, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+bl_status bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                                        float* gamma, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /* Steps A2 and A3 on binary weights: y[t, n] = (sum_k t[n,k] * xq[t,k]) *
  * gamma * max(absmax[t], eps) / 127 with t in {-1, +1}, exact in int32, as
@@ -282,9 +291,9 @@ int bitlinear_pack_weights_binary(const float* w, int64_t N, int64_t K, uint8_t*
  *            T*K < 2^31, N*K/32 < 2^31.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (BL_ALGO_LUT,
  * BL_ALGO_DOT4 or unknown), BL_ERR_HIP. */
-int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
-                             const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
-                             int32_t* acc, int algo, void* stream);
+bl_status bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const int8_t* xq,
+                                   const float* absmax, int64_t T, int64_t N, int64_t K, float* y,
+                                   int32_t* acc, int algo, void* stream);
 
 /* Row interleave of two packed matrices of the same shape, for
  * bitlinear_gated_relu2: out row 2i is row i of a, out row 2i + 1 row i of b
@@ -295,8 +304,8 @@ int bitlinear_forward_binary(const uint8_t* packed, const float* gamma, const in
  *   N, K     1 <= N <= 2^25, 16 <= K <= BITLINEAR_MAX_K, K % 16 == 0.
  *   out      [2N, K/4] uint8 output (device), 4-byte aligned; must not overlap a or b.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
-int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
-                              uint8_t* out, void* stream);
+bl_status bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int64_t K,
+                                    uint8_t* out, void* stream);
 
 /* The gate and up projections of one input (steps A1-A3 each) and the
  * squared-ReLU activation that the 2B4T report (section 2) puts in the
@@ -324,10 +333,10 @@ int bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t N, int
  *   absmax      [T] token absmax (written), 4-byte aligned.
  *   acc         [T, 2N] exact int32 sums, interleaved as the rows (gate, up), or NULL.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_HIP. */
-int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
-                          const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
-                          int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
-                          void* stream);
+bl_status bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
+                                const float* gamma_gate, const float* gamma_up, int64_t T, int64_t N,
+                                int64_t K, uint16_t* h, int8_t* xq, float* absmax, int32_t* acc,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helpers.  Not part of the forward: they measure, on the device
@@ -340,7 +349,7 @@ int bitlinear_gated_relu2(const void* x, int x_dtype, const uint8_t* packed_gu,
 int64_t bitlinear_calib_sink_len(void);
 
 /* One empty kernel on `stream`: the cost of a launch with no work. */
-int bitlinear_calib_empty(void* stream);
+bl_status bitlinear_calib_empty(void* stream);
 
 /* Reads the `bytes` bytes at `buf` (device, 16-byte aligned; `bytes` a
  * positive multiple of 16, at most 2^40) once, with 16-byte loads over a
@@ -348,7 +357,7 @@ int bitlinear_calib_empty(void* stream);
  * 32-bit words that block i read, so the XOR of those 2048 entries is the
  * XOR of the whole buffer; the rest of the sink is not written.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE (bytes), BL_ERR_ALIGN. */
-int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+bl_status bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* 4096 waves (four per SIMD on 256 CUs) each issue `iters` rounds of four
  * independent v_mfma_i32_32x32x32_i8 with every element of A and B equal to
@@ -357,7 +366,7 @@ int bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
  * receives 4 * iters * 32 * byte^2 modulo 2^32 (as int32).
  * Errors: BL_ERR_NULL, BL_ERR_ARG (iters outside [1, 2^20], byte outside
  * [-128, 127]). */
-int bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream);
+bl_status bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

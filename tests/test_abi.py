@@ -48,7 +48,7 @@ def test_binding_covers_header():
 
 
 def test_constants(lib):
-    assert lib.bitlinear_abi_version() == 1
+    assert lib.bitlinear_abi_version() == 2
     assert lib.bitlinear_gemv_max_tokens() == 64
     assert lib.bitlinear_pack_workspace_bytes(2560, 2560) == 2048
     assert lib.bitlinear_pack_workspace_bytes(28672, 8192) == 2048
@@ -107,20 +107,36 @@ def test_quant_errors(lib):
 
 def test_forward_errors(lib):
     f = lib.bitlinear_forward_algo
-    good = (A16, A16, A16, A16)
-    assert f(None, A16, A16, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_NULL
+    good = (A16, A16, A16, A16, None)          # packed, gamma, xq, absmax, rowsum
+    assert f(None, A16, A16, A16, None, 1, 16, 64, A16, None, 0, None) == BL_ERR_NULL
     assert f(*good, 1, 16, 64, None, None, 0, None) == BL_ERR_NULL
     assert f(*good, 1, 16, 48 + 1, A16, None, 0, None) == BL_ERR_SHAPE
     assert f(*good, 0, 16, 64, A16, None, 0, None) == BL_ERR_SHAPE
     assert f(*good, 1, 0, 64, A16, None, 0, None) == BL_ERR_SHAPE
     assert f(*good, 1 << 20, 1 << 20, 64, A16, None, 0, None) == BL_ERR_SHAPE
-    assert f(A16 + 4, A16, A16, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
-    assert f(A16, A16, A16 + 8, A16, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
+    assert f(A16 + 4, A16, A16, A16, None, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
+    assert f(A16, A16, A16 + 8, A16, None, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16 + 2, None, 0, None) == BL_ERR_ALIGN
     assert f(*good, 1, 16, 64, A16, A16 + 1, 0, None) == BL_ERR_ALIGN
+    # rowsum: NULL is accepted (the kernels derive the sums), a given one must be aligned
+    assert f(A16, A16, A16, A16, A16 + 2, 1, 16, 64, A16, None, 0, None) == BL_ERR_ALIGN
+    assert "alignment" in _err(lib)
+    assert f(A16, A16, A16, A16, A16, 1, 16, 64, A16, None, 5, None) == BL_ERR_ARG
     assert f(*good, 1, 16, 64, A16, None, 5, None) == BL_ERR_ARG
     assert f(*good, 1, 16, 64, A16, None, -1, None) == BL_ERR_ARG
-    assert lib.bitlinear_forward(None, A16, A16, A16, 1, 16, 64, A16, None, None) == BL_ERR_NULL
+    assert lib.bitlinear_forward(None, A16, A16, A16, None, 1, 16, 64, A16, None, None) == BL_ERR_NULL
+    assert lib.bitlinear_forward(A16, A16, A16, A16, A16 + 1, 1, 16, 64, A16, None, None) == BL_ERR_ALIGN
+
+
+def test_header_returns_bl_status():
+    # every entry point that reports a status is declared to return bl_status
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = dict((n, r) for r, n in re.findall(r"\b(\w+)\s+(bitlinear_\w+)\s*\(", text))
+    values = {"bitlinear_abi_version": "int", "bitlinear_last_error": "char",
+              "bitlinear_gemv_max_tokens": "int64_t", "bitlinear_pack_workspace_bytes": "size_t",
+              "bitlinear_calib_sink_len": "int64_t"}
+    for name, ret in decls.items():
+        assert ret == values.get(name, "bl_status"), (name, ret)
 
 
 def test_subln_quant_act_errors(lib):

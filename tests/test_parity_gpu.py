@@ -67,7 +67,7 @@ def check_quant(bl, x, dtype):
     assert bad == 0, f"{bad} of {q.size} int8 activations differ"
     assert np.array_equal(host(absmax).view(np.uint32), a_ref.view(np.uint32))
     assert np.array_equal(host(rowsum), rs_ref)
-    return xq, absmax, q_ref, a_ref
+    return xq, absmax, q_ref, a_ref, rowsum
 
 
 def check_y(y, acc_ref, gamma, absmax_ref):
@@ -81,14 +81,26 @@ def check_y(y, acc_ref, gamma, absmax_ref):
 
 
 def check_forward(bl, packed_dev, gamma_dev, xq_dev, absmax_dev, t_ref, q_ref, gamma_ref,
-                  absmax_ref, algo):
+                  absmax_ref, algo, rowsum_dev=None):
+    """The forward without row sums (each kernel derives them), and for the
+    matrix-core kernels also with the tokens' row sums given: the int32 sums
+    must equal the oracle's and y must be the same bits both ways."""
     n = t_ref.shape[0]
     y, acc = bl.forward(packed_dev, gamma_dev, xq_dev, absmax_dev, n, algo=algo, want_acc=True)
     acc_ref = oracle.contract(q_ref, t_ref)
     a = host(acc)
     bad = int(np.count_nonzero(a != acc_ref))
     assert bad == 0, f"{bad} of {a.size} int32 sums differ ({algo})"
-    check_y(host(y), acc_ref, gamma_ref, absmax_ref)
+    yh = host(y)
+    check_y(yh, acc_ref, gamma_ref, absmax_ref)
+    if algo in ("auto", "gemv", "gemm"):
+        if rowsum_dev is None:
+            rowsum_dev = dev(q_ref.astype(np.int64).sum(axis=1).astype(np.int32))
+        y2, acc2 = bl.forward(packed_dev, gamma_dev, xq_dev, absmax_dev, n, algo=algo,
+                              want_acc=True, rowsum=rowsum_dev)
+        bad = int(np.count_nonzero(host(acc2) != acc_ref))
+        assert bad == 0, f"{bad} of {a.size} int32 sums differ ({algo}, rowsum given)"
+        assert np.array_equal(host(y2).view(np.uint32), yh.view(np.uint32))
     return a
 
 
@@ -308,11 +320,12 @@ def test_workload_full_size(bl, widx, mi):
     del weights
     for t in w.tokens:
         x = w.activations(mi, t)
-        xq, absmax, q_ref, a_ref = check_quant(bl, x, w.x_dtype)
+        xq, absmax, q_ref, a_ref, rowsum = check_quant(bl, x, w.x_dtype)
         algos = ["auto"] + (["gemv", "gemm", "lut", "dot4"] if widx == 3 else []) + (
             ["lut", "dot4"] if widx == 2 else [])
         for algo in algos:
-            check_forward(bl, packed, gamma, xq, absmax, tern, q_ref, gamma_ref, a_ref, algo)
+            check_forward(bl, packed, gamma, xq, absmax, tern, q_ref, gamma_ref, a_ref, algo,
+                          rowsum_dev=rowsum)
     if widx in (2, 5):
         # the ternary zero fraction of Gaussian weights, about 31%
         assert abs(float(np.mean(tern == 0)) - 0.3101) < 0.005
