@@ -672,6 +672,9 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_STAGES
 #define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
 #endif
+#ifndef BL_GEMM_WIDE_LAYOUT
+#define BL_GEMM_WIDE_LAYOUT 1       // waves along M of the 128 x 512 tiles (1, 2 or 4)
+#endif
 #ifndef BL_GEMM_SPLIT_ITEMS
 #define BL_GEMM_SPLIT_ITEMS 256     // K split: (part, tile) items aimed for
 #endif
@@ -719,8 +722,19 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
   }
   switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true)) {
     case Tiles::kWide:
+#if BL_GEMM_WIDE_LAYOUT == 2
+      return run_lds<8, 2, 2, 4, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
+#elif BL_GEMM_WIDE_LAYOUT == 4
+      return run_lds<8, 4, 1, 8, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
+#elif BL_GEMM_WIDE_LAYOUT == 8
+      return run_lds<8, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
+#else
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
+#endif
     case Tiles::kNarrow:
       return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);

@@ -701,6 +701,254 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   }
 }
 
+// Persistent decode kernel for one raw (bf16 / f32) token over many 16-row
+// tiles, step A1 fused (the 70B-class shapes, hundreds to thousands of
+// tiles): a grid of a few blocks per CU, each block taking tiles b, b + G,
+// b + 2G, ... (G blocks), so that the tiles read at any moment are
+// neighbours in memory.  The block's waves split K as in k_gemv_dec (wave w
+// owns chunks w*per .. w*per+per-1 of every tile), but the token is fetched
+// and quantised once per block instead of once per tile, each wave's sum of
+// q over its k run is formed once, and every wave keeps the weight loads of
+// its next DEPTH - 1 tiles in flight while it contracts the current one,
+// chunk by chunk as they land.  Each tile has its own LDS slot (16 partial
+// sums and a counter); the last wave to add into it writes the tile's 16
+// outputs.  (On int8 input the same structure measured slower than
+// k_gemv_dec's block per tile, so it serves the fused calls only.)
+//
+// The int8 row sits in LDS slice-major: chunk c, lane group qg, slice j
+// hold the four dwords {4u + j : u = 0..3} of the group's 64 k, so one
+// ds_read_b128 is one MFMA B operand.  Each wave writes and reads only its
+// own k run (no block barrier between them).
+constexpr int persist_head(int tpb) { return ((16 + 17 * tpb + 1) * 4 + 15) / 16 * 16; }
+
+// byte offset, in a chunk's 256 bytes, of dword d (k = 4d .. 4d + 3) in the
+// slice-major order
+__device__ __forceinline__ int slice_off(int d) {
+  return (d >> 4) * 64 + (d & 3) * 16 + ((d >> 2) & 3) * 4;
+}
+
+// Calls f(integral_constant<int, J>) for J = 0 .. sizeof...(J) - 1, in order.
+template <class F, int... J>
+__device__ __forceinline__ void for_each_c(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+
+// HOLD_B: the B operands (the wave's int8 activations, the same for every
+// tile) may stay in registers across tiles; otherwise they are read from LDS
+// again for every tile (long K: 16 registers per chunk would not fit).
+template <int CPW, int MODE, int DEPTH, bool HOLD_B>
+__global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int nwaves, int tpb) {
+  static_assert(DEPTH >= 2 && DEPTH <= 4 && DEPTH * CPW < 64, "tiles in flight");
+  static_assert(MODE != kInt8, "raw activations (step A1 fused)");
+  extern __shared__ __align__(16) unsigned char smem[];
+  __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
+                   "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
+                   "s"(pr.per), "s"(nwaves), "s"(tpb));
+  const int N = pr.N, K = pr.K, per = pr.per;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int tiles = (N + 15) >> 4;
+  const int ntb = (tiles - b + G - 1) / G;          // this block's tiles: DEPTH <= ntb <= tpb (host)
+  const int lane = threadIdx.x & 63, nthreads = nwaves * 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qg = lane >> 4, r = lane & 15;
+  const int K16 = K >> 4;
+  const int nchunks = K >> 8;
+  const int c0 = wave * per;
+  const int cnt = min(per, nchunks - c0);           // >= 1: the host sizes nwaves to the chunks
+
+  // LDS: 16 zero ints | tpb x 16 partial sums | tpb counters | absmax bits | int8 row
+  int* zero = reinterpret_cast<int*>(smem);
+  int* slot = zero + 16;
+  int* counter = slot + 16 * tpb;
+  int* amax = counter + tpb;
+  unsigned char* xs8 = smem + persist_head(tpb);
+
+  // the raw token first (vector memory returns in issue order): the four
+  // values per chunk this lane quantises, into registers (slots past cnt
+  // repeat the row's last chunk and feed only the absmax)
+  const int run0 = c0 * 256;
+  uint4 xin[CPW];
+  {
+    const unsigned char* xr = static_cast<const unsigned char*>(pr.x);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int k0 = min(c0 + u, nchunks - 1) * 256 + 4 * lane;
+      if constexpr (MODE == kBf16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
+        xin[u] = make_uint4(v.x, v.y, 0u, 0u);
+      } else {
+        xin[u] = *reinterpret_cast<const uint4*>(xr + 4 * k0);
+      }
+    }
+  }
+  const float g = pr.gamma[0];
+  for (int i = threadIdx.x; i < 16 + 17 * tpb + 1; i += nthreads) zero[i] = 0;
+  lds_sync();   // every activation load of the block is issued ahead of every weight load
+
+  // weight loads of one tile into buffer D: this lane's 16 bytes of each of
+  // the wave's chunks (slots past cnt repeat the row's last chunk and meet a
+  // zero B operand)
+  uint4 buf[DEPTH][CPW];
+  auto issue = [&](auto dc, int it) {
+    constexpr int D = decltype(dc)::value;
+    int n = 16 * (b + it * G) + r;
+    n = n < N ? n : N - 1;                          // rows past N are computed, never stored
+    const uint4* wr = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) buf[D][i] = wr[(size_t)min(c0 + i, nchunks - 1) * 4];
+  };
+  for_each_c([&](auto dc) { issue(dc, decltype(dc)::value); }, std::make_integer_sequence<int, DEPTH>{});
+
+  // step A1 once per block: the token absmax over every wave's raw values
+  // (repeats included, which change nothing), then each lane quantises its
+  // own values into the wave's run of the int8 row in LDS (slice-major),
+  // summing q (lanes of token column 0)
+  int qsum = 0;
+  float a_t;
+  wait_vmem<DEPTH * CPW>();                         // the raw loads landed
+  {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const uint4 v = xin[u];
+      if constexpr (MODE == kBf16) {
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        const uint32_t m = 0x7fff7fffu;
+        const us2 h = __builtin_elementwise_max(__builtin_bit_cast(us2, v.x & m),
+                                                __builtin_bit_cast(us2, v.y & m));
+        mx = max(mx, (uint32_t)max(h.x, h.y) << 16);
+      } else {
+        mx = max(mx, max(max(v.x & 0x7fffffffu, v.y & 0x7fffffffu),
+                         max(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
+      }
+    }
+    const int wm = wave_max_nonneg((int)mx);
+    if (lane == 0) atomicMax(&amax[0], wm);
+    lds_sync();
+    a_t = __uint_as_float((uint32_t)amax[0]);
+    const float s = kQb / fmaxf(a_t, kEps);
+    const bool first = b == 0;
+    int tsum = 0;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      if (u >= cnt) break;                          // wave-uniform
+      const int k0 = run0 + u * 256 + 4 * lane;
+      const uint4 v = xin[u];
+      float f[4];
+      if constexpr (MODE == kBf16) {
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+      } else {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+      }
+      int q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        q[e] = (int)fminf(fmaxf(rintf(f[e] * s), -kQb), kQb);   // one binary32 product
+      const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x04000c0cu);
+      const uint32_t word = lo | hi;
+      tsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, tsum, false);
+      *reinterpret_cast<uint32_t*>(xs8 + run0 + u * 256 + slice_off(lane)) = word;
+      if (first && pr.xq_out) *reinterpret_cast<uint32_t*>(pr.xq_out + k0) = word;
+    }
+    const int sum = wave_sum_i(tsum);
+    if (r == 0) qsum = sum;
+    if (first && wave == 0 && pr.absmax_out && lane == 0) pr.absmax_out[0] = a_t;
+  }
+  const float sc = out_scale(g, a_t);
+
+  // one tile: contract each chunk as its loads land, add the partial sums
+  // (the last wave to add writes the outputs), then, with REFILL, issue the
+  // loads of tile it + DEPTH into the freed buffer.  WAIT is the number of
+  // this wave's loads of later tiles in flight.  The refill is never
+  // conditional inside a step: the compiler's own waits after a branch that
+  // may or may not have issued loads assume the worst and would wait for the
+  // loads just issued.
+  auto step = [&](auto dc, auto wc, auto rc, int it) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int WAIT = decltype(wc)::value;
+    constexpr bool REFILL = decltype(rc)::value;
+    if constexpr (!HOLD_B) __asm__ volatile("" ::: "memory");   // read B from LDS again
+    v4i a1 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0}, a16 = {0, 0, 0, 0};
+    for_each_c([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      wait_vmem<WAIT + CPW - 1 - i>();              // chunk i of this tile landed
+      const unsigned char* xb = (r == 0 && i < cnt) ? xs8 + (run0 + i * 256 + qg * 64)
+                                                    : reinterpret_cast<const unsigned char*>(zero);
+      auto xs = [&](int j) {
+        return *reinterpret_cast<const v4i*>(xb + ((r == 0 && i < cnt) ? 16 * j : 0));
+      };
+      const uint4 w4 = buf[D][i];
+      a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x03030303u), (int)(w4.y & 0x03030303u), (int)(w4.z & 0x03030303u),
+               (int)(w4.w & 0x03030303u)}),
+          xs(0), a1, 0, 0, 0);
+      a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x0C0C0C0Cu), (int)(w4.y & 0x0C0C0C0Cu), (int)(w4.z & 0x0C0C0C0Cu),
+               (int)(w4.w & 0x0C0C0C0Cu)}),
+          xs(1), a4, 0, 0, 0);
+      a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)(w4.x & 0x30303030u), (int)(w4.y & 0x30303030u), (int)(w4.z & 0x30303030u),
+               (int)(w4.w & 0x30303030u)}),
+          xs(2), a16, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          (v4i{(int)((w4.x >> 6) & 0x03030303u), (int)((w4.y >> 6) & 0x03030303u),
+               (int)((w4.z >> 6) & 0x03030303u), (int)((w4.w >> 6) & 0x03030303u)}),
+          xs(3), a1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }, std::make_integer_sequence<int, CPW>{});
+    if constexpr (REFILL) issue(dc, it + DEPTH);   // ahead of the epilogue's LDS and store work
+    // lane (qg, 0) holds rows 4qg + v of token 0
+    if (r == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        atomicAdd(&slot[16 * it + 4 * qg + v], a1[v] + (a4[v] >> 2) + (a16[v] >> 4) - qsum);
+    }
+    int ticket = 0;
+    if (lane == 0)
+      ticket = __hip_atomic_fetch_add(&counter[it], 1, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket == nwaves - 1 && lane < 16) {
+      const int n = 16 * (b + it * G) + lane;
+      if (n < N) {
+        const int sum = __hip_atomic_load(&slot[16 * it + lane], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (pr.acc) pr.acc[n] = sum;
+        pr.y[n] = (float)sum * sc;
+      }
+    }
+  };
+  // steady state: every step refills (tile it + DEPTH exists), and DEPTH - 1
+  // later tiles are in flight at each wait ...
+  int it = 0;
+  for (; it + 2 * DEPTH - 1 < ntb; it += DEPTH)
+    for_each_c([&](auto dc) {
+      step(dc, std::integral_constant<int, (DEPTH - 1) * CPW>{}, std::true_type{},
+           it + decltype(dc)::value);
+    }, std::make_integer_sequence<int, DEPTH>{});
+  // ... then the last R tiles (DEPTH <= R < 2 DEPTH), straight-line: step j
+  // refills while tile j + DEPTH exists and waits for the tiles after it
+  auto tail = [&](auto rc) {
+    constexpr int R = decltype(rc)::value;
+    for_each_c([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int AFTER = R - 1 - J < DEPTH - 1 ? R - 1 - J : DEPTH - 1;
+      step(std::integral_constant<int, J % DEPTH>{}, std::integral_constant<int, AFTER * CPW>{},
+           std::integral_constant<bool, (J + DEPTH < R)>{}, it + J);
+    }, std::make_integer_sequence<int, R>{});
+  };
+  const int left = ntb - it;
+  if (left == DEPTH) tail(std::integral_constant<int, DEPTH>{});
+  else if (left == DEPTH + 1) tail(std::integral_constant<int, DEPTH + 1>{});
+  else if constexpr (DEPTH >= 3) {
+    if (left == DEPTH + 2) tail(std::integral_constant<int, DEPTH + 2>{});
+    else if constexpr (DEPTH >= 4) { if (left == DEPTH + 3) tail(std::integral_constant<int, DEPTH + 3>{}); }
+  }
+}
+
 // Launch-shape tunables (compile-time so variants can be built and compared).
 #ifndef BL_GEMV_U
 #define BL_GEMV_U 2          // chunks whose loads a wave issues together (6912 -> 2560
@@ -901,6 +1149,71 @@ hipError_t run_dec(DecGroup& grp, int count, const DecShape& sh, size_t lds,
   return hipGetLastError();
 }
 
+#ifndef BL_GEMV_PERSIST_MIN_TILES
+#define BL_GEMV_PERSIST_MIN_TILES 512   // 16-row tiles from which one token takes the persistent kernel
+#endif
+#ifndef BL_GEMV_PERSIST_BPC
+#define BL_GEMV_PERSIST_BPC 2           // blocks per CU
+#endif
+#ifndef BL_GEMV_PERSIST_CPW
+#define BL_GEMV_PERSIST_CPW 2           // 256-k chunks per wave aimed for (at most 16 waves)
+#endif
+constexpr int kPersistMaxK = 28672;     // at most 7 chunks per wave at 16 waves
+
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+bool persist_ok(int64_t t, int64_t n, int64_t k) {
+  return t == 1 && k % 256 == 0 && k <= kPersistMaxK &&
+         (n + 15) / 16 >= BL_GEMV_PERSIST_MIN_TILES;
+}
+
+// Tiles in flight per wave and whether the B operands stay in registers, by
+// chunks per wave: about 128 KiB of weight loads in flight per CU at 16 waves.
+#ifndef BL_GEMV_PERSIST_DEPTH
+#define BL_GEMV_PERSIST_DEPTH 2         // tiles in flight per wave; 0: by chunks per wave
+#endif
+constexpr int persist_depth(int cpw) {
+  return BL_GEMV_PERSIST_DEPTH ? (BL_GEMV_PERSIST_DEPTH * cpw < 64 ? BL_GEMV_PERSIST_DEPTH : 2)
+                               : cpw <= 2 ? 4 : cpw <= 4 ? 3 : 2;
+}
+
+template <int MODE, int CPW>
+hipError_t launch_persist_cpw(const DecProblem& pr, int g, int nw, int tpb, size_t lds,
+                              hipStream_t stream) {
+  k_gemv_persist<CPW, MODE, persist_depth(CPW), (CPW <= 2)>
+      <<<g, nw * 64, lds, stream>>>(pr, nw, tpb);
+  return hipGetLastError();
+}
+
+// One raw token, one problem (plain outputs), many tiles: the persistent kernel.
+template <int MODE>
+hipError_t run_persist(DecProblem pr, hipStream_t stream) {
+  const int tiles = (pr.N + 15) / 16, nchunks = pr.K / 256;
+  int per = BL_GEMV_PERSIST_CPW;
+  if ((nchunks + per - 1) / per > 16) per = (nchunks + 15) / 16;
+  const int nw = (nchunks + per - 1) / per;
+  pr.per = per;
+  const int cpw = per <= 2 ? 2 : per <= 4 ? 4 : 7;
+  int g = device_cus() * BL_GEMV_PERSIST_BPC;
+  if (g > tiles / persist_depth(cpw)) g = tiles / persist_depth(cpw);   // DEPTH tiles per block at least
+  const int tpb = (tiles + g - 1) / g;
+  const size_t lds = persist_head(tpb) + (size_t)pr.K;
+  if (cpw == 2) return launch_persist_cpw<MODE, 2>(pr, g, nw, tpb, lds, stream);
+  if (cpw == 4) return launch_persist_cpw<MODE, 4>(pr, g, nw, tpb, lds, stream);
+  return launch_persist_cpw<MODE, 7>(pr, g, nw, tpb, lds, stream);
+}
+
 bool dec_ok(int64_t t, int64_t k, const void* packed, const void* xq) {
   return dec_shape_ok(t, k, 0) && (reinterpret_cast<uintptr_t>(packed) % 16) == 0 &&
          (reinterpret_cast<uintptr_t>(xq) % 16) == 0;
@@ -932,6 +1245,14 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
             (reinterpret_cast<uintptr_t>(probs[i].x) % 16) == 0 &&
             (reinterpret_cast<uintptr_t>(probs[i].packed) % 16) == 0;
     work += (probs[i].N + 15) / 16 * probs[i].K;
+  }
+  if (count == 1 && fused && persist_ok(t, probs[0].N, probs[0].K)) {
+    // one token over many tiles: the persistent kernel quantises once per block
+    const bl_linear& q = probs[0];
+    const DecProblem pr{reinterpret_cast<const uint32_t*>(q.packed), q.gamma, q.x, nullptr, q.y,
+                        q.acc, q.xq, q.absmax, nullptr, nullptr, (int)q.N, (int)q.K, 0,
+                        (int)q.N, nullptr};
+    return bf16 ? run_persist<kBf16>(pr, stream) : run_persist<kF32>(pr, stream);
   }
   if (!fuse_work_ok(t, work)) fused = false;
   if (!fused) {  // act-quant then forward (kernel chosen by T), problem by problem

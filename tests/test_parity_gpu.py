@@ -211,7 +211,13 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # table-lookup kernel: 4-wave blocks with word loads and a short last chunk
               (40, 900, 3088),
               # decode kernel, several int8 tokens, 257 row tiles: two per block
-              (9, 4100, 1024)]
+              (9, 4100, 1024),
+              # one int8 token over 512 tiles and more: ragged last tiles,
+              # a short last wave (K = 2304: 9 chunks), one chunk per row,
+              # 4 and 7 chunks per wave, K = 32768
+              (1, 8200, 2304), (1, 12288, 1024), (1, 20480, 512), (1, 16384, 256),
+              (1, 30000, 1024), (1, 9000, 16384), (1, 8192, 32768),
+              (1, 24576, 512), (1, 20480, 8448), (1, 12288, 16640)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
@@ -447,6 +453,15 @@ GROUPS = {
     "t1_bf16_eight_chunks_per_wave": (1, "bf16", [(16384, 300)]),
     # many row blocks: fused at one token (8.4M staged elements, under 16M)
     "t1_bf16_many_blocks": (1, "bf16", [(8192, 8200), (8192, 8200)]),
+    # one problem over many tiles: the persistent kernel quantises once per
+    # block (bf16 and f32, ragged rows, 2, 4 and 7 chunks per wave; 2 or 3
+    # tiles per block, 3 to 5, 3 or 4)
+    "t1_bf16_persistent": (1, "bf16", [(8192, 8200)]),
+    "t1_f32_persistent_ragged": (1, "f32", [(2304, 9000)]),
+    "t1_bf16_persistent_k28672": (1, "bf16", [(28672, 8192)]),
+    "t1_bf16_persistent_k16384": (1, "bf16", [(16384, 9000)]),
+    "t1_f32_persistent_many_tiles": (1, "f32", [(1024, 30000)]),
+    "t1_bf16_persistent_k12288": (1, "bf16", [(12288, 20480)]),
     # one token, K = 28672: fused, the raw row held in registers (14 waves of 8 chunks)
     "t1_k28672_fused": (1, "bf16", [(28672, 100)]),
     # one token whose int8 row does not fit the LDS limit: act-quant runs separately
