@@ -57,7 +57,7 @@ SIGNATURES["bitlinear_linear_grouped"] = (_c_int, [ctypes.POINTER(BlLinear), _c_
 SIGNATURES["bitlinear_pack_weights_noalloc"] = (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp])
 SIGNATURES["bitlinear_calib_sink_len"] = (_c_i64, [])
 SIGNATURES["bitlinear_calib_empty"] = (_c_int, [_c_vp])
-SIGNATURES["bitlinear_calib_read"] = (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp])
+SIGNATURES["bitlinear_calib_read"] = (_c_int, [_c_vp, _c_i64, _c_int, _c_vp, _c_vp])
 SIGNATURES["bitlinear_calib_mfma"] = (_c_int, [_c_i64, _c_int, _c_vp, _c_vp])
 
 
@@ -390,10 +390,16 @@ def calib_empty(device=None):
     _check(load().bitlinear_calib_empty(_stream(dev)))
 
 
-def calib_read(buf, sink=None):
+#: layouts of calib_read (bl_read_layout)
+READ_CHUNKS, READ_STRIDE = 0, 1
+
+
+def calib_read(buf, layout=READ_CHUNKS, sink=None):
     """Read the whole of `buf` (a contiguous CUDA tensor, 16-byte aligned, size a
-    multiple of 16 bytes) at full width; returns the int32 sink whose first 2048
-    entries XOR to the XOR of the buffer's 32-bit words."""
+    multiple of 16 bytes) at full width in `layout` (READ_CHUNKS: contiguous
+    32 KiB chunks per block; READ_STRIDE: a grid-stride loop); returns the int32
+    sink whose 4096 entries (one per wave) XOR to the XOR of the buffer's 32-bit
+    words."""
     lib = load()
     _need_cuda(buf, "buf")
     nbytes = buf.numel() * buf.element_size()
@@ -401,7 +407,8 @@ def calib_read(buf, sink=None):
         sink = torch.empty(lib.bitlinear_calib_sink_len(), dtype=torch.int32, device=buf.device)
     _need_cuda(sink, "sink", torch.int32)
     _need_shape(sink, "sink", (lib.bitlinear_calib_sink_len(),))
-    _check(lib.bitlinear_calib_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
+    _check(lib.bitlinear_calib_read(_ptr(buf), nbytes, int(layout), _ptr(sink),
+                                    _stream(buf.device)))
     return sink
 
 

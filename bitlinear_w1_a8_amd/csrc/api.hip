@@ -268,15 +268,19 @@ bl_status bitlinear_calib_empty(void* stream) {
   return launched("bitlinear_calib_empty", bl::launch_calib_empty(static_cast<hipStream_t>(stream)));
 }
 
-bl_status bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+bl_status bitlinear_calib_read(const void* buf, int64_t bytes, int layout, uint32_t* sink,
+                               void* stream) {
   const char* fn = "bitlinear_calib_read";
   if (!buf || !sink) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
   if (bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40))
     return fail(BL_ERR_SHAPE, "%s: bytes=%lld must be a positive multiple of 16, at most 2^40", fn,
                 (long long)bytes);
+  if (layout != BL_READ_CHUNKS && layout != BL_READ_STRIDE)
+    return fail(BL_ERR_ARG, "%s: unknown layout %d (BL_READ_CHUNKS or BL_READ_STRIDE)", fn, layout);
   if (!aligned(buf, 16) || !aligned(sink, 4))
     return fail(BL_ERR_ALIGN, "%s: buf needs 16-byte, sink 4-byte alignment", fn);
-  return launched(fn, bl::launch_calib_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+  return launched(fn, bl::launch_calib_read(buf, bytes, layout, sink,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 bl_status bitlinear_calib_mfma(int64_t iters, int byte, int32_t* sink, void* stream) {

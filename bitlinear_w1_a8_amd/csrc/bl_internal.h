@@ -18,18 +18,23 @@ constexpr float kQb = 127.0f;
 // auto_algo for the rule per shape.
 constexpr int64_t kGemvMaxTokens = 64;
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 // The automatic kernel choice of bitlinear_forward: BL_ALGO_GEMV (the decode
 // kernels) or BL_ALGO_GEMM (the tiled MFMA kernel), by shape (gemv.hip).
 int auto_algo(int64_t t, int64_t n, int64_t k);
 
 // Measurement helpers (calib.hip): the launch floor, the HBM read stream and
-// the int8 matrix-core rate of the device; the read writes kCalibReadBlocks
-// sink entries, the MFMA loop kCalibMfmaWaves.
-constexpr int kCalibReadBlocks = 2048;
+// the int8 matrix-core rate of the device; the read writes one sink entry per
+// wave (kCalibReadBlocks blocks of four), the MFMA loop kCalibMfmaWaves.
+constexpr int kCalibReadBlocks = 1024;
 constexpr int kCalibMfmaWaves = 4096;
 constexpr int64_t kCalibSinkLen = 4096;
 hipError_t launch_calib_empty(hipStream_t stream);
-hipError_t launch_calib_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+constexpr int kReadChunks = 0, kReadStride = 1;   // bl_read_layout
+hipError_t launch_calib_read(const void* buf, int64_t bytes, int layout, uint32_t* sink,
+                             hipStream_t stream);
 hipError_t launch_calib_mfma(int iters, int byte, int32_t* sink, hipStream_t stream);
 
 // Exponent buckets of the exact gamma sum: one uint64 per binary32 exponent.
@@ -138,6 +143,15 @@ __device__ __forceinline__ int wave_max_nonneg(int v) {
   v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));  // row_mirror
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_xor_u(uint32_t u) {
+  int v = (int)u;
+  v ^= __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v ^= __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v ^= __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v ^= __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return (uint32_t)(__builtin_amdgcn_readlane(v, 0) ^ __builtin_amdgcn_readlane(v, 16) ^
+                    __builtin_amdgcn_readlane(v, 32) ^ __builtin_amdgcn_readlane(v, 48));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);

@@ -4,8 +4,8 @@
 //
 //  - an empty kernel: the launch floor a short kernel cannot go below;
 //  - a read of a large buffer at full width (16-byte loads, eight in flight
-//    per lane, a grid-stride loop over every CU): the HBM read stream that a
-//    weight-streaming kernel can hope for;
+//    per lane, over every CU) in two layouts: the HBM read stream that a
+//    weight-streaming kernel can hope for is the better of the two;
 //  - back-to-back v_mfma_i32_32x32x32_i8, the tiled kernel's instruction, on
 //    register operands: the int8 matrix-core rate at the clock the device
 //    holds under that load.
@@ -17,28 +17,57 @@ namespace {
 
 __global__ void k_calib_empty() {}
 
-// Each block leaves the XOR of all 32-bit words it read in sink[blockIdx.x].
+// Each wave leaves the XOR of all 32-bit words it read in
+// sink[4 * blockIdx.x + wave].  Each lane keeps eight 16-byte loads in
+// flight, in one of two layouts:
+//  kReadChunks  - blocks take contiguous 32 KiB chunks (chunk c goes to block
+//                 c % gridDim.x); a lane's loads are 4 KiB apart;
+//  kReadStride  - a grid-stride loop; a lane's loads are a whole grid apart
+//                 (4 MiB with 1024 blocks of 256 lanes).
+// On MI355X the power-of-two distance of the second layout costs 10-20% on
+// buffers of 64 MiB and more (4.65 against 5.65 TB/s at 64 MiB, rotated over
+// 20 buffers); the caller measures both.  Eight loads in flight over 1024
+// blocks read a 56 MiB buffer about 4% faster than four over 2048.  The
+// result is reduced per wave (DPP, no LDS and no barrier): the reduction and
+// the store at the end of the kernel cost about 0.5 us of a 10 us read.
+template <int LAYOUT>
 __global__ __launch_bounds__(256) void k_calib_read(const uint4* __restrict__ p, int64_t n16,
                                                     uint32_t* __restrict__ sink) {
+  constexpr int kU = 8;
   uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    uint4 v[8];
+  int64_t tail;                                     // first vector of the part left over
+  if constexpr (LAYOUT == kReadChunks) {
+    constexpr int64_t kChunk = 256 * kU;            // 16-byte vectors per chunk
+    const int64_t nch = n16 / kChunk;
+    for (int64_t c = blockIdx.x; c < nch; c += gridDim.x) {
+      const uint4* q = p + c * kChunk + threadIdx.x;
+      uint4 v[kU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+      for (int u = 0; u < kU; ++u) v[u] = q[u * 256];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    tail = nch * kChunk;
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * 256, round = kU * stride;
+    const int64_t whole = n16 / round * round;      // vectors covered by whole rounds
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < whole; i += round) {
+      uint4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    tail = whole;
   }
-  for (; i < n16; i += stride) {
+  // the rest, vector by vector over the whole grid
+  for (int64_t i = tail + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * 256) {
     const uint4 t = p[i];
     acc ^= t.x ^ t.y ^ t.z ^ t.w;
   }
-  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
-  __shared__ uint32_t part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+  acc = wave_xor_u(acc);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
 }
 
 // Every element of A and B is the int8 `byte` (a run-time value); four independent
@@ -63,16 +92,23 @@ __global__ __launch_bounds__(256) void k_calib_mfma(int iters, int byte, int32_t
 }  // namespace
 
 constexpr int kCalibMfmaBlocks = kCalibMfmaWaves / 4;   // four waves per SIMD on 256 CUs
-static_assert(kCalibReadBlocks <= kCalibSinkLen && kCalibMfmaWaves <= kCalibSinkLen, "sink length");
+static_assert(4 * kCalibReadBlocks <= kCalibSinkLen && kCalibMfmaWaves <= kCalibSinkLen,
+              "sink length");
 
 hipError_t launch_calib_empty(hipStream_t stream) {
   k_calib_empty<<<1, 64, 0, stream>>>();
   return hipGetLastError();
 }
 
-hipError_t launch_calib_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
-  k_calib_read<<<kCalibReadBlocks, 256, 0, stream>>>(static_cast<const uint4*>(buf), bytes / 16,
-                                                     sink);
+hipError_t launch_calib_read(const void* buf, int64_t bytes, int layout, uint32_t* sink,
+                             hipStream_t stream) {
+  const uint4* p = static_cast<const uint4*>(buf);
+  if (layout == kReadChunks)
+    k_calib_read<kReadChunks><<<kCalibReadBlocks, 256, 0, stream>>>(p, bytes / 16, sink);
+  else if (layout == kReadStride)
+    k_calib_read<kReadStride><<<kCalibReadBlocks, 256, 0, stream>>>(p, bytes / 16, sink);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

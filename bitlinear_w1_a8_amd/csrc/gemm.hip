@@ -283,8 +283,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   static_assert(WBITS == 1 || WBITS == 2, "one- or two-bit weights");
   constexpr int kBRow = BK * WBITS / 8;                    // packed bytes per row per K step
   constexpr int kABuf = BM * BK, kBBuf = BN * kBRow;       // bytes per stage
-  constexpr int kAChunks = BM / 8 / WAVES, kBChunks = kBBuf / 1024 / WAVES;  // 1 KiB loads per wave
-  static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the wave count");
+  // 1 KiB loads per stage: kATot of the activation tile, kBTot of the
+  // weights, shared out over the waves; where they do not divide evenly the
+  // last waves load the tile's last chunk again (the same bytes to the same
+  // LDS place), so every wave issues the same count
+  constexpr int kATot = BM / 8, kBTot = kBBuf / 1024;
+  constexpr int kAChunks = (kATot + WAVES - 1) / WAVES, kBChunks = (kBTot + WAVES - 1) / WAVES;
+  static_assert(kBBuf % 1024 == 0, "weight tile in whole 1 KiB chunks");
   __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf];
   __shared__ __align__(16) unsigned char A2[STAGES > 2 ? kABuf : 16];
   __shared__ __align__(16) unsigned char A3[STAGES > 3 ? kABuf : 16];
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   uint32_t aoff[kAChunks];
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
-    const int c = wave * kAChunks + i;
+    const int c = min(wave * kAChunks + i, kATot - 1);
     const int r = 8 * c + (lane >> 3);
     const int slot = (lane & 7) ^ ((r >> 1) & 7);
     int tok = m0 + r;
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   uint32_t boff[kBChunks];
 #pragma unroll
   for (int i = 0; i < kBChunks; ++i) {
-    const int c = wave * kBChunks + i;
+    const int c = min(wave * kBChunks + i, kBTot - 1);
     if constexpr (WBITS == 2) {   // 1 KiB = 32 rows x 32 bytes
       int n = n0 + 32 * c + (lane >> 1);
       n = n < N ? n : N - 1;
@@ -387,11 +392,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(xq + (aoff[i] + k0)),
-                                       (lds_ptr_t)(As + (wave * kAChunks + i) * 1024), 16, 0, 0);
+                                       (lds_ptr_t)(As + min(wave * kAChunks + i, kATot - 1) * 1024),
+                                       16, 0, 0);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)))),
-                                       (lds_ptr_t)(Bs + (wave * kBChunks + i) * 1024), 16, 0, 0);
+                                       (lds_ptr_t)(Bs + min(wave * kBChunks + i, kBTot - 1) * 1024),
+                                       16, 0, 0);
   };
 
   v16i acc[WMF][WNF];
@@ -440,8 +447,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       // 16 bytes per lane, slot order irrelevant to a sum): sum of q
 #pragma unroll
       for (int i = 0; i < kAChunks; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(abuf(stage_c) +
-                                                        (wave * kAChunks + i) * 1024 + 16 * lane);
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            abuf(stage_c) + min(wave * kAChunks + i, kATot - 1) * 1024 + 16 * lane);
         int p = qpart[i];
         p = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, p, false);
         p = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, p, false);
@@ -516,7 +523,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
-      if ((lane & 7) == 0) rsum[8 * (wave * kAChunks + i) + (lane >> 3)] = v;
+      // a repeated chunk writes the same sums again
+      if ((lane & 7) == 0) rsum[8 * min(wave * kAChunks + i, kATot - 1) + (lane >> 3)] = v;
     }
     lds_sync();
   }
@@ -672,9 +680,6 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_STAGES
 #define BL_GEMM_STAGES 3            // LDS pipeline depth (tiles in flight + 1)
 #endif
-#ifndef BL_GEMM_WIDE_LAYOUT
-#define BL_GEMM_WIDE_LAYOUT 1       // waves along M of the 128 x 512 tiles (1, 2 or 4)
-#endif
 #ifndef BL_GEMM_SPLIT_ITEMS
 #define BL_GEMM_SPLIT_ITEMS 256     // K split: (part, tile) items aimed for
 #endif
@@ -685,6 +690,7 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #define BL_GEMM_SPLIT_MAX_TILES 128 // ... that make fewer than this many 64 x 128 tiles
 #endif
 
+
 namespace {
 
 // Tile shape of the LDS-direct kernel for a problem, from measurements on
@@ -692,16 +698,24 @@ namespace {
 // that still give most CUs a block, 64-row tiles (several blocks per CU) when
 // 128-row ones would leave CUs idle or rows unused, and a K split only for
 // long K with very few tiles.
-enum class Tiles { kWide, kNarrow, kM64W256, kM64W128, kSplit };
+enum class Tiles { kWide, kNarrow, kM64W256, kM64W320, kM64W128, kSplit };
 
-Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow_w128) {
+Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow_w128,
+                   bool allow_w320 = false) {
   const int64_t m128 = (t + 127) / 128, m64 = (t + 63) / 64;
   const int64_t wide = m128 * ((n + 511) / 512), narrow = m128 * ((n + 255) / 256);
   const int64_t w256 = m64 * ((n + 255) / 256), w128 = m64 * ((n + 127) / 128);
   const bool rows_used = 10 * t >= 9 * 128 * m128;   // 128-row tiles at least 90% full
   if (wide >= BL_GEMM_WIDE_MIN_TILES) return Tiles::kWide;
   if (narrow >= BL_GEMM_NARROW_MIN_TILES && rows_used) return Tiles::kNarrow;
-  if (w256 >= BL_GEMM_M64_MIN_TILES || !allow_w128) return Tiles::kM64W256;
+  if (w256 >= BL_GEMM_M64_MIN_TILES || !allow_w128) {
+    // 64 x 256 tiles that would spill into a second round, where 64 x 320
+    // tiles fill the CUs once (2048 x 6912 -> 2560: 320 against 256 tiles,
+    // 48.5 -> 43.9 us; 128 x 160 tiles measured 46.0 us)
+    const int64_t cus = device_cus(), w320 = m64 * ((n + 319) / 320);
+    if (allow_w320 && w256 > cus && 8 * w320 >= 7 * cus && w320 <= cus) return Tiles::kM64W320;
+    return Tiles::kM64W256;
+  }
   if (allow_split && k >= BL_GEMM_SPLIT_MIN_K && w128 < BL_GEMM_SPLIT_MAX_TILES && k / BK >= 8)
     return Tiles::kSplit;
   return Tiles::kM64W128;
@@ -720,26 +734,18 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
     return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   }
-  switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true)) {
+  switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true, true)) {
     case Tiles::kWide:
-#if BL_GEMM_WIDE_LAYOUT == 2
-      return run_lds<8, 2, 2, 4, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
-                                                 1, 0, nullptr, nullptr, rowsum);
-#elif BL_GEMM_WIDE_LAYOUT == 4
-      return run_lds<8, 4, 1, 8, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
-                                                 1, 0, nullptr, nullptr, rowsum);
-#elif BL_GEMM_WIDE_LAYOUT == 8
-      return run_lds<8, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
-                                                 1, 0, nullptr, nullptr, rowsum);
-#else
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
-#endif
     case Tiles::kNarrow:
       return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W256:
       return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                 1, 0, nullptr, nullptr, rowsum);
+    case Tiles::kM64W320:
+      return run_lds<4, 2, 1, 5, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W128:
       return run_lds<4, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,

@@ -1160,19 +1160,6 @@ hipError_t run_dec(DecGroup& grp, int count, const DecShape& sh, size_t lds,
 #endif
 constexpr int kPersistMaxK = 28672;     // at most 7 chunks per wave at 16 waves
 
-// Compute units of the current device, looked up once per device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-    v = 256;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
 bool persist_ok(int64_t t, int64_t n, int64_t k) {
   return t == 1 && k % 256 == 0 && k <= kPersistMaxK &&
          (n + 15) / 16 >= BL_GEMV_PERSIST_MIN_TILES;
@@ -1232,6 +1219,18 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
 }
 
 }  // namespace
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int bf16,
                                hipStream_t stream) {

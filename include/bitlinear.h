@@ -351,13 +351,23 @@ int64_t bitlinear_calib_sink_len(void);
 /* One empty kernel on `stream`: the cost of a launch with no work. */
 bl_status bitlinear_calib_empty(void* stream);
 
+/* Layouts of bitlinear_calib_read: which 16-byte vectors a lane keeps in
+ * flight (eight at a time). */
+typedef enum {
+  BL_READ_CHUNKS = 0, /* blocks take contiguous 32 KiB chunks; a lane's loads 4 KiB apart */
+  BL_READ_STRIDE = 1  /* grid-stride loop; a lane's loads one grid (4 MiB) apart */
+} bl_read_layout;
+
 /* Reads the `bytes` bytes at `buf` (device, 16-byte aligned; `bytes` a
  * positive multiple of 16, at most 2^40) once, with 16-byte loads over a
- * grid that fills the device.  sink[i] for i < 2048 receives the XOR of the
- * 32-bit words that block i read, so the XOR of those 2048 entries is the
- * XOR of the whole buffer; the rest of the sink is not written.
- * Errors: BL_ERR_NULL, BL_ERR_SHAPE (bytes), BL_ERR_ALIGN. */
-bl_status bitlinear_calib_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+ * grid of 1024 blocks of four waves that fills the device, in the given
+ * bl_read_layout.  sink[w] for w < 4096 receives the XOR of the 32-bit words
+ * that wave w read, so the XOR of those 4096 entries is the XOR of the whole
+ * buffer.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (bytes), BL_ERR_ARG (layout),
+ * BL_ERR_ALIGN. */
+bl_status bitlinear_calib_read(const void* buf, int64_t bytes, int layout, uint32_t* sink,
+                               void* stream);
 
 /* 4096 waves (four per SIMD on 256 CUs) each issue `iters` rounds of four
  * independent v_mfma_i32_32x32x32_i8 with every element of A and B equal to

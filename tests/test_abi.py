@@ -259,13 +259,17 @@ def test_calib_errors(lib):
     """The measurement helpers check their arguments like every other call."""
     assert lib.bitlinear_calib_sink_len() == 4096
     r = lib.bitlinear_calib_read
-    assert r(None, 1024, A16, None) == BL_ERR_NULL
-    assert r(A16, 1024, None, None) == BL_ERR_NULL
-    assert r(A16, 0, A16, None) == BL_ERR_SHAPE
-    assert r(A16, 1000, A16, None) == BL_ERR_SHAPE                  # not a multiple of 16
-    assert r(A16, (1 << 40) + 16, A16, None) == BL_ERR_SHAPE
-    assert r(A16 + 8, 1024, A16, None) == BL_ERR_ALIGN
-    assert r(A16, 1024, A_ODD, None) == BL_ERR_ALIGN
+    for lay in (0, 1):
+        assert r(None, 1024, lay, A16, None) == BL_ERR_NULL
+        assert r(A16, 1024, lay, None, None) == BL_ERR_NULL
+        assert r(A16, 0, lay, A16, None) == BL_ERR_SHAPE
+        assert r(A16, 1000, lay, A16, None) == BL_ERR_SHAPE         # not a multiple of 16
+        assert r(A16, (1 << 40) + 16, lay, A16, None) == BL_ERR_SHAPE
+        assert r(A16 + 8, 1024, lay, A16, None) == BL_ERR_ALIGN
+        assert r(A16, 1024, lay, A_ODD, None) == BL_ERR_ALIGN
+    assert r(A16, 1024, 2, A16, None) == BL_ERR_ARG
+    assert r(A16, 1024, -1, A16, None) == BL_ERR_ARG
+    assert "layout" in (r(A16, 1024, 2, A16, None) and _err(lib))
     m = lib.bitlinear_calib_mfma
     assert m(16, 1, None, None) == BL_ERR_NULL
     assert m(0, 1, A16, None) == BL_ERR_ARG

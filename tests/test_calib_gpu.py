@@ -1,6 +1,6 @@
 """The measurement helpers do the work they claim (needs a HIP device).
 
-The read helper must touch every byte: the XOR of its per-block results has
+The read helper must touch every byte: the XOR of its per-wave results has
 to equal the XOR of the buffer's 32-bit words computed on the host.  The
 matrix-core loop must run every MFMA: each wave's result is the closed form
 4 * iters * 32 * byte^2 (mod 2^32).
@@ -21,14 +21,19 @@ def bl(built_lib):
     return binding
 
 
-@pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, 64 << 20])
-def test_calib_read_touches_every_word(bl, nbytes):
-    rng = np.random.default_rng(nbytes)
+# sizes: one vector; less than a chunk; chunks plus a ragged tail; whole
+# grid-stride rounds (1024 blocks x 256 lanes x 8 loads of 16 bytes) plus a
+# tail; 64 MiB; 56 MiB + 48 bytes
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, (1024 * 256 * 16 * 8) * 3 + 4112,
+                                    64 << 20, (56 << 20) + 48])
+def test_calib_read_touches_every_word(bl, nbytes, layout):
+    rng = np.random.default_rng(nbytes + layout)
     words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).cuda()
-    sink = bl.calib_read(buf)
+    sink = bl.calib_read(buf, layout)
     torch.cuda.synchronize()
-    got = np.bitwise_xor.reduce(sink[:2048].cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
 
 
