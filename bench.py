@@ -574,7 +574,8 @@ def crossover_extra(torch, mats, sets, dev, stream, calls):
 
 def prefill_extra(torch, binding, wl, dev, stream):
     """Context: prefill (T = 2048) on both 2B shapes, TOP/s of the tiled MFMA
-    kernel alone and of act-quant + kernel.  As in a model, where every layer
+    kernel alone and of act-quant + kernel, each with the row sums derived in
+    the kernel and handed in from act-quant.  As in a model, where every layer
     has its own weights, consecutive calls rotate through 64 copies of the
     packed matrix."""
     wk = wl.WORKLOADS[4]
@@ -604,12 +605,30 @@ def prefill_extra(torch, binding, wl, dev, stream):
             calls.forward(P[i], Q[0], Q[1], Q[2], t, m.n, m.k, Q[3], 2, h)
 
         us2 = rotated_time_us(torch, both, len(copies), stream, reps=4)
+        # the same with the tokens' row sums: act-quant writes them, the
+        # tiled kernel takes them instead of summing q in its K loop
+        rs = torch.empty(t, dtype=torch.int32, device=dev)
+        calls.quant(Q[4], Q[1], Q[2], t, m.k, ctypes.c_void_p(stream.cuda_stream), ptr(rs))
+        us3 = rotated_time_us(
+            torch, lambda s, i: calls.forward(P[i], Q[0], Q[1], Q[2], t, m.n, m.k, Q[3], 2,
+                                              ctypes.c_void_p(s.cuda_stream), ptr(rs)),
+            len(copies), stream, reps=4)
+
+        def both_rs(s, i):
+            h = ctypes.c_void_p(s.cuda_stream)
+            calls.quant(Q[4], Q[1], Q[2], t, m.k, h, ptr(rs))
+            calls.forward(P[i], Q[0], Q[1], Q[2], t, m.n, m.k, Q[3], 2, h, ptr(rs))
+
+        us4 = rotated_time_us(torch, both_rs, len(copies), stream, reps=4)
         ops = 2.0 * t * m.n * m.k
         out[f"{m.k}->{m.n}"] = {
             "gemm_us": round(us1, 2), "gemm_tops": round(ops / us1 / 1e6, 1),
             "gemm_frac_of_int8_peak": round(ops / us1 / 1e6 / INT8_PEAK_TOPS, 4),
             "quant_plus_gemm_us": round(us2, 2),
-            "quant_plus_gemm_tops": round(ops / us2 / 1e6, 1)}
+            "quant_plus_gemm_tops": round(ops / us2 / 1e6, 1),
+            "gemm_rowsum_given_us": round(us3, 2),
+            "gemm_rowsum_given_frac_of_int8_peak": round(ops / us3 / 1e6 / INT8_PEAK_TOPS, 4),
+            "quant_plus_gemm_rowsum_us": round(us4, 2)}
         del copies, packed
         torch.cuda.empty_cache()
     return out

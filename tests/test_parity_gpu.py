@@ -217,7 +217,10 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # 4 and 7 chunks per wave, K = 32768
               (1, 8200, 2304), (1, 12288, 1024), (1, 20480, 512), (1, 16384, 256),
               (1, 30000, 1024), (1, 9000, 16384), (1, 8192, 32768),
-              (1, 24576, 512), (1, 20480, 8448), (1, 12288, 16640)]
+              (1, 24576, 512), (1, 20480, 8448), (1, 12288, 16640),
+              # the longest rows the boundary takes (K = 131072: the largest
+              # sums, 127 K, are still exact in binary32)
+              (2, 40, 131072), (70, 300, 131072)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
