@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 2
+#define BITLINEAR_ABI_VERSION 3   /* 3: bitlinear_calib_read takes a layout */
 
 /* Largest K accepted: keeps every |acc| <= 127*K below 2^24, so the int32
  * sum converts to binary32 exactly. */
