@@ -328,7 +328,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   // (gated outputs: token l >> 3 of lane l, eight outputs per token)
   constexpr bool gated = GATED;
   float am = 0.0f;
-  if constexpr (MODE == kInt8) am = pr.absmax[min(lane / (gated ? kRows / 2 : kRows), T - 1)];
+  int rsv = 0;   // ... and, given, the token's row sum (both used by the epilogue's first pass)
+  if constexpr (MODE == kInt8) {
+    const int tl0 = min(lane / (gated ? kRows / 2 : kRows), T - 1);
+    am = pr.absmax[tl0];
+    if (pr.rowsum) rsv = pr.rowsum[tl0];
+  }
   // ... then the activations, straight into LDS (lane l's 16 bytes land at
   // the wave's base + 16 l): int8 input, this wave's own k run; raw input
   // (step A1 fused), the whole rows, shared by the block ...
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
       const int i = idx % (kRows / 2), tl = idx / (kRows / 2);
       const int nn = n0 + 2 * i;
       if (nn >= N) continue;
-      const int qt = MODE == kInt8 && pr.rowsum ? pr.rowsum[tl] : 0;
+      const int qt = MODE == kInt8 && pr.rowsum ? (idx < 64 ? rsv : pr.rowsum[tl]) : 0;
       const int sg = __hip_atomic_load(&tile[tl * kRows + 2 * i], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP) - qt;
       const int su = __hip_atomic_load(&tile[tl * kRows + 2 * i + 1], __ATOMIC_RELAXED,
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
     const int nn = n0 + i;
     if (nn >= N) continue;
     const int sum = __hip_atomic_load(&tile[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) -
-                    (MODE == kInt8 && pr.rowsum ? pr.rowsum[tl] : 0);
+                    (MODE == kInt8 && pr.rowsum ? (idx < 64 ? rsv : pr.rowsum[tl]) : 0);
     const int64_t o = (int64_t)tl * pr.ldy + nn;
     if (pr.acc) pr.acc[o] = sum;
     float a;                                        // the token's absmax (int8: lane's own first)
