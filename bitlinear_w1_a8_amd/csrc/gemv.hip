@@ -706,6 +706,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   }
 }
 
+#ifndef BL_GEMV_PERSIST_EARLY
+#define BL_GEMV_PERSIST_EARLY 2         // weight chunks per wave issued ahead of step A1
+#endif
+
 // Persistent decode kernel for one raw (bf16 / f32) token over many 16-row
 // tiles, step A1 fused (the 70B-class shapes, hundreds to thousands of
 // tiles): a grid of a few blocks per CU, each block taking tiles b, b + G,
@@ -794,15 +798,28 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
   // the wave's chunks (slots past cnt repeat the row's last chunk and meet a
   // zero B operand)
   uint4 buf[DEPTH][CPW];
-  auto issue = [&](auto dc, int it) {
-    constexpr int D = decltype(dc)::value;
+  // chunks LO .. HI - 1 of tile it into buffer D
+  auto issue_part = [&](auto dc, int it, auto loc, auto hic) {
+    constexpr int D = decltype(dc)::value, LO = decltype(loc)::value, HI = decltype(hic)::value;
     int n = 16 * (b + it * G) + r;
     n = n < N ? n : N - 1;                          // rows past N are computed, never stored
     const uint4* wr = reinterpret_cast<const uint4*>(pr.packed + (int64_t)n * K16) + qg;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) buf[D][i] = wr[(size_t)min(c0 + i, nchunks - 1) * 4];
+    for (int i = LO; i < HI; ++i) buf[D][i] = wr[(size_t)min(c0 + i, nchunks - 1) * 4];
   };
-  for_each_c([&](auto dc) { issue(dc, decltype(dc)::value); }, std::make_integer_sequence<int, DEPTH>{});
+  using C0 = std::integral_constant<int, 0>;
+  using CW = std::integral_constant<int, CPW>;
+  auto issue = [&](auto dc, int it) { issue_part(dc, it, C0{}, CW{}); };
+  // A few chunks of the first tile go ahead of step A1, the rest after it.
+  // A wave issues its instructions in order, and while the CU's memory queue
+  // is full (every wave asking for DEPTH x CPW weight vectors at once) loads
+  // are accepted only as data returns: with all of them issued first, every
+  // wave's absmax and quantisation waited behind the weight stream (one bf16
+  // row of 28672: the block's absmax done at a median of 9.3 us into the
+  // kernel, against 1.6 us now).  The early chunks keep HBM busy meanwhile.
+  constexpr int kEarly = BL_GEMV_PERSIST_EARLY < CPW ? BL_GEMV_PERSIST_EARLY : CPW;
+  using CE = std::integral_constant<int, kEarly>;
+  issue_part(std::integral_constant<int, 0>{}, 0, C0{}, CE{});
 
   // step A1 once per block: the token absmax over every wave's raw values
   // (repeats included, which change nothing), then each lane quantises its
@@ -810,7 +827,7 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
   // summing q (lanes of token column 0)
   int qsum = 0;
   float a_t;
-  wait_vmem<DEPTH * CPW>();                         // the raw loads landed
+  wait_vmem<kEarly>();                              // the raw loads landed
   {
     uint32_t mx = 0;
 #pragma unroll
@@ -863,6 +880,12 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     if (first && wave == 0 && pr.absmax_out && lane == 0) pr.absmax_out[0] = a_t;
   }
   const float sc = out_scale(g, a_t);
+  // the rest of the first DEPTH tiles' weight loads (chunk order per wave
+  // unchanged, which the waits below count on)
+  issue_part(std::integral_constant<int, 0>{}, 0, CE{}, CW{});
+  for_each_c([&](auto dc) {
+    if constexpr (decltype(dc)::value > 0) issue(dc, decltype(dc)::value);
+  }, std::make_integer_sequence<int, DEPTH>{});
 
   // one tile: contract each chunk as its loads land, add the partial sums
   // (the last wave to add writes the outputs), then, with REFILL, issue the
