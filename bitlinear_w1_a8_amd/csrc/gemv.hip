@@ -706,13 +706,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   }
 }
 
+#ifndef BL_GEMV_PERSIST_INT8_MAX_K
+// One int8 token over many tiles takes the persistent kernel for rows up to
+// this long (8192 -> 28672 at one token: 13.1-13.3 -> 12.7 us; on 28672-long
+// rows, seven chunks per wave, it measured 14.85 against 14.4 us)
+#define BL_GEMV_PERSIST_INT8_MAX_K 8192
+#endif
 #ifndef BL_GEMV_PERSIST_EARLY
 #define BL_GEMV_PERSIST_EARLY 2         // weight chunks per wave issued ahead of step A1
 #endif
 
-// Persistent decode kernel for one raw (bf16 / f32) token over many 16-row
-// tiles, step A1 fused (the 70B-class shapes, hundreds to thousands of
-// tiles): a grid of a few blocks per CU, each block taking tiles b, b + G,
+// Persistent decode kernel for one token over many 16-row tiles (the
+// 70B-class shapes, hundreds to thousands of tiles), raw (bf16 / f32, step
+// A1 fused) or int8: a grid of a few blocks per CU, each block taking tiles b, b + G,
 // b + 2G, ... (G blocks), so that the tiles read at any moment are
 // neighbours in memory.  The block's waves split K as in k_gemv_dec (wave w
 // owns chunks w*per .. w*per+per-1 of every tile), but the token is fetched
@@ -721,8 +727,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 // its next DEPTH - 1 tiles in flight while it contracts the current one,
 // chunk by chunk as they land.  Each tile has its own LDS slot (16 partial
 // sums and a counter); the last wave to add into it writes the tile's 16
-// outputs.  (On int8 input the same structure measured slower than
-// k_gemv_dec's block per tile, so it serves the fused calls only.)
+// outputs.  On int8 input the codes are copied into the row as they are
+// (with the token's row sum, if given, subtracted once); there it serves
+// rows of up to 8192 only (longer rows measured faster with k_gemv_dec's
+// block per tile).
 //
 // The int8 row sits in LDS slice-major: chunk c, lane group qg, slice j
 // hold the four dwords {4u + j : u = 0..3} of the group's 64 k, so one
@@ -748,11 +756,10 @@ __device__ __forceinline__ void for_each_c(F&& f, std::integer_sequence<int, J..
 template <int CPW, int MODE, int DEPTH, bool HOLD_B>
 __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int nwaves, int tpb) {
   static_assert(DEPTH >= 2 && DEPTH <= 4 && DEPTH * CPW < 64, "tiles in flight");
-  static_assert(MODE != kInt8, "raw activations (step A1 fused)");
   extern __shared__ __align__(16) unsigned char smem[];
   __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
                    "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
-                   "s"(pr.per), "s"(nwaves), "s"(tpb));
+                   "s"(pr.per), "s"(pr.rowsum), "s"(nwaves), "s"(tpb));
   const int N = pr.N, K = pr.K, per = pr.per;
   const int G = gridDim.x, b = blockIdx.x;
   const int tiles = (N + 15) >> 4;
@@ -782,7 +789,9 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int k0 = min(c0 + u, nchunks - 1) * 256 + 4 * lane;
-      if constexpr (MODE == kBf16) {
+      if constexpr (MODE == kInt8) {
+        xin[u] = make_uint4(*reinterpret_cast<const uint32_t*>(xr + k0), 0u, 0u, 0u);
+      } else if constexpr (MODE == kBf16) {
         const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
         xin[u] = make_uint4(v.x, v.y, 0u, 0u);
       } else {
@@ -791,6 +800,12 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     }
   }
   const float g = pr.gamma[0];
+  float a_in = 0.0f;   // int8 input: the token's absmax (and, given, its row sum)
+  int rs_in = 0;
+  if constexpr (MODE == kInt8) {
+    a_in = pr.absmax[0];
+    if (pr.rowsum) rs_in = pr.rowsum[0];
+  }
   for (int i = threadIdx.x; i < 16 + 17 * tpb + 1; i += nthreads) zero[i] = 0;
   lds_sync();   // every activation load of the block is issued ahead of every weight load
 
@@ -828,7 +843,25 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
   int qsum = 0;
   float a_t;
   wait_vmem<kEarly>();                              // the raw loads landed
-  {
+  if constexpr (MODE == kInt8) {
+    // int8 input: the codes go into the wave's run of the row as they are;
+    // the sum of q over the run unless the token's row sum is given
+    a_t = a_in;
+    int tsum = 0;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      if (u >= cnt) break;                          // wave-uniform
+      const uint32_t word = xin[u].x;
+      tsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, tsum, false);
+      *reinterpret_cast<uint32_t*>(xs8 + run0 + u * 256 + slice_off(lane)) = word;
+    }
+    if (pr.rowsum) {
+      if (wave == 0 && r == 0) qsum = rs_in;       // the total once, on one wave's lanes
+    } else {
+      const int sum = wave_sum_i(tsum);
+      if (r == 0) qsum = sum;
+    }
+  } else {
     uint32_t mx = 0;
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -1241,6 +1274,13 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
   grp.T = t;
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
                         nullptr, nullptr, gamma2, h, n, k, 0, 0, rowsum};
+  if (h == nullptr && k <= BL_GEMV_PERSIST_INT8_MAX_K && persist_ok(t, n, k)) {
+    // one token over many tiles: the persistent kernel (the int8 row staged
+    // once per block)
+    DecProblem pr = grp.p[0];
+    pr.ldy = n;
+    return run_persist<kInt8>(pr, stream);
+  }
   const int blocks = (n + 15) / 16;
   const DecShape sh = dec_shape(blocks, k, t);
   return run_dec<kInt8>(grp, 1, sh, dec_lds(t, k, 0, sh.rt), stream);
