@@ -259,6 +259,10 @@ struct DecGroup {
 constexpr int dec_head(int rt) { return 64 + 256 * rt * 4 + 4 + 16 * 4 + 12; }
 static_assert(dec_head(1) % 16 == 0 && dec_head(2) % 16 == 0, "LDS header alignment");
 
+#ifndef BL_GEMV_DEC_EARLY_DIV
+#define BL_GEMV_DEC_EARLY_DIV 4       // CPW / this (at least 1) weight chunks per wave go out early
+#endif
+
 // Waves per SIMD the decode kernel is compiled for: eight with int8 input on
 // one row tile (64 VGPRs), fewer where the raw activations or a second row
 // tile's weights take registers.
@@ -391,20 +395,32 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   // same barrier orders the header clearing before the tile adds.
   for (int i = threadIdx.x; i < 16 + 256 * RT + 1 + 16; i += nthreads) zero[i] = 0;
   lds_sync();
-  // ... and last every weight chunk of this wave; slots past cnt repeat the
+  // ... and last the weight chunks of this wave; slots past cnt repeat the
   // row's last chunk and meet a zero B operand below.
   uint4 buf[RT][CPW];
+  auto issue_w = [&](auto loc, auto hic) {
+    constexpr int LO = decltype(loc)::value, HI = decltype(hic)::value;
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int c = min(c0 + i, nchunks - 1);
+    for (int i = LO; i < HI; ++i) {
+      const int c = min(c0 + i, nchunks - 1);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) buf[rt][i] = wrow[rt][(size_t)c * 4];
-  }
+      for (int rt = 0; rt < RT; ++rt) buf[rt][i] = wrow[rt][(size_t)c * 4];
+    }
+  };
+  // Only a quarter of the chunks (at least one) go out now, the rest after
+  // the activation work: a wave issues in order, and while the CU's memory
+  // queue is full, loads are accepted only as data returns, which held the
+  // activation work back behind the weight stream (measured: the 2B layer
+  // 1192 -> 1208 GB/s with one of two chunks early, 70B 28672 -> 8192 at one
+  // int8 token 14.4 -> 14.2 us with two of eight; all chunks early as before,
+  // or one of eight, measured the old times).
+  constexpr int kE = CPW / BL_GEMV_DEC_EARLY_DIV > 1 ? CPW / BL_GEMV_DEC_EARLY_DIV : 1;
+  issue_w(std::integral_constant<int, 0>{}, std::integral_constant<int, kE>{});
 
   int qsum = 0;     // sum of q over this wave's k run, token of lane l: l & 15
   float a_t = 0.0f; // one raw token: its absmax
   if constexpr (MODE == kInt8) {
-    wait_vmem<RT * CPW>();                               // this wave's activation run landed
+    wait_vmem<RT * kE>();                               // this wave's activation run landed
     for (int t = 0; t < (pr.rowsum ? 0 : T); ++t) {     // with rowsum: the totals, at the end
       const uint4* xt = reinterpret_cast<const uint4*>(xs8 + t * tstride + run0);
       int part = 0;
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   } else if constexpr (ONE) {
     // Step A1 in the block, one token, from registers: the absmax over this
     // wave's run (its repeats included), then over the block through LDS ...
-    wait_vmem<RT * CPW>();                               // this lane's raw activations landed
+    wait_vmem<RT * kE>();                               // this lane's raw activations landed
     uint32_t mx = 0;                                // magnitude bit patterns
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   } else {
     // Step A1 in the block.  The absmax of each token (T <= 4) over all of
     // K, from every wave's share of the raw rows ...
-    wait_vmem<RT * CPW>();                               // wave 0: the raw rows landed
+    wait_vmem<RT * kE>();                               // wave 0: the raw rows landed
     lds_sync();                                     // ... for every wave
     constexpr int E = MODE == kBf16 ? 8 : 4;        // elements per 16 bytes
     const int per_tok = K / E, nvec = T * per_tok;
@@ -575,6 +591,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
     if (first && wave == 0 && pr.absmax_out && lane < T)
       pr.absmax_out[lane] = __uint_as_float((uint32_t)amax[lane]);
   }
+
+  // the rest of the weight chunks, after the activation work (a wave issues
+  // in order, and loads wait in issue while the CU's memory queue is full)
+  issue_w(std::integral_constant<int, kE>{}, std::integral_constant<int, CPW>{});
 
   // B operands of slot i: this token's 64 bytes of chunk c0 + i (four
   // 16-byte vectors; slice j takes dword j of each), or zeros for tokens past
