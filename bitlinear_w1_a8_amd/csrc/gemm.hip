@@ -430,6 +430,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 
   const int h = lane >> 5, m = lane & 31;
   const int aswz = (m >> 1) & 7;
+  // With four stages the refill goes out after the step's MFMAs, not before
+  // them: a wave issues in order, and while the CU's memory queue is full
+  // the refill's loads are accepted only as data returns, holding the
+  // step's LDS reads and MFMAs back; three stages in flight still cover
+  // the loads' latency.  (70B T = 256, 28672 -> 8192 on 64 x 128 tiles:
+  // 81.7-82.1 -> 79.4-79.6 us, 78.4 -> 72.5-73.6 with the row sums handed
+  // in; on the other tile shapes within 2% either way, so they keep three
+  // stages and the early refill.)
+  constexpr bool kLateRefill = STAGES >= 4;
   // One K step on stage S; refill stage (S + STAGES - 1) % STAGES, which the
   // previous step finished reading, with tile kt + STAGES - 1.
   auto step = [&](auto stage_c, int kt) {
@@ -438,7 +447,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     // unconditional (no branch, so no join where the compiler would drain
     // every load): past the end it re-fetches the last tile into a stage that
     // is never read again
-    issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, abuf(R{}), bbuf(R{}));
+    auto refill = [&]() {
+      issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, abuf(R{}), bbuf(R{}));
+    };
+    if constexpr (!kLateRefill) refill();
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
     const unsigned char* Bt =
         bbuf(stage_c) + (wn * 32 * WNF + m) * kBRow + (WBITS == 2 ? 16 * h : 0);
@@ -490,6 +502,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       // one sub-step's LDS reads with the previous one's MFMAs measured 1-4%
       // faster at the same register count
     }
+    if constexpr (kLateRefill) refill();
     // Tile kt+1 must have landed: this wave's loads by the wait, everyone's
     // by the barrier.  A plain s_barrier, not __syncthreads(): the latter's
     // release fence would also wait for the refill issued above.  The only
@@ -748,8 +761,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run_lds<4, 2, 1, 5, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W128:
-      return run_lds<4, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
-                                                 1, 0, nullptr, nullptr, rowsum);
+      return run_lds<4, 2, 1, 2, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                    1, 0, nullptr, nullptr, rowsum);
     case Tiles::kSplit: {
       // 128 x 512 tiles, K in parts: y is cleared, takes the exact int32
       // partial sums by atomics and is rescaled in place
