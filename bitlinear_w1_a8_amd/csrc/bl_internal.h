@@ -202,23 +202,68 @@ __device__ __forceinline__ void limbs_add(uint32_t (&limb)[L], unsigned long lon
 
 // limbs_to_f64: the integer times 2^scale, rounded once to binary64 (nearest,
 // ties to even); the result must lie in the normal binary64 range or be 0.
+// Word-wise: the top four limbs give the significand, the round bit and part
+// of the sticky bit, the limbs below only the rest of the sticky bit.  (A
+// bit-by-bit scan for the sticky bit ran through hundreds of zero bits of a
+// sum of bf16 squares, in scratch memory, and cost tens of microseconds.)
 template <int L>
 __device__ __forceinline__ double limbs_to_f64(const uint32_t (&limb)[L], int scale) {
-  int top = -1;
-  for (int i = L - 1; i >= 0 && top < 0; --i)
-    if (limb[i]) top = i * 32 + (31 - __builtin_clz(limb[i]));
-  if (top < 0) return 0.0;
+  int tw = -1;
+  for (int i = L - 1; i >= 0; --i)
+    if (limb[i]) { tw = i; break; }
+  if (tw < 0) return 0.0;
+  const int top = tw * 32 + (31 - __builtin_clz(limb[tw]));
   if (top <= 52) {
     const unsigned long long x = ((unsigned long long)limb[1] << 32) | limb[0];
     return ldexp((double)x, scale);
   }
-  auto bit = [&](int i) -> uint32_t { return (limb[i >> 5] >> (i & 31)) & 1u; };
-  unsigned long long m = 0;
-  for (int i = top; i >= top - 52; --i) m = (m << 1) | bit(i);
-  const uint32_t rnd = bit(top - 53);
-  uint32_t sticky = 0;
-  for (int i = top - 54; i >= 0 && !sticky; --i) sticky |= bit(i);
-  int e = top - 52;
+  // the 128-bit window of limbs tw .. tw - 3 (missing ones are 0), bit 0 at
+  // bit 32 (tw - 3) of the integer, shifted so that its top bit is bit 127
+  unsigned long long hi = ((unsigned long long)limb[tw] << 32) | (tw >= 1 ? limb[tw - 1] : 0u);
+  unsigned long long lo = ((unsigned long long)(tw >= 2 ? limb[tw - 2] : 0u) << 32) |
+                          (tw >= 3 ? limb[tw - 3] : 0u);
+  bool sticky = false;
+  for (int i = tw - 4; i >= 0; --i) sticky |= limb[i] != 0u;
+  const int lz = __builtin_clzll(hi);
+  if (lz) {
+    hi = (hi << lz) | (lo >> (64 - lz));
+    lo <<= lz;
+  }
+  unsigned long long m = hi >> 11;                  // 53 bits
+  const unsigned long long rem = hi & 0x7ffull;
+  const bool rnd = (rem >> 10) & 1ull;
+  sticky |= (rem & 0x3ffull) != 0 || lo != 0;
+  int e = (tw - 3) * 32 - lz + 75;                  // weight of m's lowest bit
+  if (rnd && (sticky || (m & 1ull))) {
+    ++m;
+    if (m == (1ull << 53)) { m >>= 1; ++e; }
+  }
+  return ldexp((double)m, e + scale);
+}
+
+// (s2:s1:s0) * 2^scale rounded once to binary64 (nearest, ties to even), in
+// registers; the result must lie in the normal binary64 range or be 0.
+__device__ __forceinline__ double u192_to_f64(unsigned long long s0, unsigned long long s1,
+                                              unsigned long long s2, int scale) {
+  unsigned long long hi, lo;
+  bool sticky = false;
+  int base;                                         // bit of the integer at lo's bit 0
+  if (s2) { hi = s2; lo = s1; sticky = s0 != 0; base = 64; }
+  else if (s1) { hi = s1; lo = s0; base = 0; }
+  else {
+    if (s0 < (1ull << 53)) return ldexp((double)s0, scale);
+    hi = s0; lo = 0; base = -64;
+  }
+  const int lz = __builtin_clzll(hi);
+  if (lz) {
+    hi = (hi << lz) | (lo >> (64 - lz));
+    lo <<= lz;
+  }
+  unsigned long long m = hi >> 11;                  // 53 bits
+  const unsigned long long rem = hi & 0x7ffull;
+  const bool rnd = (rem >> 10) & 1ull;
+  sticky |= (rem & 0x3ffull) != 0 || lo != 0;
+  int e = base - lz + 75;                           // weight of m's lowest bit
   if (rnd && (sticky || (m & 1ull))) {
     ++m;
     if (m == (1ull << 53)) { m >>= 1; ++e; }

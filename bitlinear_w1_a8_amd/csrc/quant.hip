@@ -20,6 +20,10 @@ namespace bl {
 namespace {
 
 constexpr int kMaxVec = 8;      // 16-byte vectors held per thread
+#ifndef BL_QUANT_VPT
+#define BL_QUANT_VPT kMaxVec      // vectors per thread the launch aims for (<= kMaxVec)
+#endif
+static_assert(BL_QUANT_VPT >= 1 && BL_QUANT_VPT <= kMaxVec, "vectors per thread");
 constexpr int kMaxWaves = 16;   // up to 1024 threads per row
 
 // DPP controls (GCN/CDNA encoding).
@@ -215,19 +219,20 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 // RN32(RN32(x * g) * r), then step A1 on x_hat; scale[t] = max |x_hat|.
 //
 // The exact sum: with x = m * 2^(e-150) (24-bit m; e = 1 and no hidden bit
-// for subnormals), x^2 = m^2 * 2^(2e-300) with m^2 < 2^48.  Each wave takes
-// the exponent E of its largest |x| and adds m^2 << (2(e - E) + 62) into a
-// 128-bit integer per lane (no carry-out: fewer than 2^17 terms of < 2^110).
-// That is exact for every element within 31 binades of the wave's largest;
+// for subnormals), x^2 = m^2 * 2^(2e-300) with m^2 < 2^48.  Every lane takes
+// the exponent E of the row's largest |x| and adds m^2 << (2(e - E) + 62)
+// into a 128-bit integer (no carry-out: fewer than 2^17 terms of < 2^110).
+// That is exact for every element within 31 binades of the row's largest;
 // a smaller one (none in ordinary data) sets a flag, and then the block
 // sums those elements into per-exponent LDS buckets instead.  One thread
-// adds the waves' 128-bit sums and the buckets into a 576-bit integer in
-// units of 2^-298 and rounds it once to binary64.
+// adds the waves' 128-bit sums, all in the same units, in 192 bits and
+// rounds the total once to binary64 (in registers); with the flag set it
+// adds them and the buckets into a 576-bit integer in units of 2^-298.
 //
 // max |x_hat| is RN32(max |u| * r): rounding is monotonic, so the largest
 // |u| gives the largest |x_hat|.
 
-constexpr int kSqShift = 62;       // bit of m^2 for an element at the wave's exponent
+constexpr int kSqShift = 62;       // bit of m^2 for an element at the row's exponent
 constexpr int kSqLimbs = 18;       // 576 bits: sums below 2^17 * 2^256 in units of 2^-298
 
 struct U128 {
@@ -248,7 +253,7 @@ __device__ __forceinline__ void split_f32(float x, uint32_t& m, int& e) {
   if (e) m |= 0x800000u; else e = 1;
 }
 
-// Adds x^2 to the lane's sum at the wave's exponent ew; returns false (and
+// Adds x^2 to the lane's sum at the row's exponent ew; returns false (and
 // adds nothing) for an element too small for the 128-bit window.
 __device__ __forceinline__ bool add_square(U128& acc, float x, int ew) {
   uint32_t m;
@@ -282,6 +287,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   __shared__ int red_e[kMaxWaves], red_umax[kMaxWaves], red_far[kMaxWaves], red2[kMaxWaves];
   __shared__ float sh_r, sh_s;
   __shared__ unsigned long long far_hist[2][256];   // buckets of the small elements (rare)
+  __shared__ uint32_t far_limb[kSqLimbs];            // their exact total (rare)
   const int nvec = k / E;
   const int64_t row = blockIdx.x;
   const uint4* xr = x + row * (int64_t)nvec;
@@ -311,10 +317,19 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
     elems_gain<BF16>(xr[idx], gain + idx * E, f);
     mu = max(mu, absmax_bits(f));
   }
-  const int ew = max(wave_max_u(mx) >> 23, 1);   // exponent of the wave's largest |x|
+  // the block's largest |x| sets one exponent for every wave's sum
+  mx = wave_max_u(mx);
   mu = wave_max_u(mu);
+  if (lane == 0) {
+    red_e[wave] = mx;
+    red_umax[wave] = mu;
+  }
+  __syncthreads();
+  int bmx = 0;
+  for (int wv = 0; wv < nwaves; ++wv) bmx = max(bmx, red_e[wv]);
+  const int ew = max(bmx >> 23, 1);             // exponent of the block's largest |x|
 
-  // 2. exact sum of squares, per lane at the wave's exponent
+  // 2. exact sum of squares, per lane at the row's exponent
   U128 acc = {0ull, 0ull};
   bool fits = true;
 #pragma unroll
@@ -338,15 +353,13 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   if (lane == 0) {
     red_lo[wave] = acc.lo;
     red_hi[wave] = acc.hi;
-    red_e[wave] = ew;
-    red_umax[wave] = mu;
     red_far[wave] = wave_far;
   }
   __syncthreads();
   bool far = false;
   for (int wv = 0; wv < nwaves; ++wv) far |= red_far[wv] != 0;
 
-  if (far) {   // block-uniform: some element lay more than 31 binades below its wave's largest
+  if (far) {   // block-uniform: some element lay more than 31 binades below the row's largest
     for (int j = tid; j < 512; j += nthr) (&far_hist[0][0])[j] = 0ull;
     __syncthreads();
     // the same elements per thread as above, read again (this path is rare)
@@ -370,32 +383,48 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
 
   // 3. one thread: the exact sum, r, the absmax of x_hat and the step-A1 scale
   if (tid == 0) {
-    uint32_t limb[kSqLimbs];
-    for (int i = 0; i < kSqLimbs; ++i) limb[i] = 0;
+    // the waves' sums, all in units of 2^(2 ew - 362), added in 192 bits
+    // (at most 16 sums below 2^127 each)
+    unsigned long long s0 = 0, s1 = 0, s2 = 0;
     int um = 0;
     for (int wv = 0; wv < nwaves; ++wv) {
-      // the wave's sum is in units of 2^(2 ew - 362) = 2^(2 ew - 64) * 2^-298
-      unsigned long long lo = red_lo[wv], hi = red_hi[wv];
-      const int off = 2 * red_e[wv] - 64;
-      if (off < 0) {     // exact: every term's lowest set bit is at or above -off
-        const int sft = -off;
-        lo = (lo >> sft) | (hi << (64 - sft));
-        hi >>= sft;
-        limbs_add(limb, lo, 0);
-        limbs_add(limb, hi, 64);
-      } else {
-        limbs_add(limb, lo, off);
-        limbs_add(limb, hi, off + 64);
-      }
+      const unsigned long long lo = red_lo[wv], hi = red_hi[wv];
+      const unsigned long long a0 = s0 + lo;
+      const unsigned long long c0 = a0 < lo ? 1ull : 0ull;
+      const unsigned long long b1 = hi + c0;
+      const unsigned long long c1 = b1 < c0 ? 1ull : 0ull;
+      const unsigned long long a1 = s1 + b1;
+      s2 += c1 + (a1 < b1 ? 1ull : 0ull);
+      s0 = a0;
+      s1 = a1;
       um = max(um, red_umax[wv]);
     }
-    if (far) {
+    double ssum;
+    if (!far) {
+      ssum = u192_to_f64(s0, s1, s2, 2 * ew - 362);
+    } else {
+      // rare: elements more than 31 binades below the largest, in
+      // per-exponent buckets; everything in 576 bits in units of 2^-298
+      // (in LDS: an array indexed at run time would take scratch memory)
+      uint32_t (&limb)[kSqLimbs] = far_limb;
+      for (int i = 0; i < kSqLimbs; ++i) limb[i] = 0;
+      const int off = 2 * ew - 64;                  // units 2^(2 ew - 362) = 2^off * 2^-298
+      if (off < 0) {     // exact: every term's lowest set bit is at or above -off
+        const int sft = -off;
+        limbs_add(limb, (s0 >> sft) | (s1 << (64 - sft)), 0);
+        limbs_add(limb, (s1 >> sft) | (s2 << (64 - sft)), 64);
+        limbs_add(limb, s2 >> sft, 128);
+      } else {
+        limbs_add(limb, s0, off);
+        limbs_add(limb, s1, off + 64);
+        limbs_add(limb, s2, off + 128);
+      }
       for (int ex = 1; ex < 255; ++ex) {   // m^2 = hi * 2^24 + lo, at 2^(2 ex - 300)
         limbs_add(limb, far_hist[0][ex], 2 * ex + 22);
         limbs_add(limb, far_hist[1][ex], 2 * ex - 2);
       }
+      ssum = limbs_to_f64(limb, -298);
     }
-    const double ssum = limbs_to_f64(limb, -298);
     const float ms = (float)(ssum / (double)k);   // binary64 mean, one rounding to binary32
     const float root = sqrtf(ms + eps_n);          // binary32 add; correctly rounded root
     const float r = 1.0f / root;                   // IEEE binary32 division
@@ -442,7 +471,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
 // Enough threads that each holds at most kMaxVec vectors, in whole waves.
 dim3 row_block(int64_t k, int e) {
   const int64_t nvec = k / e;
-  int64_t thr = (nvec + kMaxVec - 1) / kMaxVec;
+  int64_t thr = (nvec + BL_QUANT_VPT - 1) / BL_QUANT_VPT;
   thr = ((thr + 63) / 64) * 64;
   if (thr < 64) thr = 64;
   if (thr > 64 * kMaxWaves) thr = 64 * kMaxWaves;
