@@ -20,11 +20,8 @@ namespace bl {
 namespace {
 
 constexpr int kMaxVec = 8;      // 16-byte vectors held per thread
-#ifndef BL_QUANT_VPT
-#define BL_QUANT_VPT kMaxVec      // vectors per thread the launch aims for (<= kMaxVec)
-#endif
-static_assert(BL_QUANT_VPT >= 1 && BL_QUANT_VPT <= kMaxVec, "vectors per thread");
 constexpr int kMaxWaves = 16;   // up to 1024 threads per row
+constexpr int kQuantVpt = 4;    // vectors per thread of the act-quant launch
 
 // DPP controls (GCN/CDNA encoding).
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
@@ -218,22 +215,36 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 // RN32(RN64(S / K)), r = RN32(1 / RN32(sqrt(RN32(ms + eps_n)))), x_hat =
 // RN32(RN32(x * g) * r), then step A1 on x_hat; scale[t] = max |x_hat|.
 //
-// The exact sum: with x = m * 2^(e-150) (24-bit m; e = 1 and no hidden bit
-// for subnormals), x^2 = m^2 * 2^(2e-300) with m^2 < 2^48.  Every lane takes
-// the exponent E of the row's largest |x| and adds m^2 << (2(e - E) + 62)
-// into a 128-bit integer (no carry-out: fewer than 2^17 terms of < 2^110).
-// That is exact for every element within 31 binades of the row's largest;
-// a smaller one (none in ordinary data) sets a flag, and then the block
-// sums those elements into per-exponent LDS buckets instead.  One thread
-// adds the waves' 128-bit sums, all in the same units, in 192 bits and
-// rounds the total once to binary64 (in registers); with the flag set it
-// adds them and the buckets into a 576-bit integer in units of 2^-298.
+// The exact sum.  Let E be the exponent field of the row's largest |x| and
+// d = E - e for an element with exponent field e (e = 1 for subnormals and
+// zero).  The first pass also finds the smallest nonzero |x|; when every
+// nonzero element has d <= 31 (ordinary data) each lane adds its squares
+// exactly in fixed point at the row's exponent, branch-free:
+//  - binary32 input, x = m * 2^(e-150) with a 24-bit m: m^2 << (62 - 2d)
+//    into a 128-bit integer (fewer than 2^17 terms below 2^110);
+//  - bf16 input, x = m * 2^(e-134) with an 8-bit m: x^2 scaled by a power
+//    of two into one of two binary64 accumulators, d <= 15 in units of
+//    2^(2E-298) and 16 <= d <= 31 in units of 2^(2E-330).  Each scaled
+//    square is an integer m^2 * 2^(2(15-d)) or m^2 * 2^(2(31-d)) below
+//    2^46, and a lane adds at most 128 of them (K <= 131072 over at most
+//    1024 lanes), so every partial sum is an integer below 2^53 and each
+//    binary64 operation is exact.
+// The lanes' sums go to 128 bits in units of 2^(2E-362), are added across
+// the wave, and one thread adds the waves' sums in 192 bits and rounds the
+// total once to binary64.  A row with a nonzero element more than 31
+// binades below its largest (none in ordinary data) instead sums every
+// element into per-exponent LDS buckets and rounds their 576-bit total.
 //
 // max |x_hat| is RN32(max |u| * r): rounding is monotonic, so the largest
 // |u| gives the largest |x_hat|.
 
 constexpr int kSqShift = 62;       // bit of m^2 for an element at the row's exponent
+constexpr int kSqWindow = 31;      // binades below the largest that the fixed point holds
 constexpr int kSqLimbs = 18;       // 576 bits: sums below 2^17 * 2^256 in units of 2^-298
+// a lane's bf16 squares: at most 128, each below 2^46, stay below 2^53
+static_assert(8 * (kMaxVec > BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)
+                       ? kMaxVec : BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)) <= 128,
+              "bf16 squares per lane");
 
 struct U128 {
   unsigned long long lo, hi;
@@ -253,18 +264,37 @@ __device__ __forceinline__ void split_f32(float x, uint32_t& m, int& e) {
   if (e) m |= 0x800000u; else e = 1;
 }
 
-// Adds x^2 to the lane's sum at the row's exponent ew; returns false (and
-// adds nothing) for an element too small for the 128-bit window.
-__device__ __forceinline__ bool add_square(U128& acc, float x, int ew) {
+// Smallest (|x| bits - 1) over the elements, unsigned: 0xffffffff when all are zero.
+template <int E>
+__device__ __forceinline__ uint32_t minnz_bits_m1(const float (&f)[E], uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < E; ++i) m = min(m, (__float_as_uint(f[i]) & 0x7fffffffu) - 1u);
+  return m;
+}
+
+// binary32 input: adds x^2 to the lane's 128-bit sum at the row's exponent
+// field ew.  Nonzero elements lie within kSqWindow binades of it; a zero
+// adds nothing whatever its shift.
+__device__ __forceinline__ void add_square(U128& acc, float x, int ew) {
   uint32_t m;
   int e;
   split_f32(x, m, e);
-  if (!m) return true;
-  const int sh = 2 * (e - ew) + kSqShift;
-  if (sh < 0) return false;
+  const int sh = max(2 * (e - ew) + kSqShift, 0);
   const unsigned long long sq = (unsigned long long)m * m;
   u128_add(acc, sq << sh, (sq >> 1) >> (63 - sh));
-  return true;
+}
+
+// bf16 input: x^2 * 2^(2(149 - ew)) into a (d <= 15) or x^2 * 2^(2(165 - ew))
+// into b (16 <= d <= 31); thr = 2^(ew - 142), the smallest |x| with d <= 15
+// (0 when every element has it); ha, hb: high words of the two binary64 scales.
+__device__ __forceinline__ void add_square_bf16(double& a, double& b, float x, float thr,
+                                                int ha, int hb) {
+  const double xd = (double)x;
+  const bool near = fabsf(x) >= thr;
+  const double sa = __hiloint2double(near ? ha : 0, 0);
+  const double sb = __hiloint2double(near ? 0 : hb, 0);
+  a = fma(xd * sa, xd, a);
+  b = fma(xd * sb, xd, b);
 }
 
 __device__ __forceinline__ U128 wave_sum_u128(U128 a) {
@@ -284,10 +314,10 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
                                                       int32_t* __restrict__ rowsum) {
   constexpr int E = In<BF16>::E;
   __shared__ unsigned long long red_lo[kMaxWaves], red_hi[kMaxWaves];
-  __shared__ int red_e[kMaxWaves], red_umax[kMaxWaves], red_far[kMaxWaves], red2[kMaxWaves];
+  __shared__ int red_e[kMaxWaves], red_umax[kMaxWaves], red_nz[kMaxWaves], red2[kMaxWaves];
   __shared__ float sh_r, sh_s;
-  __shared__ unsigned long long far_hist[2][256];   // buckets of the small elements (rare)
-  __shared__ uint32_t far_limb[kSqLimbs];            // their exact total (rare)
+  __shared__ unsigned long long far_hist[2][256];   // per-exponent buckets (rare rows)
+  __shared__ uint32_t far_limb[kSqLimbs];            // their exact total (rare rows)
   const int nvec = k / E;
   const int64_t row = blockIdx.x;
   const uint4* xr = x + row * (int64_t)nvec;
@@ -295,9 +325,10 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
 
-  // 1. the row in registers; largest |x| and |u| = |x * g|
+  // 1. the row in registers; largest |x| and |u| = |x * g|, smallest nonzero |x|
   uint4 v[kMaxVec];
   int mx = 0, mu = 0;
+  uint32_t nz = 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < kMaxVec; ++i) {
     const int idx = tid + i * nthr;
@@ -306,6 +337,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
       float f[E];
       elems<BF16>(v[i], f);
       mx = max(mx, absmax_bits(f));
+      nz = minnz_bits_m1(f, nz);
       elems_gain<BF16>(v[i], gain + idx * E, f);
       mu = max(mu, absmax_bits(f));
     }
@@ -314,55 +346,86 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
     float f[E];
     elems<BF16>(xr[idx], f);
     mx = max(mx, absmax_bits(f));
+    nz = minnz_bits_m1(f, nz);
     elems_gain<BF16>(xr[idx], gain + idx * E, f);
     mu = max(mu, absmax_bits(f));
   }
-  // the block's largest |x| sets one exponent for every wave's sum
+  // signed max of 0x7fffffff - nz picks the smallest nz (all-zero lanes: INT_MIN)
   mx = wave_max_u(mx);
   mu = wave_max_u(mu);
+  const int nzk = wave_max_u((int)(0x7fffffffu - nz));
   if (lane == 0) {
     red_e[wave] = mx;
     red_umax[wave] = mu;
+    red_nz[wave] = nzk;
   }
   __syncthreads();
-  int bmx = 0;
-  for (int wv = 0; wv < nwaves; ++wv) bmx = max(bmx, red_e[wv]);
-  const int ew = max(bmx >> 23, 1);             // exponent of the block's largest |x|
+  int bmx = 0, bnz = INT_MIN;
+  for (int wv = 0; wv < nwaves; ++wv) {
+    bmx = max(bmx, red_e[wv]);
+    bnz = max(bnz, red_nz[wv]);
+  }
+  const int ew = max(bmx >> 23, 1);             // exponent field of the row's largest |x|
+  const uint32_t nzb = 0x7fffffffu - (uint32_t)bnz + 1u;   // smallest nonzero |x| bits (0: none)
+  const bool far = nzb != 0u && ew - max((int)(nzb >> 23), 1) > kSqWindow;   // block-uniform
 
-  // 2. exact sum of squares, per lane at the row's exponent
-  U128 acc = {0ull, 0ull};
-  bool fits = true;
+  if (!far) {
+    // 2. exact sum of squares, per lane at the row's exponent
+    U128 acc;
+    if constexpr (BF16) {
+      const float thr = ew > 16 ? __uint_as_float((uint32_t)(ew - 15) << 23) : 0.0f;
+      const int ha = (1321 - 2 * ew) << 20;     // 2^(2(149 - ew))
+      const int hb = (1353 - 2 * ew) << 20;     // 2^(2(165 - ew))
+      double sa = 0.0, sb = 0.0;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int idx = tid + i * nthr;
-    if (idx < nvec) {
-      float f[E];
-      elems<BF16>(v[i], f);
+      for (int i = 0; i < kMaxVec; ++i) {
+        const int idx = tid + i * nthr;
+        if (idx < nvec) {
+          float f[E];
+          elems<BF16>(v[i], f);
 #pragma unroll
-      for (int e = 0; e < E; ++e) fits &= add_square(acc, f[e], ew);
+          for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr, ha, hb);
+        }
+      }
+      for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+        float f[E];
+        elems<BF16>(xr[idx], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr, ha, hb);
+      }
+      // a in units of 2^(2 ew - 298) = 2^64 units, b in 2^(2 ew - 330) = 2^32 units
+      const unsigned long long ia = (unsigned long long)sa, ib = (unsigned long long)sb;
+      acc.lo = ib << 32;
+      acc.hi = ia + (ib >> 32);
+    } else {
+      acc = {0ull, 0ull};
+#pragma unroll
+      for (int i = 0; i < kMaxVec; ++i) {
+        const int idx = tid + i * nthr;
+        if (idx < nvec) {
+          float f[E];
+          elems<BF16>(v[i], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) add_square(acc, f[e], ew);
+        }
+      }
+      for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+        float f[E];
+        elems<BF16>(xr[idx], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) add_square(acc, f[e], ew);
+      }
     }
-  }
-  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
-    float f[E];
-    elems<BF16>(xr[idx], f);
-#pragma unroll
-    for (int e = 0; e < E; ++e) fits &= add_square(acc, f[e], ew);
-  }
-  acc = wave_sum_u128(acc);
-  const bool wave_far = __ballot(!fits) != 0;
-  if (lane == 0) {
-    red_lo[wave] = acc.lo;
-    red_hi[wave] = acc.hi;
-    red_far[wave] = wave_far;
-  }
-  __syncthreads();
-  bool far = false;
-  for (int wv = 0; wv < nwaves; ++wv) far |= red_far[wv] != 0;
-
-  if (far) {   // block-uniform: some element lay more than 31 binades below the row's largest
+    acc = wave_sum_u128(acc);
+    if (lane == 0) {
+      red_lo[wave] = acc.lo;
+      red_hi[wave] = acc.hi;
+    }
+  } else {
+    // rare: every element into per-exponent buckets (m^2 in 24-bit halves),
+    // the row read again
     for (int j = tid; j < 512; j += nthr) (&far_hist[0][0])[j] = 0ull;
     __syncthreads();
-    // the same elements per thread as above, read again (this path is rare)
     for (int idx = tid; idx < nvec; idx += nthr) {
       float f[E];
       elems<BF16>(xr[idx], f);
@@ -371,54 +434,42 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
         uint32_t m;
         int ex;
         split_f32(f[e], m, ex);
-        if (m && 2 * (ex - ew) + kSqShift < 0) {
+        if (m) {
           const unsigned long long sq = (unsigned long long)m * m;
           atomicAdd(&far_hist[0][ex], sq >> 24);
           atomicAdd(&far_hist[1][ex], sq & 0xffffffull);
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // 3. one thread: the exact sum, r, the absmax of x_hat and the step-A1 scale
   if (tid == 0) {
-    // the waves' sums, all in units of 2^(2 ew - 362), added in 192 bits
-    // (at most 16 sums below 2^127 each)
-    unsigned long long s0 = 0, s1 = 0, s2 = 0;
     int um = 0;
-    for (int wv = 0; wv < nwaves; ++wv) {
-      const unsigned long long lo = red_lo[wv], hi = red_hi[wv];
-      const unsigned long long a0 = s0 + lo;
-      const unsigned long long c0 = a0 < lo ? 1ull : 0ull;
-      const unsigned long long b1 = hi + c0;
-      const unsigned long long c1 = b1 < c0 ? 1ull : 0ull;
-      const unsigned long long a1 = s1 + b1;
-      s2 += c1 + (a1 < b1 ? 1ull : 0ull);
-      s0 = a0;
-      s1 = a1;
-      um = max(um, red_umax[wv]);
-    }
+    for (int wv = 0; wv < nwaves; ++wv) um = max(um, red_umax[wv]);
     double ssum;
     if (!far) {
+      // the waves' sums, all in units of 2^(2 ew - 362), added in 192 bits
+      // (at most 16 sums below 2^127 each)
+      unsigned long long s0 = 0, s1 = 0, s2 = 0;
+      for (int wv = 0; wv < nwaves; ++wv) {
+        const unsigned long long lo = red_lo[wv], hi = red_hi[wv];
+        const unsigned long long a0 = s0 + lo;
+        const unsigned long long c0 = a0 < lo ? 1ull : 0ull;
+        const unsigned long long b1 = hi + c0;
+        const unsigned long long c1 = b1 < c0 ? 1ull : 0ull;
+        const unsigned long long a1 = s1 + b1;
+        s2 += c1 + (a1 < b1 ? 1ull : 0ull);
+        s0 = a0;
+        s1 = a1;
+      }
       ssum = u192_to_f64(s0, s1, s2, 2 * ew - 362);
     } else {
-      // rare: elements more than 31 binades below the largest, in
-      // per-exponent buckets; everything in 576 bits in units of 2^-298
-      // (in LDS: an array indexed at run time would take scratch memory)
+      // the buckets in 576 bits in units of 2^-298 (in LDS: an array
+      // indexed at run time would take scratch memory)
       uint32_t (&limb)[kSqLimbs] = far_limb;
       for (int i = 0; i < kSqLimbs; ++i) limb[i] = 0;
-      const int off = 2 * ew - 64;                  // units 2^(2 ew - 362) = 2^off * 2^-298
-      if (off < 0) {     // exact: every term's lowest set bit is at or above -off
-        const int sft = -off;
-        limbs_add(limb, (s0 >> sft) | (s1 << (64 - sft)), 0);
-        limbs_add(limb, (s1 >> sft) | (s2 << (64 - sft)), 64);
-        limbs_add(limb, s2 >> sft, 128);
-      } else {
-        limbs_add(limb, s0, off);
-        limbs_add(limb, s1, off + 64);
-        limbs_add(limb, s2, off + 128);
-      }
       for (int ex = 1; ex < 255; ++ex) {   // m^2 = hi * 2^24 + lo, at 2^(2 ex - 300)
         limbs_add(limb, far_hist[0][ex], 2 * ex + 22);
         limbs_add(limb, far_hist[1][ex], 2 * ex - 2);
@@ -468,21 +519,33 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   }
 }
 
-// Enough threads that each holds at most kMaxVec vectors, in whole waves.
-dim3 row_block(int64_t k, int e) {
+// Threads for a row of k elements, e per vector, so that each holds about
+// vpt (<= kMaxVec) vectors, in whole waves; beyond 1024 threads the loops
+// past the register-held vectors take the rest.
+dim3 row_block(int64_t k, int e, int vpt) {
   const int64_t nvec = k / e;
-  int64_t thr = (nvec + BL_QUANT_VPT - 1) / BL_QUANT_VPT;
+  int64_t thr = (nvec + vpt - 1) / vpt;
   thr = ((thr + 63) / 64) * 64;
   if (thr < 64) thr = 64;
   if (thr > 64 * kMaxWaves) thr = 64 * kMaxWaves;
   return dim3((unsigned)thr);
 }
 
+// SubLN does more arithmetic per element than act-quant: the largest vpt of
+// 8, 4, 2 that still gives the launch two waves per SIMD (t rows of
+// blockDim / 64 waves against 1024 SIMDs), so short launches spread each row
+// over more waves.
+int subln_vpt(int64_t t, int64_t k, int e) {
+  int vpt = kMaxVec;
+  while (vpt > 2 && t * (int64_t)(row_block(k, e, vpt).x / 64) < 2048) vpt /= 2;
+  return vpt;
+}
+
 }  // namespace
 
 hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* xq,
                         float* absmax, int32_t* rowsum, hipStream_t stream) {
-  const dim3 grid((unsigned)t), block = row_block(k, bf16 ? 8 : 4);
+  const dim3 grid((unsigned)t), block = row_block(k, bf16 ? 8 : 4, kQuantVpt);
   const uint4* xv = static_cast<const uint4*>(x);
   if (bf16)
     k_act_quant<1><<<grid, block, 0, stream>>>(xv, (int)k, xq, absmax, rowsum);
@@ -494,7 +557,8 @@ hipError_t launch_quant(const void* x, int bf16, int64_t t, int64_t k, int8_t* x
 hipError_t launch_subln_quant(const void* x, int bf16, const float* gain, float eps_n, int64_t t,
                               int64_t k, int8_t* xq, float* scale, int32_t* rowsum,
                               hipStream_t stream) {
-  const dim3 grid((unsigned)t), block = row_block(k, bf16 ? 8 : 4);
+  const int e = bf16 ? 8 : 4;
+  const dim3 grid((unsigned)t), block = row_block(k, e, subln_vpt(t, k, e));
   const uint4* xv = static_cast<const uint4*>(x);
   if (bf16)
     k_subln_quant<1><<<grid, block, 0, stream>>>(xv, (int)k, gain, eps_n, xq, scale, rowsum);

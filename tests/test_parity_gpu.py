@@ -381,12 +381,15 @@ def test_subln_quant(bl, t, k, dtype):
 
 
 def _subln_special_rows(k, seed):
-    """Rows that take every branch of the exact sum of squares: elements far
-    below their wave's largest (the per-exponent buckets), a row of
-    subnormals (the sum shifted down), zeros, a constant row, one huge entry
-    among ones, and the worked example's values tiled."""
+    """Rows that take every branch of the exact sum of squares: nonzero
+    elements more than 31 binades below the row's largest (the per-exponent
+    buckets), a row of subnormals (the sum shifted down), zeros, a constant
+    row, one huge entry among ones, the worked example's values tiled, and
+    the window's edge: every binade from 0 to 31 below the largest (fixed
+    point, both bf16 accumulators) and the same with one element 32 below
+    (buckets)."""
     rng = np.random.default_rng(seed)
-    x = np.zeros((8, k), np.float32)
+    x = np.zeros((10, k), np.float32)
     x[0] = rng.standard_normal(k) * 10.0 ** rng.uniform(-30, 17, k)
     x[1] = rng.standard_normal(k) * np.float32(1e-39)
     x[2] = 0.0
@@ -398,6 +401,9 @@ def _subln_special_rows(k, seed):
     x[6] = np.tile(np.float32([-1.0, -1.0, 4.0, 2.0]), k // 4)
     x[7] = rng.standard_normal(k) * np.float32(1e-30)
     x[7, 5] = np.float32(3e-3)
+    x[8] = np.float32(-1.5) * np.exp2(-(np.arange(k) % 32)).astype(np.float32)
+    x[9] = x[8]
+    x[9, k // 2] = np.float32(2.0 ** -32)
     g = (1.0 + 0.5 * rng.standard_normal(k)).astype(np.float32)
     g[:4] = [1.0, 0.5, 0.25, 0.5]
     return x, g
