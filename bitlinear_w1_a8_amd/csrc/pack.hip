@@ -70,17 +70,51 @@ __global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __res
   }
 }
 
-// One thread: exact big-integer combine, single rounding to binary64, mean.
-__global__ void k_gamma_finalize(const unsigned long long* __restrict__ buckets, int64_t count,
-                                 float* __restrict__ gamma) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// One wave: the exact sum of v_b * 2^(b - 1) over buckets b = 1 .. 254 (units
+// of 2^-149) as a 384-bit integer, rounded once to binary64; then the mean.
+// Lane l takes buckets 4l .. 4l + 3, whose pieces (each v_b << ((b - 1) % 32),
+// 96 bits) fall in four consecutive 32-bit words from word (4l - 1) / 32, and
+// adds them into twelve 64-bit word sums in LDS (below 64 lanes x 4 pieces of
+// 32 bits each, so none overflows); one lane then propagates the carries.
+__global__ __launch_bounds__(64) void k_gamma_finalize(const unsigned long long* __restrict__ buckets,
+                                                       int64_t count, float* __restrict__ gamma) {
   constexpr int kLimbs = 12;  // 384 bits > 253 + 64 + 8
-  uint32_t limb[kLimbs];
-  for (int i = 0; i < kLimbs; ++i) limb[i] = 0;
-  for (int b = 1; b < 255; ++b) limbs_add(limb, buckets[b], b - 1);  // v * 2^(b-1) * 2^-149
-  const double sum = limbs_to_f64(limb, -149);
-  const double mean = sum / (double)count;
-  gamma[0] = (float)mean;
+  __shared__ unsigned long long wsum[kLimbs];
+  __shared__ uint32_t limb[kLimbs];
+  const int l = threadIdx.x;
+  if (l < kLimbs) wsum[l] = 0ull;
+  __syncthreads();
+  const int w0 = max(4 * l - 1, 0) >> 5;
+  unsigned long long win[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * l + j;
+    const unsigned long long v = (b >= 1 && b <= 254) ? buckets[b] : 0ull;
+    const int off = max(b - 1, 0), sh = off & 31;
+    const unsigned long long lo = v << sh;
+    const uint32_t p0 = (uint32_t)lo, p1 = (uint32_t)(lo >> 32);
+    const uint32_t p2 = sh ? (uint32_t)(v >> (64 - sh)) : 0u;
+    const bool d0 = (off >> 5) == w0;   // else one word further up
+    win[0] += d0 ? p0 : 0u;
+    win[1] += d0 ? p1 : p0;
+    win[2] += d0 ? p2 : p1;
+    win[3] += d0 ? 0u : p2;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (win[i]) atomicAdd(&wsum[w0 + i], win[i]);
+  __syncthreads();
+  if (l == 0) {
+    unsigned long long carry = 0;
+    for (int i = 0; i < kLimbs; ++i) {
+      const unsigned long long s = wsum[i] + carry;   // < 2^41 + 2^10
+      limb[i] = (uint32_t)s;
+      carry = s >> 32;
+    }
+    const double sum = limbs_to_f64(limb, -149);
+    const double mean = sum / (double)count;
+    gamma[0] = (float)mean;
+  }
 }
 
 __device__ __forceinline__ uint32_t tern_code(float w, float d) {
