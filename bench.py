@@ -393,6 +393,55 @@ def rotated_time_us(torch, body, n, stream, reps=10):
     return time_graph(torch, g, reps, 2, stream) * 1e3 / (reps * n)
 
 
+def pack_extra(torch, binding, dev, stream):
+    """Step A0 on the device: bitlinear_pack_weights on seeded fp32 latent
+    weights (N(0, 0.02)) of the 2B and 70B-class shapes, microseconds per
+    call from HIP events around ten eager calls (the buckets zeroed, the
+    exact histogram of |w|, gamma, then ternarise and pack).  GB/s counts one
+    read of W plus the packed write against the 8 TB/s peak; gamma has to be
+    known before any weight is rounded, so the method reads W twice, and the
+    two-read figure is given beside it."""
+    lib = binding.load()
+    out = {}
+    shapes = ((2560, 2560), (2560, 640), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192))
+    for k, n in shapes:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(8000 + n + k)
+        w = torch.randn((n, k), device=dev, generator=gen) * 0.02
+        packed = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(int(lib.bitlinear_pack_workspace_bytes(n, k)), dtype=torch.uint8, device=dev)
+        h = ctypes.c_void_p(stream.cuda_stream)
+
+        def call():
+            rc = lib.bitlinear_pack_weights(ptr(w), n, k, ptr(packed), ptr(gamma), ptr(ws), ws.numel(), h)
+            if rc:
+                raise RuntimeError(lib.bitlinear_last_error().decode())
+
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                call()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            best = float("inf")
+            for _ in range(3):
+                e0.record(stream)
+                for _ in range(10):
+                    call()
+                e1.record(stream)
+                e1.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1e3 / 10)
+        one = 4.0 * n * k + n * k / 4 + 4
+        two = 8.0 * n * k + n * k / 4 + 4
+        out[f"{k}->{n}"] = {"pack_us": round(best, 1),
+                            "gb_s_one_read": round(one / best / 1e3, 1),
+                            "frac_of_hbm_peak_one_read": round(one / best / 1e3 / HBM_PEAK_GBS, 4),
+                            "gb_s_two_reads": round(two / best / 1e3, 1)}
+        del w, packed
+        torch.cuda.empty_cache()
+    return out
+
+
 def subln_extra(torch, binding, dev, stream):
     """The sub-layer norm fused with act-quant against act-quant alone: bf16
     rows of K in {2560, 6912} at T in {1, 2048}, over 64 distinct activation
@@ -968,7 +1017,7 @@ def main():
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     want = set(args.extra.split(",")) if args.extra != "all" else {
-        "calib", "toy", "prefill", "crossover", "70b", "subln", "gated", "lut", "binary"}
+        "calib", "toy", "prefill", "crossover", "70b", "subln", "gated", "lut", "binary", "pack"}
     if not args.no_extra:
         if "calib" in want:
             extra["device_ceilings"] = calibration(torch, binding, dev, stream)
@@ -984,6 +1033,8 @@ def main():
             extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
         if "subln" in want:
             extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
+        if "pack" in want:
+            extra["a0_pack"] = pack_extra(torch, binding, dev, stream)
         if "gated" in want:
             extra["gated_relu2_ffn"] = gated_extra(torch, binding, dev, stream)
         if "binary" in want:

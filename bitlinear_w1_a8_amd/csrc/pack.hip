@@ -29,6 +29,9 @@ namespace {
 
 constexpr int kHistThreads = 256;
 constexpr int kHistWaves = kHistThreads / 64;
+#ifndef BL_GAMMA_HIST_VPT
+#define BL_GAMMA_HIST_VPT 16            // 16-byte vectors per thread the histogram grid aims for
+#endif
 
 __global__ void k_zero_u64(unsigned long long* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -43,8 +46,9 @@ __device__ __forceinline__ void hist_add(unsigned long long* h, float v) {
   if (m) atomicAdd(&h[e], (unsigned long long)m);
 }
 
-// Grid-stride pass over all N*K weights; one LDS histogram per wave cuts
-// contention, then each block adds its sums to the global buckets.
+// Grid-stride pass over all N*K weights, four 16-byte loads in flight per
+// thread; one LDS histogram per wave cuts contention, then each block adds
+// its sums to the global buckets.
 __global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __restrict__ w4,
                                                              int64_t n4,
                                                              unsigned long long* __restrict__ buckets) {
@@ -54,7 +58,20 @@ __global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __res
   __syncthreads();
   unsigned long long* mine = h[threadIdx.x >> 6];
   const int64_t stride = (int64_t)gridDim.x * kHistThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < n4; i += stride) {
+  int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = w4[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      hist_add(mine, v[u].x);
+      hist_add(mine, v[u].y);
+      hist_add(mine, v[u].z);
+      hist_add(mine, v[u].w);
+    }
+  }
+  for (; i < n4; i += stride) {
     const float4 v = w4[i];
     hist_add(mine, v.x);
     hist_add(mine, v.y);
@@ -163,6 +180,18 @@ int grid_for(int64_t items, int threads, int cap) {
   return (int)g;
 }
 
+// Blocks of the histogram pass: about BL_GAMMA_HIST_VPT vectors per thread,
+// from 256 to 2048 blocks (every block ends with global atomics on the same
+// few buckets, so small matrices take fewer blocks).
+int hist_grid(int64_t n4) {
+  int64_t g = (n4 + (int64_t)kHistThreads * BL_GAMMA_HIST_VPT - 1) /
+              ((int64_t)kHistThreads * BL_GAMMA_HIST_VPT);
+  const int64_t lo = (n4 + kHistThreads - 1) / kHistThreads;   // one vector per thread
+  if (g < 256) g = lo < 256 ? lo : 256;
+  if (g > 2048) g = 2048;
+  return (int)g;
+}
+
 }  // namespace
 
 hipError_t launch_gamma(const float* w, int64_t n, int64_t k, float* gamma,
@@ -170,7 +199,7 @@ hipError_t launch_gamma(const float* w, int64_t n, int64_t k, float* gamma,
   const int64_t count = n * k;
   k_zero_u64<<<1, kGammaBuckets, 0, stream>>>(buckets, kGammaBuckets);
   const int64_t n4 = count / 4;
-  k_gamma_hist<<<grid_for(n4, kHistThreads, 2048), kHistThreads, 0, stream>>>(
+  k_gamma_hist<<<hist_grid(n4), kHistThreads, 0, stream>>>(
       reinterpret_cast<const float4*>(w), n4, buckets);
   k_gamma_finalize<<<1, 64, 0, stream>>>(buckets, count, gamma);
   return hipGetLastError();
