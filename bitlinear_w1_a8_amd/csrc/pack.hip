@@ -8,10 +8,12 @@
 // gamma must be bit-identical however the sum is split over the GPU, so it is
 // computed exactly: every |w| is m * 2^(e-150) with a 24-bit integer m and a
 // biased exponent e (subnormals use e = 1 without the hidden bit).  The
-// integers m are summed per exponent in uint64 (at most 2^26 * 2^10 entries
-// of < 2^24 each stay below 2^64), the 254 bucket sums are combined into one
-// 384-bit integer, and that is rounded once to binary64, divided by N*K in
-// binary64 and rounded to binary32.
+// total is gathered in 256 uint64 buckets, bucket b counting units of
+// 2^(b - 150): most weights through exact fixed-point sums per wave placed
+// there as 32-bit pieces, the rest one m at a time (below 2^62 + 2^45 per
+// bucket for N*K <= 2^38); the 254 bucket sums are combined into one 384-bit
+// integer, and that is rounded once to binary64, divided by N*K in binary64
+// and rounded to binary32.
 #include <mutex>
 
 #include "bl_internal.h"
@@ -28,7 +30,6 @@ static __device__ __align__(256) unsigned long long scratch[kGammaBuckets];
 namespace {
 
 constexpr int kHistThreads = 256;
-constexpr int kHistWaves = kHistThreads / 64;
 #ifndef BL_GAMMA_HIST_VPT
 #define BL_GAMMA_HIST_VPT 16            // 16-byte vectors per thread the histogram grid aims for
 #endif
@@ -38,52 +39,32 @@ __global__ void k_zero_u64(unsigned long long* __restrict__ p, int n) {
   if (i < n) p[i] = 0ull;
 }
 
-__device__ __forceinline__ void hist_add(unsigned long long* h, float v) {
+// |w| = m * 2^(e - 150): 24-bit significand, biased exponent (1 for subnormals).
+__device__ __forceinline__ void split_abs(float v, uint32_t& m, int& e) {
   const uint32_t u = __float_as_uint(v) & 0x7fffffffu;
-  uint32_t e = u >> 23;
-  uint32_t m = u & 0x7fffffu;
+  e = (int)(u >> 23);
+  m = u & 0x7fffffu;
   if (e) m |= 0x800000u; else e = 1;
-  if (m) atomicAdd(&h[e], (unsigned long long)m);
 }
 
-// Grid-stride pass over all N*K weights, four 16-byte loads in flight per
-// thread; one LDS histogram per wave cuts contention, then each block adds
-// its sums to the global buckets.
-__global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __restrict__ w4,
-                                                             int64_t n4,
-                                                             unsigned long long* __restrict__ buckets) {
-  __shared__ unsigned long long h[kHistWaves][kGammaBuckets];
-  for (int i = threadIdx.x; i < kHistWaves * kGammaBuckets; i += kHistThreads)
-    (&h[0][0])[i] = 0ull;
-  __syncthreads();
-  unsigned long long* mine = h[threadIdx.x >> 6];
-  const int64_t stride = (int64_t)gridDim.x * kHistThreads;
-  int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x;
-  for (; i + 3 * stride < n4; i += 4 * stride) {
-    float4 v[4];
+// The wave's fixed-point sums (lo, hi: integers in units of 2^(u - 150)),
+// added over the wave, into the block's buckets: bucket b counts units of
+// 2^(b - 150), so 32-bit piece j goes to bucket u + 32j.  A lane's sum is below
+// 2^83 (at most 2^19 terms below 2^64), the wave's below 2^89: three pieces.
+// Called by every lane of the wave.
+__device__ __forceinline__ void flush_fixed(unsigned long long lo, unsigned long long hi, int u,
+                                            unsigned long long* h, int lane) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = w4[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      hist_add(mine, v[u].x);
-      hist_add(mine, v[u].y);
-      hist_add(mine, v[u].z);
-      hist_add(mine, v[u].w);
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+    const unsigned long long s = lo + l2;
+    hi += h2 + (s < l2 ? 1ull : 0ull);
+    lo = s;
   }
-  for (; i < n4; i += stride) {
-    const float4 v = w4[i];
-    hist_add(mine, v.x);
-    hist_add(mine, v.y);
-    hist_add(mine, v.z);
-    hist_add(mine, v.w);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < kGammaBuckets; b += kHistThreads) {
-    unsigned long long s = 0;
-#pragma unroll
-    for (int wv = 0; wv < kHistWaves; ++wv) s += h[wv][b];
-    if (s) atomicAdd(&buckets[b], s);
+  if (lane == 0) {
+    if (lo & 0xffffffffull) atomicAdd(&h[u], lo & 0xffffffffull);
+    if (lo >> 32) atomicAdd(&h[u + 32], lo >> 32);
+    if (hi) atomicAdd(&h[u + 64], hi);
   }
 }
 
@@ -93,20 +74,22 @@ __global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __res
 // 96 bits) fall in four consecutive 32-bit words from word (4l - 1) / 32, and
 // adds them into twelve 64-bit word sums in LDS (below 64 lanes x 4 pieces of
 // 32 bits each, so none overflows); one lane then propagates the carries.
-__global__ __launch_bounds__(64) void k_gamma_finalize(const unsigned long long* __restrict__ buckets,
-                                                       int64_t count, float* __restrict__ gamma) {
-  constexpr int kLimbs = 12;  // 384 bits > 253 + 64 + 8
-  __shared__ unsigned long long wsum[kLimbs];
-  __shared__ uint32_t limb[kLimbs];
-  const int l = threadIdx.x;
-  if (l < kLimbs) wsum[l] = 0ull;
-  __syncthreads();
+constexpr int kGammaLimbs = 12;  // 384 bits > 253 + 64 + 8
+__device__ void gamma_finalize_wave(const unsigned long long* buckets, int64_t count,
+                                    float* gamma, unsigned long long* wsum, uint32_t* limb_arr,
+                                    int l) {
+  if (l < kGammaLimbs) wsum[l] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int w0 = max(4 * l - 1, 0) >> 5;
   unsigned long long win[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = 4 * l + j;
-    const unsigned long long v = (b >= 1 && b <= 254) ? buckets[b] : 0ull;
+    const unsigned long long v =
+        (b >= 1 && b <= 254)
+            ? __hip_atomic_load(&buckets[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : 0ull;
     const int off = max(b - 1, 0), sh = off & 31;
     const unsigned long long lo = v << sh;
     const uint32_t p0 = (uint32_t)lo, p1 = (uint32_t)(lo >> 32);
@@ -120,10 +103,12 @@ __global__ __launch_bounds__(64) void k_gamma_finalize(const unsigned long long*
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (win[i]) atomicAdd(&wsum[w0 + i], win[i]);
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (l == 0) {
+    uint32_t (&limb)[kGammaLimbs] = *reinterpret_cast<uint32_t(*)[kGammaLimbs]>(limb_arr);
     unsigned long long carry = 0;
-    for (int i = 0; i < kLimbs; ++i) {
+    for (int i = 0; i < kGammaLimbs; ++i) {
       const unsigned long long s = wsum[i] + carry;   // < 2^41 + 2^10
       limb[i] = (uint32_t)s;
       carry = s >> 32;
@@ -132,6 +117,101 @@ __global__ __launch_bounds__(64) void k_gamma_finalize(const unsigned long long*
     const double mean = sum / (double)count;
     gamma[0] = (float)mean;
   }
+}
+
+// Grid-stride pass over all N*K weights, four 16-byte loads per lane and
+// step, the next step's loads issued before the current step's arithmetic.
+// Each wave takes a reference exponent R two binades above the largest of its
+// first 16 x 64 weights and every lane adds m << (e - u), u = R - kFixWindow
+// (at least 1), for each normal weight with u <= e <= R into a 128-bit
+// integer: every term is below 2^64 and the sum is exact.  Other nonzero
+// weights (subnormals, or outside that window: none or few in a weight
+// matrix) go straight into the block's LDS buckets, and at the end each wave
+// adds its lanes' sums and moves the total there as three 32-bit pieces.
+// Each block then adds its nonzero buckets to the global ones.
+constexpr int kFixWindow = 40;
+constexpr int kFixMaxE = 200;   // u + 64 <= 224 stays inside the buckets
+__global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __restrict__ w4,
+                                                             int64_t n4,
+                                                             unsigned long long* __restrict__ buckets) {
+  __shared__ unsigned long long h[kGammaBuckets];
+  for (int i = threadIdx.x; i < kGammaBuckets; i += kHistThreads) h[i] = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * kHistThreads;
+  // four vectors from i on, stride apart; past the end: zeros (the address
+  // clamped, so every load stays in bounds and needs no branch)
+  auto load = [&](int64_t i, uint32_t (&b)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t idx = i + q * stride;
+      const float4 v = w4[idx < n4 ? idx : n4 - 1];
+      const bool in = idx < n4;
+      b[4 * q] = in ? __float_as_uint(v.x) : 0u;
+      b[4 * q + 1] = in ? __float_as_uint(v.y) : 0u;
+      b[4 * q + 2] = in ? __float_as_uint(v.z) : 0u;
+      b[4 * q + 3] = in ? __float_as_uint(v.w) : 0u;
+    }
+  };
+  int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x;
+  uint32_t cur[16], nxt[16];
+  load(i, cur);                                  // zeros for lanes past the end
+  int em = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) em = max(em, (int)((cur[q] & 0x7fffffffu) >> 23));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) em = max(em, __shfl_xor(em, o));
+  const int R = min(em + 2, kFixMaxE);           // wave-uniform
+  const int u = max(R - kFixWindow, 1);
+  const uint32_t span = (uint32_t)(R - u);
+  unsigned long long lo = 0ull, hi = 0ull;
+  if (i < n4) {
+    for (;;) {
+      const int64_t in = i + 4 * stride;
+      const bool more = in < n4;
+      if (more) load(in, nxt);
+      uint32_t rare = 0u;                        // nonzero: some weight outside the window
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t b = cur[q] & 0x7fffffffu;
+        const int d = (int)(b >> 23) - u;        // subnormals and zeros: below the window
+        const bool fix = (uint32_t)d <= span;
+        const uint32_t m = fix ? ((b & 0x7fffffu) | 0x800000u) : 0u;
+        const unsigned long long t = (unsigned long long)m << (d & 63);
+        const unsigned long long s = lo + t;
+        hi += s < t ? 1ull : 0ull;
+        lo = s;
+        rare |= fix ? 0u : b;
+      }
+      if (rare) {                                // rare: outside the window
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          uint32_t m;
+          int e;
+          split_abs(__uint_as_float(cur[q]), m, e);
+          if (m != 0u && (e < u || e > R || (cur[q] & 0x7f800000u) == 0u))
+            atomicAdd(&h[e], (unsigned long long)m);
+        }
+      }
+      if (!more) break;
+      i = in;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) cur[q] = nxt[q];
+    }
+  }
+  flush_fixed(lo, hi, u, h, lane);               // every lane of the wave
+  __syncthreads();
+  for (int b = threadIdx.x; b < kGammaBuckets; b += kHistThreads) {
+    const unsigned long long s = h[b];
+    if (s) atomicAdd(&buckets[b], s);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_gamma_finalize(const unsigned long long* __restrict__ buckets,
+                                                       int64_t count, float* __restrict__ gamma) {
+  __shared__ unsigned long long wsum[kGammaLimbs];
+  __shared__ uint32_t limb[kGammaLimbs];
+  gamma_finalize_wave(buckets, count, gamma, wsum, limb, threadIdx.x);
 }
 
 __device__ __forceinline__ uint32_t tern_code(float w, float d) {

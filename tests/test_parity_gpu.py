@@ -146,8 +146,30 @@ def _awkward_matrix():
     return w
 
 
+def _huge_matrix():
+    """Exponents from 2^-100 to 2^120: some above where the histogram pass
+    sums in fixed point, the rest spread over more than its window."""
+    rng = np.random.default_rng(78)
+    mant = rng.random((64, 128)) + 0.5
+    expo = rng.integers(-100, 121, size=(64, 128))
+    w = (mant * np.exp2(expo.astype(np.float64))).astype(np.float32)
+    return w * np.where(rng.random((64, 128)) < 0.5, -1, 1).astype(np.float32)
+
+
+def _late_large_matrix():
+    """Small weights first, then a few far larger ones late in the scan: the
+    sums taken so far move into the buckets and the reference rises."""
+    w = wl.latent_weights(128, 512, 0.02, 79)
+    w[100, 7] = np.float32(1e20)
+    w[127, 511] = np.float32(-3e36)
+    w[120, 300] = np.float32(7.5e-3)
+    return w
+
+
 SPECIAL = {
     "all_zero": lambda: np.zeros((32, 64), np.float32),
+    "huge_exponents": _huge_matrix,
+    "late_large": _late_large_matrix,
     "constant": lambda: np.full((8, 128), np.float32(-0.0123), np.float32),
     "ties": _tie_matrix,
     "awkward_exponents": _awkward_matrix,
