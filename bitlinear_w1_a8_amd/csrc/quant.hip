@@ -219,16 +219,18 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 // d = E - e for an element with exponent field e (e = 1 for subnormals and
 // zero).  The first pass also finds the smallest nonzero |x|; when every
 // nonzero element has d <= 31 (ordinary data) each lane adds its squares
-// exactly in fixed point at the row's exponent, branch-free:
+// exactly in fixed point at the row's exponent:
 //  - binary32 input, x = m * 2^(e-150) with a 24-bit m: m^2 << (62 - 2d)
-//    into a 128-bit integer (fewer than 2^17 terms below 2^110);
-//  - bf16 input, x = m * 2^(e-134) with an 8-bit m: x^2 scaled by a power
-//    of two into one of two binary64 accumulators, d <= 15 in units of
-//    2^(2E-298) and 16 <= d <= 31 in units of 2^(2E-330).  Each scaled
-//    square is an integer m^2 * 2^(2(15-d)) or m^2 * 2^(2(31-d)) below
-//    2^46, and a lane adds at most 128 of them (K <= 131072 over at most
-//    1024 lanes), so every partial sum is an integer below 2^53 and each
-//    binary64 operation is exact.
+//    into a 128-bit integer (fewer than 2^17 terms below 2^110), branch-free;
+//  - bf16 input, x = m * 2^(e-134) with an 8-bit m: x^2 by binary64 FMAs
+//    into one of two accumulators, d <= 15 (a multiple of 2^(2E-298)) and
+//    16 <= d <= 31 (a multiple of 2^(2E-330)).  Each square is below 2^46 of
+//    its window's units and a lane adds at most 128 of them (K <= 131072
+//    over at most 1024 lanes), so every partial sum is a multiple of the
+//    unit below 2^53 units and each FMA is exact; the two sums are then
+//    scaled to integers by powers of two.  A lane whose own smallest
+//    nonzero |x| has d <= 15 (nearly every lane) uses the first only and
+//    tests nothing per element.
 // The lanes' sums go to 128 bits in units of 2^(2E-362), are added across
 // the wave, and one thread adds the waves' sums in 192 bits and rounds the
 // total once to binary64.  A row with a nonzero element more than 31
@@ -284,17 +286,15 @@ __device__ __forceinline__ void add_square(U128& acc, float x, int ew) {
   u128_add(acc, sq << sh, (sq >> 1) >> (63 - sh));
 }
 
-// bf16 input: x^2 * 2^(2(149 - ew)) into a (d <= 15) or x^2 * 2^(2(165 - ew))
-// into b (16 <= d <= 31); thr = 2^(ew - 142), the smallest |x| with d <= 15
-// (0 when every element has it); ha, hb: high words of the two binary64 scales.
-__device__ __forceinline__ void add_square_bf16(double& a, double& b, float x, float thr,
-                                                int ha, int hb) {
-  const double xd = (double)x;
+// bf16 input: x^2 into a (d <= 15) or into b (16 <= d <= 31); thr =
+// 2^(ew - 142), the smallest |x| with d <= 15 (0 when every element has it).
+// Each square is exact in binary64, and every partial sum is a multiple of
+// its window's unit below 2^53 of them, so each FMA is exact.
+__device__ __forceinline__ void add_square_bf16(double& a, double& b, float x, float thr) {
   const bool near = fabsf(x) >= thr;
-  const double sa = __hiloint2double(near ? ha : 0, 0);
-  const double sb = __hiloint2double(near ? 0 : hb, 0);
-  a = fma(xd * sa, xd, a);
-  b = fma(xd * sb, xd, b);
+  const double xa = (double)(near ? x : 0.0f), xb = (double)(near ? 0.0f : x);
+  a = fma(xa, xa, a);
+  b = fma(xb, xb, b);
 }
 
 __device__ __forceinline__ U128 wave_sum_u128(U128 a) {
@@ -373,28 +373,59 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
     // 2. exact sum of squares, per lane at the row's exponent
     U128 acc;
     if constexpr (BF16) {
-      const float thr = ew > 16 ? __uint_as_float((uint32_t)(ew - 15) << 23) : 0.0f;
-      const int ha = (1321 - 2 * ew) << 20;     // 2^(2(149 - ew))
-      const int hb = (1353 - 2 * ew) << 20;     // 2^(2(165 - ew))
+      // a lane whose smallest nonzero |x| lies within 15 binades of the row's
+      // largest (nearly every lane of ordinary data) needs no window test
+      const uint32_t lnz = nz + 1u;              // this lane's smallest nonzero |x| bits, 0: none
+      const bool lane_near = lnz == 0u || ew - max((int)(lnz >> 23), 1) <= 15;
       double sa = 0.0, sb = 0.0;
+      if (lane_near) {
 #pragma unroll
-      for (int i = 0; i < kMaxVec; ++i) {
-        const int idx = tid + i * nthr;
-        if (idx < nvec) {
+        for (int i = 0; i < kMaxVec; ++i) {
+          const int idx = tid + i * nthr;
+          if (idx < nvec) {
+            float f[E];
+            elems<BF16>(v[i], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const double xd = (double)f[e];
+              sa = fma(xd, xd, sa);
+            }
+          }
+        }
+        for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
           float f[E];
-          elems<BF16>(v[i], f);
+          elems<BF16>(xr[idx], f);
 #pragma unroll
-          for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr, ha, hb);
+          for (int e = 0; e < E; ++e) {
+            const double xd = (double)f[e];
+            sa = fma(xd, xd, sa);
+          }
+        }
+      } else {
+        const float thr = ew > 16 ? __uint_as_float((uint32_t)(ew - 15) << 23) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kMaxVec; ++i) {
+          const int idx = tid + i * nthr;
+          if (idx < nvec) {
+            float f[E];
+            elems<BF16>(v[i], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr);
+          }
+        }
+        for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+          float f[E];
+          elems<BF16>(xr[idx], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr);
         }
       }
-      for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
-        float f[E];
-        elems<BF16>(xr[idx], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr, ha, hb);
-      }
-      // a in units of 2^(2 ew - 298) = 2^64 units, b in 2^(2 ew - 330) = 2^32 units
-      const unsigned long long ia = (unsigned long long)sa, ib = (unsigned long long)sb;
+      // scaled to integers: a in units of 2^(2 ew - 298) = 2^64 units, b in
+      // 2^(2 ew - 330) = 2^32 units (exact power-of-two products)
+      const unsigned long long ia =
+          (unsigned long long)(sa * __hiloint2double((1321 - 2 * ew) << 20, 0));   // 2^(2(149 - ew))
+      const unsigned long long ib =
+          (unsigned long long)(sb * __hiloint2double((1353 - 2 * ew) << 20, 0));   // 2^(2(165 - ew))
       acc.lo = ib << 32;
       acc.hi = ia + (ib >> 32);
     } else {
