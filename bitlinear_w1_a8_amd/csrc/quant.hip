@@ -6,7 +6,7 @@
 // s = 127 / max(a, eps) (IEEE binary32 division), q = clamp(rne(x * s)).
 //
 // One block per token row.  The row is read once into registers (up to
-// kMaxVec 16-byte vectors per thread), the absmax is reduced with DPP row
+// kQuantVpt 16-byte vectors per thread), the absmax is reduced with DPP row
 // operations inside each wave and across waves through LDS, and the same
 // registers are then scaled, rounded, clipped and stored as int8.
 //
@@ -19,9 +19,10 @@
 namespace bl {
 namespace {
 
-constexpr int kMaxVec = 8;      // 16-byte vectors held per thread
 constexpr int kMaxWaves = 16;   // up to 1024 threads per row
-constexpr int kQuantVpt = 4;    // vectors per thread of the act-quant launch
+constexpr int kSublnRegs = 4;   // 16-byte vectors of the row SubLN holds per thread
+constexpr int kQuantVpt = 4;    // vectors per thread of the act-quant launch, held in registers
+                                // (longer rows read the rest again); 64 VGPRs, eight waves per SIMD
 
 // DPP controls (GCN/CDNA encoding).
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
@@ -166,17 +167,17 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
 
-  uint4 v[kMaxVec];
+  uint4 v[kQuantVpt];
   int m = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
+  for (int i = 0; i < kQuantVpt; ++i) {
     const int idx = tid + i * nthr;
     if (idx < nvec) {
       v[i] = xr[idx];
       m = max(m, vec_absmax_bits<BF16>(v[i]));
     }
   }
-  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr)
+  for (int idx = tid + kQuantVpt * nthr; idx < nvec; idx += nthr)
     m = max(m, vec_absmax_bits<BF16>(xr[idx]));
 
   m = wave_max_u(m);
@@ -189,11 +190,11 @@ __global__ __launch_bounds__(1024) void k_act_quant(const uint4* __restrict__ x,
 
   int sum = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
+  for (int i = 0; i < kQuantVpt; ++i) {
     const int idx = tid + i * nthr;
     if (idx < nvec) quant_store<BF16>(v[i], s, qr + (int64_t)idx * E, sum);
   }
-  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr)
+  for (int idx = tid + kQuantVpt * nthr; idx < nvec; idx += nthr)
     quant_store<BF16>(xr[idx], s, qr + (int64_t)idx * E, sum);
 
   if (rowsum) {
@@ -244,8 +245,8 @@ constexpr int kSqShift = 62;       // bit of m^2 for an element at the row's exp
 constexpr int kSqWindow = 31;      // binades below the largest that the fixed point holds
 constexpr int kSqLimbs = 18;       // 576 bits: sums below 2^17 * 2^256 in units of 2^-298
 // a lane's bf16 squares: at most 128, each below 2^46, stay below 2^53
-static_assert(8 * (kMaxVec > BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)
-                       ? kMaxVec : BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)) <= 128,
+static_assert(8 * (kSublnRegs > BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)
+                       ? kSublnRegs : BITLINEAR_MAX_K / 8 / (64 * kMaxWaves)) <= 128,
               "bf16 squares per lane");
 
 struct U128 {
@@ -326,11 +327,11 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
 
   // 1. the row in registers; largest |x| and |u| = |x * g|, smallest nonzero |x|
-  uint4 v[kMaxVec];
+  uint4 v[kSublnRegs];
   int mx = 0, mu = 0;
   uint32_t nz = 0xffffffffu;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
+  for (int i = 0; i < kSublnRegs; ++i) {
     const int idx = tid + i * nthr;
     if (idx < nvec) {
       v[i] = xr[idx];
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
       mu = max(mu, absmax_bits(f));
     }
   }
-  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+  for (int idx = tid + kSublnRegs * nthr; idx < nvec; idx += nthr) {
     float f[E];
     elems<BF16>(xr[idx], f);
     mx = max(mx, absmax_bits(f));
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
       double sa = 0.0, sb = 0.0;
       if (lane_near) {
 #pragma unroll
-        for (int i = 0; i < kMaxVec; ++i) {
+        for (int i = 0; i < kSublnRegs; ++i) {
           const int idx = tid + i * nthr;
           if (idx < nvec) {
             float f[E];
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
             }
           }
         }
-        for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+        for (int idx = tid + kSublnRegs * nthr; idx < nvec; idx += nthr) {
           float f[E];
           elems<BF16>(xr[idx], f);
 #pragma unroll
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
       } else {
         const float thr = ew > 16 ? __uint_as_float((uint32_t)(ew - 15) << 23) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxVec; ++i) {
+        for (int i = 0; i < kSublnRegs; ++i) {
           const int idx = tid + i * nthr;
           if (idx < nvec) {
             float f[E];
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
             for (int e = 0; e < E; ++e) add_square_bf16(sa, sb, f[e], thr);
           }
         }
-        for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+        for (int idx = tid + kSublnRegs * nthr; idx < nvec; idx += nthr) {
           float f[E];
           elems<BF16>(xr[idx], f);
 #pragma unroll
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
     } else {
       acc = {0ull, 0ull};
 #pragma unroll
-      for (int i = 0; i < kMaxVec; ++i) {
+      for (int i = 0; i < kSublnRegs; ++i) {
         const int idx = tid + i * nthr;
         if (idx < nvec) {
           float f[E];
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
           for (int e = 0; e < E; ++e) add_square(acc, f[e], ew);
         }
       }
-      for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+      for (int idx = tid + kSublnRegs * nthr; idx < nvec; idx += nthr) {
         float f[E];
         elems<BF16>(xr[idx], f);
 #pragma unroll
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
   // 4. x_hat = RN32(u * r), quantised with step A1's scale
   int sum = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
+  for (int i = 0; i < kSublnRegs; ++i) {
     const int idx = tid + i * nthr;
     if (idx < nvec) {
       float f[E];
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
       quant_store_f(f, s, qr + (int64_t)idx * E, sum);
     }
   }
-  for (int idx = tid + kMaxVec * nthr; idx < nvec; idx += nthr) {
+  for (int idx = tid + kSublnRegs * nthr; idx < nvec; idx += nthr) {
     float f[E];
     elems_gain<BF16>(xr[idx], gain + idx * E, f);
 #pragma unroll
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(1024) void k_subln_quant(const uint4* __restrict__ 
 }
 
 // Threads for a row of k elements, e per vector, so that each holds about
-// vpt (<= kMaxVec) vectors, in whole waves; beyond 1024 threads the loops
+// vpt (at most the kernel's register vectors) vectors, in whole waves; beyond 1024 threads the loops
 // past the register-held vectors take the rest.
 dim3 row_block(int64_t k, int e, int vpt) {
   const int64_t nvec = k / e;
@@ -562,12 +563,12 @@ dim3 row_block(int64_t k, int e, int vpt) {
   return dim3((unsigned)thr);
 }
 
-// SubLN does more arithmetic per element than act-quant: the largest vpt of
-// 8, 4, 2 that still gives the launch two waves per SIMD (t rows of
-// blockDim / 64 waves against 1024 SIMDs), so short launches spread each row
-// over more waves.
+// SubLN does more arithmetic per element than act-quant: 4 vectors per
+// thread, or 2 where that leaves the launch below two waves per SIMD (t rows
+// of blockDim / 64 waves against 1024 SIMDs), so short launches spread each
+// row over more waves.
 int subln_vpt(int64_t t, int64_t k, int e) {
-  int vpt = kMaxVec;
+  int vpt = kSublnRegs;
   while (vpt > 2 && t * (int64_t)(row_block(k, e, vpt).x / 64) < 2048) vpt /= 2;
   return vpt;
 }
