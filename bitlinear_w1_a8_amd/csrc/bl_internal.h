@@ -14,9 +14,8 @@ namespace bl {
 constexpr float kEps = 1e-5f;
 constexpr float kQb = 127.0f;
 
-// Largest T that the automatic choice may send to the decode kernel; see
-// auto_algo for the rule per shape.
-constexpr int64_t kGemvMaxTokens = 64;
+// Largest T that the automatic choice sends to the decode kernel (auto_algo).
+constexpr int64_t kGemvMaxTokens = 32;
 
 // Compute units of the current device (looked up once per device).
 int device_cus();

@@ -702,6 +702,11 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_SPLIT_MAX_TILES
 #define BL_GEMM_SPLIT_MAX_TILES 128 // ... that make fewer than this many 64 x 128 tiles
 #endif
+#ifndef BL_GEMM_SPLIT64_MAX_TILES
+#define BL_GEMM_SPLIT64_MAX_TILES 40    // up to 64 tokens: 64 x 128 tiles in K parts below this many
+// (T = 64, 6912 -> 2560, 20 tiles: 23.9 -> 14.1 us; 2560 -> 6912, 54 tiles:
+// 12.4 -> 16.5 us, the clearing and finishing launches costing more there)
+#endif
 
 
 namespace {
@@ -711,7 +716,7 @@ namespace {
 // that still give most CUs a block, 64-row tiles (several blocks per CU) when
 // 128-row ones would leave CUs idle or rows unused, and a K split only for
 // long K with very few tiles.
-enum class Tiles { kWide, kNarrow, kM64W256, kM64W320, kM64W128, kSplit };
+enum class Tiles { kWide, kNarrow, kM64W256, kM64W320, kM64W128, kSplit, kSplit64 };
 
 Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow_w128,
                    bool allow_w320 = false) {
@@ -729,6 +734,10 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
     if (allow_w320 && w256 > cus && 8 * w320 >= 7 * cus && w320 <= cus) return Tiles::kM64W320;
     return Tiles::kM64W256;
   }
+  // a few tokens over few tiles: 64-row tiles, K in parts, so that the
+  // launch has work for every CU
+  if (allow_split && t <= 64 && w128 < BL_GEMM_SPLIT64_MAX_TILES && k / BK >= 8)
+    return Tiles::kSplit64;
   if (allow_split && k >= BL_GEMM_SPLIT_MIN_K && w128 < BL_GEMM_SPLIT_MAX_TILES && k / BK >= 8)
     return Tiles::kSplit;
   return Tiles::kM64W128;
@@ -747,7 +756,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
     return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   }
-  switch (choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true, true)) {
+  const Tiles choice = choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true, true);
+  switch (choice) {
     case Tiles::kWide:
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
@@ -763,20 +773,28 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
     case Tiles::kM64W128:
       return run_lds<4, 2, 1, 2, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                     1, 0, nullptr, nullptr, rowsum);
-    case Tiles::kSplit: {
-      // 128 x 512 tiles, K in parts: y is cleared, takes the exact int32
-      // partial sums by atomics and is rescaled in place
-      const int64_t nkt = k / BK, wide = ((t + 127) / 128) * ((n + 511) / 512);
-      int64_t parts = (BL_GEMM_SPLIT_ITEMS + wide - 1) / wide;
+    case Tiles::kSplit:
+    case Tiles::kSplit64: {
+      // 128 x 512 (or, up to 64 tokens, 64 x 128) tiles, K in parts: y is
+      // cleared, takes the exact int32 partial sums by atomics and is
+      // rescaled in place
+      const bool t64 = choice == Tiles::kSplit64;
+      const int64_t nkt = k / BK;
+      const int64_t tl = t64 ? ((t + 63) / 64) * ((n + 127) / 128)
+                             : ((t + 127) / 128) * ((n + 511) / 512);
+      int64_t parts = (BL_GEMM_SPLIT_ITEMS + tl - 1) / tl;
       int64_t steps = (nkt + parts - 1) / parts;
       if (steps < 4) steps = 4;
       parts = (nkt + steps - 1) / steps;             // every part has at least one step
       const int64_t total = t * n;
       k_clear_i32<<<(unsigned)std::min<int64_t>((total + 255) / 256, 4096), 256, 0, stream>>>(
           reinterpret_cast<int*>(y), total);
-      hipError_t e = run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
-                                                         stream, (int)parts, (int)steps, nullptr,
-                                                         nullptr, rowsum);
+      hipError_t e =
+          t64 ? run_lds<4, 2, 1, 2, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                       (int)parts, (int)steps, nullptr, nullptr, rowsum)
+              : run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc,
+                                                    stream, (int)parts, (int)steps, nullptr,
+                                                    nullptr, rowsum);
       if (e != hipSuccess) return e;
       const int col_blocks = (int)((n + 1023) / 1024);
       k_split_finish<<<(unsigned)(t * col_blocks), 256, 0, stream>>>(y, acc, gamma, absmax, (int)n,

@@ -1434,13 +1434,12 @@ hipError_t gemv_any(const uint8_t* packed, const float* gamma, const int8_t* xq,
 int auto_algo(int64_t t, int64_t n, int64_t k) {
   // Measured against the tiled MFMA kernel with its own tile choice: the
   // decode kernels win through T = 32 on the 2B shapes (2560 -> 6912 at
-  // T = 32: 8.4 against 12.1 us; 6912 -> 2560: 11.4 against 23.7); at T = 64
-  // they still win where the rows are long and few (6912 -> 2560: 17.7
-  // against 23.9 us) but not on wide, short rows (2560 -> 6912: 12.8
-  // against 12.4); from T = 128 on the MFMA kernel wins on both.
-  if (t <= 32) return BL_ALGO_GEMV;
-  if (t <= kGemvMaxTokens && n <= k) return BL_ALGO_GEMV;
-  return BL_ALGO_GEMM;
+  // T = 32: 8.5 against 12.6 us; 6912 -> 2560: 11.4 against 11.9, the tiled
+  // kernel splitting K there); from T = 64 on the tiled kernel wins on both
+  // (12.4 against 12.6 us; 14.1 against 17.6).
+  (void)n;
+  (void)k;
+  return t <= kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,

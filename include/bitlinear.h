@@ -89,8 +89,8 @@ typedef enum {
 typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 
 typedef enum {
-  BL_ALGO_AUTO = 0, /* decode kernel for T <= 32, and for T <= bitlinear_gemv_max_tokens()
-                       when N <= K (few, long rows); else GEMM (measured crossovers) */
+  BL_ALGO_AUTO = 0, /* decode kernel for T <= bitlinear_gemv_max_tokens() (32), else GEMM
+                       (measured crossovers) */
   BL_ALGO_GEMV = 1, /* streaming decode kernel, any T (tokens taken 64 at a time) */
   BL_ALGO_GEMM = 2, /* LDS-tiled int8 MFMA kernel, any T */
   BL_ALGO_LUT = 3   /* table-lookup decode kernel in the style of bitnet.cpp's TL1/TL2
@@ -108,8 +108,7 @@ int bitlinear_abi_version(void);
  * The pointer stays valid until the next call on the same thread. */
 const char* bitlinear_last_error(void);
 
-/* Largest T that BL_ALGO_AUTO sends to the decode (GEMV) kernel (for N <= K;
- * for N > K the limit is 32). */
+/* Largest T that BL_ALGO_AUTO sends to the decode (GEMV) kernel. */
 int64_t bitlinear_gemv_max_tokens(void);
 
 /* Bytes of device workspace that bitlinear_pack_weights needs for an N x K
