@@ -1240,10 +1240,14 @@ hipError_t run_dec(DecGroup& grp, int count, const DecShape& sh, size_t lds,
 #define BL_GEMV_PERSIST_CPW 2           // 256-k chunks per wave aimed for (at most 16 waves)
 #endif
 constexpr int kPersistMaxK = 28672;     // at most 7 chunks per wave at 16 waves
+// Tiles per block at most: the LDS header holds 17 ints per tile of the block
+// (with the staged row, 4.4 KB + K per block at 64 tiles).
+constexpr int kPersistMaxTpb = 64;
 
 bool persist_ok(int64_t t, int64_t n, int64_t k) {
-  return t == 1 && k % 256 == 0 && k <= kPersistMaxK &&
-         (n + 15) / 16 >= BL_GEMV_PERSIST_MIN_TILES;
+  const int64_t tiles = (n + 15) / 16;
+  return t == 1 && k % 256 == 0 && k <= kPersistMaxK && tiles >= BL_GEMV_PERSIST_MIN_TILES &&
+         tiles <= (int64_t)device_cus() * BL_GEMV_PERSIST_BPC * kPersistMaxTpb;
 }
 
 // Tiles in flight per wave and whether the B operands stay in registers, by
