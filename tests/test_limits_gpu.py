@@ -228,3 +228,75 @@ def test_max_rows_fused_bf16(bl, n):
     bad = np.flatnonzero(a != want)
     assert bad.size == 0, f"{bad.size} int32 sums differ, first rows {bad[:4]}"
     check_y(yh[None, :], want[None, :].astype(np.int32), gamma_ref, a_ref)
+
+
+def test_max_rows_binary(bl):
+    """Binary weights, N = 2^26 rows at one token (K = 256): rows of all -1
+    (byte 0x00) and all +1 (0xFF) alternate, sampled random rows."""
+    from oracle import binary_ref
+    rng = np.random.default_rng(4500)
+    n, k = N_MAX, 256
+    idx = sample_idx(rng, n)
+    t_s = np.where(rng.random((idx.size, k)) < 0.5, -1, 1).astype(np.int8)
+    packed = torch.empty((n, k // 8), dtype=torch.uint8, device="cuda")
+    const_byte = torch.tensor([0x00, 0xFF], dtype=torch.uint8, device="cuda")
+    rows = torch.arange(n, device="cuda", dtype=torch.int64)
+    packed[:] = const_byte[rows % 2][:, None]
+    del rows
+    packed[torch.from_numpy(idx).cuda()] = torch.from_numpy(binary_ref.pack_binary(t_s)).cuda()
+    gamma_ref = np.float32(0.0217)
+    gamma = torch.tensor([gamma_ref], device="cuda")
+    q = rng.integers(-127, 128, size=(1, k)).astype(np.int8)
+    a_ref = np.array([2.5], np.float32)
+    print(f"max rows binary: N={n} K={k}", flush=True)
+    y, acc = bl.forward_binary(packed, gamma, torch.from_numpy(q).cuda(),
+                               torch.from_numpy(a_ref).cuda(), want_acc=True)
+    a = host(acc)[0]
+    yh = host(y)[0]
+    del packed, y, acc
+    torch.cuda.empty_cache()
+    sq = int(q.astype(np.int64).sum())
+    want = (2 * (np.arange(n, dtype=np.int64) % 2) - 1) * sq
+    want[idx] = oracle.contract(q, t_s)[0]
+    bad = np.flatnonzero(a != want)
+    assert bad.size == 0, f"{bad.size} int32 sums differ, first rows {bad[:4]}"
+    check_y(yh[None, :], want[None, :].astype(np.int32), gamma_ref, a_ref)
+
+
+def test_max_tokens_subln(bl):
+    """SubLN + A1 over T = 2^24 bf16 rows (K = 16, gain 1): row r a constant
+    x_r, whose codes are sign(x) * 127 and whose scale the oracle gives from
+    one such row; sampled random rows against the oracle."""
+    from oracle import subln_ref
+    rng = np.random.default_rng(4600)
+    t, k = T_MAX, 16
+    idx = sample_idx(rng, t)
+    bits_s = wl.bf16_bits(rng.standard_normal((idx.size, k)).astype(np.float32))
+    vals = np.array([-3.5, -0.25, 0.0078125, 1.0, 0.0029296875, -15360.0, 6.0], np.float32)
+    vbits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    gain = np.ones(k, np.float32)
+    r = torch.arange(t, device="cuda", dtype=torch.int64)
+    row_bits = torch.from_numpy(vbits.view(np.int16)).cuda()[r % vals.size]
+    x = row_bits[:, None].expand(t, k).contiguous()
+    x[torch.from_numpy(idx).cuda()] = torch.from_numpy(bits_s.view(np.int16)).cuda()
+    del r, row_bits
+    print(f"max tokens subln: T={t} K={k}", flush=True)
+    xq, scale, rowsum = bl.subln_quant_act(x.view(torch.bfloat16), torch.from_numpy(gain).cuda())
+    del x
+    torch.cuda.empty_cache()
+    q_ref, s_ref, rs_ref, _ = subln_ref.subln_quant_act(bits_s, gain)
+    assert np.array_equal(host(xq[torch.from_numpy(idx).cuda()]), q_ref)
+    sc, rs = host(scale), host(rowsum)
+    assert np.array_equal(sc[idx].view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(rs[idx], rs_ref)
+    const_rows = np.repeat(vbits[:, None], k, axis=1)
+    qc, sc_c, rs_c, _ = subln_ref.subln_quant_act(const_rows, gain)
+    keep = np.ones(t, bool)
+    keep[idx] = False
+    j = np.arange(t) % vals.size
+    assert np.array_equal(sc[keep].view(np.uint32), sc_c[j[keep]].view(np.uint32))
+    assert np.array_equal(rs[keep], rs_c[j[keep]])
+    keep_d = torch.from_numpy(keep).cuda()
+    sel = torch.arange(t, device="cuda")[keep_d]
+    want_q = torch.from_numpy(qc).cuda()[sel % vals.size]
+    assert bool(torch.all(xq[sel] == want_q).item())
