@@ -1396,7 +1396,7 @@ hipError_t launch_linear_group(const bl_linear* probs, int count, int64_t t, int
                              q.gamma, q.x, nullptr, q.y + row0,
                              q.acc ? q.acc + row0 : nullptr, head ? q.xq : nullptr,
                              head ? q.absmax : nullptr, nullptr, nullptr, (int)rows, (int)q.K, 0,
-                             (int)q.N};
+                             (int)q.N, nullptr};
       ++np;
     }
   }
@@ -1471,7 +1471,8 @@ hipError_t launch_gated(const void* x, int bf16, const uint8_t* packed, const fl
     DecGroup grp = {};
     grp.T = (int)t;
     grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma_gate, x, nullptr,
-                          nullptr, acc, xq, absmax, gamma_up, h, (int)n, (int)k, 0};
+                          nullptr, acc, xq, absmax, gamma_up, h, (int)n, (int)k, 0, (int)n,
+                          nullptr};
     const DecShape sh = dec_shape(blocks, k, t);
     const size_t lds = dec_lds(t, k, rb, sh.rt);
     return bf16 ? run_dec<kBf16>(grp, 1, sh, lds, stream)

@@ -195,7 +195,6 @@ __global__ __launch_bounds__(kHistThreads) void k_gamma_hist(const float4* __res
       }
       if (!more) break;
       i = in;
-#pragma unroll
       for (int q = 0; q < 16; ++q) cur[q] = nxt[q];
     }
   }

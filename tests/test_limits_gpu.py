@@ -300,3 +300,47 @@ def test_max_tokens_subln(bl):
     sel = torch.arange(t, device="cuda")[keep_d]
     want_q = torch.from_numpy(qc).cuda()[sel % vals.size]
     assert bool(torch.all(xq[sel] == want_q).item())
+
+
+def test_max_outputs_gated(bl):
+    """Gated ReLU^2 with the largest output count, N = 2^25 (2^26 interleaved
+    gate / up rows) at one bf16 token, K = 256: row r of a constant code
+    (r % 3), so output i takes one of three (gate, up) sum pairs; sampled
+    outputs with random gate and up rows; every h checked against the
+    oracle's gated epilogue."""
+    rng = np.random.default_rng(4700)
+    n, k = N_MAX // 2, 256
+    idx = sample_idx(rng, n)
+    tg = rng.integers(-1, 2, size=(idx.size, k)).astype(np.int8)
+    tu = rng.integers(-1, 2, size=(idx.size, k)).astype(np.int8)
+    packed = torch.empty((2 * n, k // 4), dtype=torch.uint8, device="cuda")
+    const_byte = torch.tensor([0x00, 0x55, 0xAA], dtype=torch.uint8, device="cuda")
+    rows = torch.arange(2 * n, device="cuda", dtype=torch.int64)
+    packed[:] = const_byte[rows % 3][:, None]
+    del rows
+    di = torch.from_numpy(idx).cuda()
+    packed[2 * di] = torch.from_numpy(oracle.pack_ternary(tg)).cuda()
+    packed[2 * di + 1] = torch.from_numpy(oracle.pack_ternary(tu)).cuda()
+    gg_ref, gu_ref = np.float32(0.0123), np.float32(0.0311)
+    bits = wl.bf16_bits(rng.standard_normal((1, k)).astype(np.float32))
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    print(f"max outputs gated: N={n} K={k}", flush=True)
+    h, xq, absmax, acc = bl.gated_relu2(x, packed, torch.tensor([gg_ref], device="cuda"),
+                                        torch.tensor([gu_ref], device="cuda"), want_acc=True)
+    q_ref, a_ref, _ = oracle.quant_act(bits)
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(absmax).view(np.uint32), a_ref.view(np.uint32))
+    hb = host(h.view(torch.int16)).view(np.uint16)[0]
+    a = host(acc)[0]
+    del packed, h, acc
+    torch.cuda.empty_cache()
+    sq = int(q_ref.astype(np.int64).sum())
+    want = ((np.arange(2 * n, dtype=np.int64) % 3) - 1) * sq
+    want[2 * idx] = oracle.contract(q_ref, tg)[0]
+    want[2 * idx + 1] = oracle.contract(q_ref, tu)[0]
+    bad = np.flatnonzero(a != want)
+    assert bad.size == 0, f"{bad.size} int32 sums differ, first rows {bad[:4]}"
+    h_ref = oracle.gated_relu2(want[0::2][None, :].astype(np.int32),
+                               want[1::2][None, :].astype(np.int32), gg_ref, gu_ref, a_ref)
+    bad = np.flatnonzero(hb != np.asarray(h_ref).reshape(-1).view(np.uint16))
+    assert bad.size == 0, f"{bad.size} bf16 outputs differ, first {bad[:4]}"
