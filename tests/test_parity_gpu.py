@@ -242,7 +242,10 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               (1, 24576, 512), (1, 20480, 8448), (1, 12288, 16640),
               # the longest rows the boundary takes (K = 131072: the largest
               # sums, 127 K, are still exact in binary32)
-              (2, 40, 131072), (70, 300, 131072)]
+              (2, 40, 131072), (70, 300, 131072),
+              # up to 64 tokens over fewer than 40 tiles of 64 x 128: K split
+              # into parts, the last one short (18 and 54 steps of 128)
+              (33, 200, 2304), (64, 2560, 6912), (61, 4900, 1152)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
