@@ -702,6 +702,12 @@ hipError_t run(const uint8_t* packed, const float* gamma, const int8_t* xq, cons
 #ifndef BL_GEMM_SPLIT_MAX_TILES
 #define BL_GEMM_SPLIT_MAX_TILES 128 // ... that make fewer than this many 64 x 128 tiles
 #endif
+#ifndef BL_GEMM_SPLIT64_WIDE_TILES
+#define BL_GEMM_SPLIT64_WIDE_TILES 96   // any T: 64 x 128 tiles in K parts below this many ...
+#endif
+#ifndef BL_GEMM_SPLIT64_WIDE_STEPS
+#define BL_GEMM_SPLIT64_WIDE_STEPS 32   // ... when the rows take at least this many 128-wide steps
+#endif
 #ifndef BL_GEMM_SPLIT64_MAX_TILES
 #define BL_GEMM_SPLIT64_MAX_TILES 40    // up to 64 tokens: 64 x 128 tiles in K parts below this many
 // (T = 64, 6912 -> 2560, 20 tiles: 23.9 -> 14.1 us; 2560 -> 6912, 54 tiles:
@@ -737,6 +743,11 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
   // a few tokens over few tiles: 64-row tiles, K in parts, so that the
   // launch has work for every CU
   if (allow_split && t <= 64 && w128 < BL_GEMM_SPLIT64_MAX_TILES && k / BK >= 8)
+    return Tiles::kSplit64;
+  // any T over few tiles of long rows: the same split (6912 -> 2560 at
+  // T = 128 / 256, 40 / 80 tiles of 54 steps: 22.9 / 23.0 -> 18.0 / 21.6 us;
+  // with rows of 20 steps, 2560 -> 6912, it did not pay at 54 tiles)
+  if (allow_split && w128 < BL_GEMM_SPLIT64_WIDE_TILES && k / BK >= BL_GEMM_SPLIT64_WIDE_STEPS)
     return Tiles::kSplit64;
   if (allow_split && k >= BL_GEMM_SPLIT_MIN_K && w128 < BL_GEMM_SPLIT_MAX_TILES && k / BK >= 8)
     return Tiles::kSplit;

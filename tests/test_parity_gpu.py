@@ -227,9 +227,11 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # decode kernel edges: ragged N, T = 16 at the staging limit,
               # many waves per block, one chunk per wave
               (3, 37, 512), (16, 50, 2048), (2, 17, 8192), (1, 3, 256), (1, 1000, 28672),
-              # prefill kernel: K split into 38 parts (the last one short) on
-              # ragged T and N; the 128 x 256 tiles; the 128 x 512 tiles
-              (200, 1500, 28672), (1100, 3800, 512), (1500, 8100, 256),
+              # prefill kernel on ragged T and N: 48 tiles of 64 x 128 with K
+              # in 6 parts (the last one short); 112 tiles, which take
+              # 128 x 512 tiles with K in parts; the 128 x 256 tiles; the
+              # 128 x 512 tiles
+              (200, 1500, 28672), (200, 3500, 16384), (1100, 3800, 512), (1500, 8100, 256),
               # table-lookup kernel: 4-wave blocks with word loads and a short last chunk
               (40, 900, 3088),
               # decode kernel, several int8 tokens, 257 row tiles: two per block
