@@ -233,6 +233,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 #ifndef BL_GEMM_GROUP_M
 #define BL_GEMM_GROUP_M 4   // row blocks per group of the tile order
 #endif
+#ifndef BL_GEMM_BREG
+#define BL_GEMM_BREG 1      // two-bit weights of one-wave-row tiles straight into registers
+#endif
 
 // The exact sum from the contraction of the weight codes and the token's sum
 // of q: two-bit codes c = t + 1 give sum t*q = acc - sum q, one-bit codes
@@ -293,9 +296,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   __shared__ __align__(16) unsigned char A0[kABuf], A1[kABuf];
   __shared__ __align__(16) unsigned char A2[STAGES > 2 ? kABuf : 16];
   __shared__ __align__(16) unsigned char A3[STAGES > 3 ? kABuf : 16];
-  __shared__ __align__(16) unsigned char B0[kBBuf], B1[kBBuf];
-  __shared__ __align__(16) unsigned char B2[STAGES > 2 ? kBBuf : 16];
-  __shared__ __align__(16) unsigned char B3[STAGES > 3 ? kBBuf : 16];
+  // Two-bit weights of a tile with one row of waves skip LDS: each weight
+  // fragment is then read by one wave only, so each lane loads its own 16
+  // bytes per fragment and step into registers, STAGES - 1 steps ahead (the
+  // DMA write and the read of the weight tile leave the LDS traffic; T = 2048,
+  // 2560 -> 6912: 43.9 -> 41.6-42.1 us; 70B T = 256, 8192 -> 28672: 65.2-66.2
+  // -> 62.6-63.0 us).  With two rows of waves each fragment would be loaded
+  // twice, and that measured slower (6912 -> 2560 on 64 x 320 tiles: 47.1 ->
+  // 58.1 us).
+  constexpr bool kBReg = BL_GEMM_BREG != 0 && WBITS == 2 && WAVES_M == 1;
+  __shared__ __align__(16) unsigned char B0[kBReg ? 16 : kBBuf], B1[kBReg ? 16 : kBBuf];
+  __shared__ __align__(16) unsigned char B2[STAGES > 2 && !kBReg ? kBBuf : 16];
+  __shared__ __align__(16) unsigned char B3[STAGES > 3 && !kBReg ? kBBuf : 16];
   __shared__ float scale[BM];
   __shared__ double gm_gate[GATED ? BM : 1], gm_up[GATED ? BM : 1];   // gamma * m, binary64
   __shared__ int rsum[BM];   // each token's sum of q over the block's K range
@@ -387,18 +399,39 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
       boff[i] = (uint32_t)n * (uint32_t)KW;
     }
   }
-  auto issue = [&](int kt, unsigned char* As, unsigned char* Bs) {
+  // register weights: lane (m, h) of fragment j takes row wn*32*WNF + 32j + m,
+  // bytes 16h .. 16h + 15 of the step's 32
+  uint32_t roff[kBReg ? WNF : 1];
+  if constexpr (kBReg) {
+#pragma unroll
+    for (int j = 0; j < WNF; ++j) {
+      int n = n0 + wn * 32 * WNF + 32 * j + (lane & 31);
+      n = n < N ? n : N - 1;
+      roff[j] = (uint32_t)n * (uint32_t)KW + 4u * (lane >> 5);
+    }
+  }
+  uint4 breg[kBReg ? STAGES : 1][kBReg ? WNF : 1];
+  auto issue = [&](int kt, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    unsigned char* As = abuf(stage_c);
     const uint32_t k0 = kbase + (uint32_t)kt * BK;
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(xq + (aoff[i] + k0)),
                                        (lds_ptr_t)(As + min(wave * kAChunks + i, kATot - 1) * 1024),
                                        16, 0, 0);
+    if constexpr (kBReg) {
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)))),
-                                       (lds_ptr_t)(Bs + min(wave * kBChunks + i, kBTot - 1) * 1024),
-                                       16, 0, 0);
+      for (int j = 0; j < WNF; ++j)
+        breg[S][j] = *reinterpret_cast<const uint4*>(packed + (roff[j] + (k0 >> 4)));
+    } else {
+      unsigned char* Bs = bbuf(stage_c);
+#pragma unroll
+      for (int i = 0; i < kBChunks; ++i)
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)))),
+                                         (lds_ptr_t)(Bs + min(wave * kBChunks + i, kBTot - 1) * 1024),
+                                         16, 0, 0);
+    }
   };
 
   v16i acc[WMF][WNF];
@@ -414,13 +447,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   for (int i = 0; i < kAChunks; ++i) qpart[i] = 0;
 
   const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : K / BK;   // >= 1 (host)
-  constexpr int kLoads = kAChunks + kBChunks;     // this wave's loads per tile
+  constexpr int kLoads = kAChunks + (kBReg ? WNF : kBChunks);   // this wave's loads per tile
   static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
   // prologue: tiles 0 .. STAGES-2 (repeats of the last tile when K is short)
-  issue(0, abuf(I0{}), bbuf(I0{}));
-  if constexpr (STAGES >= 3) issue(nk > 1 ? 1 : 0, abuf(I1{}), bbuf(I1{}));
-  if constexpr (STAGES == 4) issue(nk > 2 ? 2 : nk - 1, abuf(I2{}), bbuf(I2{}));
+  issue(0, I0{});
+  if constexpr (STAGES >= 3) issue(nk > 1 ? 1 : 0, I1{});
+  if constexpr (STAGES == 4) issue(nk > 2 ? 2 : nk - 1, I2{});
   // tile 0 landed (the rest stays in flight) and the scale writes are done;
   // a fence-free barrier, as a fence would wait for every load
   wait_vm_lgkm0<kLoads * (STAGES - 2)>();
@@ -448,7 +481,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     // every load): past the end it re-fetches the last tile into a stage that
     // is never read again
     auto refill = [&]() {
-      issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, abuf(R{}), bbuf(R{}));
+      issue(kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1, R{});
     };
     if constexpr (!kLateRefill) refill();
     const unsigned char* At = abuf(stage_c) + (wm * 32 * WMF + m) * BK;
@@ -470,7 +503,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     }
     uint4 bw[WNF];
 #pragma unroll
-    for (int j = 0; j < WNF; ++j) bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * kBRow);
+    for (int j = 0; j < WNF; ++j) {
+      if constexpr (kBReg) bw[j] = breg[S][j];
+      else bw[j] = *reinterpret_cast<const uint4*>(Bt + j * 32 * kBRow);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int off = 16 * ((WBITS == 2 ? 4 * h + s : 2 * s + h) ^ aswz);
