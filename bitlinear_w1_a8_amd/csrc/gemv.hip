@@ -304,14 +304,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qg = lane >> 4, r = lane & 15;
   const int K16 = K >> 4;
-  const int nchunks = K >> 8;                       // 16 words (256 k) per chunk
+  // 16 words (256 k) per chunk; a row whose K is not a multiple of 256 ends
+  // in a chunk of tailq valid 64-k quads (K % 64 == 0, host): the lanes of the
+  // missing quads load the last valid quad again and meet zero activations
+  const int nchunks = (K + 255) >> 8;
+  const int tailq = (K >> 6) & 3;                   // 0: the last chunk is whole
   const int c0 = wave * per;
   const int cnt = min(per, nchunks - c0);           // <= 0 when K is narrower than the block
 
-  // LDS: [header][T x (K + 16) int8 activations, row-major; the 16-byte pad
-  //      per token spreads the tokens of one B-operand read over the banks]
+  // LDS: [header][T x (Kp + 16) int8 activations, row-major, Kp = K rounded
+  //      up to whole chunks and zero past K; the 16-byte pad per token
+  //      spreads the tokens of one B-operand read over the banks]
   //      [fused modes: the raw activations, T x K]
-  const int tstride = K + 16;
+  const int tstride = ((K + 255) & ~255) + 16;
   int* zero = reinterpret_cast<int*>(smem);                    // 16 ints of zeros
   int* tile = zero + 16;                                       // [token][row]
   int* counter = tile + 256 * RT;
@@ -342,15 +347,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
   // the wave's base + 16 l): int8 input, this wave's own k run; raw input
   // (step A1 fused), the whole rows, shared by the block ...
   const int run0 = c0 * 256, runb = cnt > 0 ? cnt * 256 : 0;   // this wave's k run
+  const int runv = cnt > 0 ? min(runb, K - run0) : 0;         // ... of it inside the row
   uint4 xraw[ONE && MODE != kInt8 ? CPW : 1];                  // one-token raw units
   if constexpr (MODE == kInt8) {
     const int8_t* x8 = static_cast<const int8_t*>(pr.x);
-    for (int t = 0; t < T; ++t)
-      for (int base = 0; base < runb; base += 1024)
-        if (base + 16 * lane < runb)
+    for (int t = 0; t < T; ++t) {
+      for (int base = 0; base < runv; base += 1024)
+        if (base + 16 * lane < runv)
           __builtin_amdgcn_global_load_lds(
               (dec_glb_t)(x8 + (int64_t)t * K + run0 + base + 16 * lane),
               (dec_lds_t)(xs8 + t * tstride + run0 + base), 16, 0, 0);
+      // the end of a row's last chunk past K: zeros (fewer than 256 bytes)
+      if (run0 + runv + 16 * lane < run0 + runb)
+        *reinterpret_cast<uint4*>(xs8 + t * tstride + run0 + runv + 16 * lane) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
   } else if constexpr (ONE) {
     // one token: each lane loads, into registers, the four raw activations
     // it will quantise in each chunk of this wave's run (elements 4l .. 4l+3
@@ -360,11 +371,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int k0 = min(c0 + u, nchunks - 1) * 256 + 4 * lane;
-      if constexpr (MODE == kBf16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
-        xraw[u] = make_uint4(v.x, v.y, 0u, 0u);
-      } else {
-        xraw[u] = *reinterpret_cast<const uint4*>(xr + 4 * k0);
+      xraw[u] = make_uint4(0u, 0u, 0u, 0u);         // past K (a short last chunk): zeros
+      if (k0 < K) {
+        if constexpr (MODE == kBf16) {
+          const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
+          xraw[u] = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+          xraw[u] = *reinterpret_cast<const uint4*>(xr + 4 * k0);
+        }
       }
     }
   } else {
@@ -403,8 +417,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 #pragma unroll
     for (int i = LO; i < HI; ++i) {
       const int c = min(c0 + i, nchunks - 1);
+      // a short last chunk: lanes of the missing quads reload the last valid one
+      const int qd = (tailq != 0 && c == nchunks - 1 && qg >= tailq) ? tailq - 1 - qg : 0;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) buf[rt][i] = wrow[rt][(size_t)c * 4];
+      for (int rt = 0; rt < RT; ++rt) buf[rt][i] = wrow[rt][(size_t)c * 4 + qd];
     }
   };
   // Only a quarter of the chunks (at least one) go out now, the rest after
@@ -485,8 +501,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
       const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x04000c0cu);
       const uint32_t word = lo | hi;
       tsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, tsum, false);
-      *reinterpret_cast<uint32_t*>(xs8 + k0) = word;
-      if (first && pr.xq_out) *reinterpret_cast<uint32_t*>(pr.xq_out + k0) = word;
+      *reinterpret_cast<uint32_t*>(xs8 + k0) = word;     // zeros past K
+      if (first && pr.xq_out && k0 < K) *reinterpret_cast<uint32_t*>(pr.xq_out + k0) = word;
     }
     const int sum = wave_sum_i(tsum);
     if (r == 0) qsum = sum;
@@ -1144,7 +1160,7 @@ DecShape dec_shape(int64_t tiles, int64_t kmax, int64_t t) {
   // Several tokens stage T times the activations per block, so two tiles
   // pay from fewer tiles on (measured: 2560 -> 6912 at T = 8, 432 tiles,
   // 6.1 -> 5.7 us; at T = 1 the same change costs 1.5%).
-  const int nchunks = (int)(kmax / 256);
+  const int nchunks = (int)((kmax + 255) / 256);
   const int64_t min_tiles = t > 1 ? BL_GEMV_DEC_RT2_MIN_TILES_MULTI : BL_GEMV_DEC_RT2_MIN_TILES;
   const int rt = tiles >= min_tiles && nchunks <= BL_GEMV_DEC_RT2_MAX_CHUNKS ? 2 : 1;
   const int64_t blocks = (tiles + rt - 1) / rt;
@@ -1164,9 +1180,13 @@ DecShape dec_shape(int64_t tiles, int64_t kmax, int64_t t) {
 // the size of one raw activation (step A1 fused, at most 4 tokens; one token
 // keeps its raw activations in registers, more are staged in LDS).
 bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
-  if ((k % 256) != 0 || t * k > BL_GEMV_DEC_XLDS) return false;
+  // rows of whole 64-k quads; those not a multiple of 256 (a short last
+  // chunk) with int8 input or one raw token
+  const int64_t kp = (k + 255) / 256 * 256;
+  if ((k % 64) != 0 || t * kp > BL_GEMV_DEC_XLDS) return false;
   if (raw_bytes == 0) return t <= 16;
-  return t == 1 || (t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS);
+  if (t == 1) return true;
+  return k % 256 == 0 && t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
 }
 
 // Fused launches redo the token absmax in every block: worth it while that
@@ -1179,7 +1199,7 @@ bool fuse_work_ok(int64_t t, int64_t work) {
 
 size_t dec_lds(int64_t t, int64_t kmax, int raw_bytes, int rt) {
   const size_t staged = t == 1 ? 0 : (size_t)t * kmax * raw_bytes;   // raw rows, T > 1
-  return dec_head(rt) + (size_t)t * (kmax + 16) + staged;
+  return dec_head(rt) + (size_t)t * ((kmax + 255) / 256 * 256 + 16) + staged;
 }
 
 template <int MODE, bool ONE, bool GATED, int RT>
@@ -1208,7 +1228,7 @@ hipError_t run_dec(DecGroup& grp, int count, const DecShape& sh, size_t lds,
   grp.nw = sh.nw;
   int bx = 0;   // blocks of the problem with the most rows
   for (int i = 0; i < count; ++i) {
-    grp.p[i].per = (grp.p[i].K / 256 + sh.nw - 1) / sh.nw;
+    grp.p[i].per = ((grp.p[i].K + 255) / 256 + sh.nw - 1) / sh.nw;
     if (grp.p[i].ldy == 0) grp.p[i].ldy = grp.p[i].N;
     const int b = (grp.p[i].N + 16 * sh.rt - 1) / (16 * sh.rt);
     bx = b > bx ? b : bx;

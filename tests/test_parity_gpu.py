@@ -247,7 +247,13 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               (2, 40, 131072), (70, 300, 131072),
               # up to 64 tokens over fewer than 40 tiles of 64 x 128: K split
               # into parts, the last one short (18 and 54 steps of 128)
-              (33, 200, 2304), (64, 2560, 6912), (61, 4900, 1152)]
+              (33, 200, 2304), (64, 2560, 6912), (61, 4900, 1152),
+              # decode kernel, rows not a multiple of 256 k (a short last
+              # chunk of one to three 64-k quads): the 3B-class rows (3200,
+              # 8640), one partial chunk only, T = 16, two row tiles per
+              # block (several tokens; one token over 513 tiles)
+              (1, 3200, 3200), (1, 3200, 8640), (4, 300, 64), (3, 100, 128),
+              (16, 40, 448), (9, 4100, 576), (1, 8200, 704)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
@@ -510,6 +516,12 @@ GROUPS = {
     # block in the fused kernel (ragged last block, a cut narrow problem)
     "t3_bf16_two_tiles_ragged": (3, "bf16", [(2560, 4100), (2560, 37)]),
     "t4_f32_two_tiles": (4, "f32", [(1024, 4096)]),
+    # one token, rows not a multiple of 256 k: the fused kernel on a short
+    # last chunk (the 3B-class layer shapes; mixed K in one launch)
+    "t1_bf16_3b_qkv": (1, "bf16", [(3200, 3200), (3200, 3200), (3200, 3200)]),
+    "t1_bf16_3b_gateup": (1, "bf16", [(3200, 8640), (3200, 8640)]),
+    "t1_f32_3b_down": (1, "f32", [(8640, 3200)]),
+    "t1_bf16_short_chunks_mixed": (1, "bf16", [(320, 100), (2560, 37), (64, 20), (448, 300)]),
 }
 
 
@@ -569,7 +581,10 @@ GATED_CASES = [(1, 6912, 2560, "bf16"), (3, 100, 512, "f32"), (4, 37, 256, "bf16
                # two row tiles per block with several tokens: the int8 decode
                # kernel (T = 8, 864 tiles), the fused one (T = 3, 2 * 2100
                # rows), the 64-token kernel (T = 32)
-               (8, 6912, 2560, "bf16"), (3, 2100, 1024, "f32"), (32, 2100, 512, "bf16")]
+               (8, 6912, 2560, "bf16"), (3, 2100, 1024, "f32"), (32, 2100, 512, "bf16"),
+               # rows not a multiple of 256 k: fused at one token, and int8
+               # after a separate act-quant at five
+               (1, 8640, 3200, "bf16"), (1, 100, 448, "f32"), (5, 300, 320, "bf16")]
 
 
 def _gated_inputs(bl, t, n, k, dtype, seed):
