@@ -21,8 +21,8 @@ kernel against the HBM roofline, the CPU oracle timed on a bounded sample,
 and, as extra context: the device's measured ceilings (launch floor, HBM read
 stream, int8 matrix-core loop), the spread of the step time, the prefill GEMM
 (T = 2048) in int8 TOP/s, the batched decode crossover between the decode
-kernel and the tiled MFMA kernel, and the 70B-class shapes at T = 1 (GB/s)
-and T = 256 (TOP/s).
+kernel and the tiled MFMA kernel, the 70B-class shapes at T = 1 (GB/s)
+and T = 256 (TOP/s), and the 3B-class layer (decode GB/s, prefill TOP/s).
 """
 
 import argparse
@@ -60,7 +60,7 @@ def parse():
                         "program that the prefill rocprofv3 summaries profile")
     p.add_argument("--extra", default="all",
                    help="context runs to do: 'all' or a comma list of calib, toy, prefill, "
-                        "crossover, 70b, subln, gated, lut, binary")
+                        "crossover, 70b, 3b, subln, gated, lut, binary, pack")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     p.add_argument("--fused-only", action="store_true",
@@ -596,6 +596,107 @@ def big_extra(torch, binding, wl, dev, stream):
     return out
 
 
+# 3B-class layer: the BitNet b1.58 3B model (listed among the released models
+# on the bitnet.cpp pages) follows the LLaMA-3B layout, hidden 3200, FFN 8640,
+# keys and values as wide as the queries; the pages give no dimensions, so
+# these are a stated reading.  K = 3200 and 8640 are not multiples of 256
+# (short last decode chunks) and 8640 is not one of 128 (the register-staged
+# MFMA kernel at T = 2048).
+THREE_B = [("q", 3200, 3200), ("k", 3200, 3200), ("v", 3200, 3200), ("o", 3200, 3200),
+           ("gate", 3200, 8640), ("up", 3200, 8640), ("down", 8640, 3200)]
+
+
+def three_b_extra(torch, binding, dev, stream):
+    """Context: the 3B-class layer.  Decode, T = 1: the seven projections as
+    the headline's four fused launches [q, k, v], [o], [gate, up], [down],
+    layer sets rotated over > 1 GB, GB/s of the step.  Prefill, T = 2048:
+    act-quant + tiled MFMA kernel on 3200 -> 8640 and 8640 -> 3200, TOP/s.
+    Weights N(0, 0.02) and bf16 activations N(0, 1), drawn on the GPU
+    (seeded) and packed there."""
+    lib = binding.load()
+    calls = Calls(lib)
+    mats = []
+    for mi, (name, k, n) in enumerate(THREE_B):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7000 + mi)
+        w = torch.randn((n, k), device=dev, generator=gen) * 0.02
+        packed, gamma = binding.pack_weights(w)
+        del w
+        x = torch.randn((1, k), device=dev, generator=gen).to(torch.bfloat16)
+        mats.append(dict(name=name, k=k, n=n, packed=packed, gamma=gamma, x=x,
+                         xq=torch.empty((1, k), dtype=torch.int8, device=dev),
+                         absmax=torch.empty(1, dtype=torch.float32, device=dev),
+                         y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    layer_bytes = sum(d["packed"].numel() for d in mats)
+    n_sets = int(np.ceil(ROT_BYTES / layer_bytes))
+    sets = [[d["packed"] for d in mats]] + [[d["packed"].clone() for d in mats]
+                                            for _ in range(n_sets - 1)]
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    descs = []
+    for sp in sets:
+        per = []
+        for grp in groups:
+            arr = (binding.BlLinear * len(grp))()
+            for gi, mi in enumerate(grp):
+                d = mats[mi]
+                arr[gi] = binding.BlLinear(d["x"].data_ptr(), sp[mi].data_ptr(), d["gamma"].data_ptr(),
+                                           d["n"], d["k"], d["y"].data_ptr(), d["xq"].data_ptr(),
+                                           d["absmax"].data_ptr(), None)
+            per.append(arr)
+        descs.append(per)
+
+    def steps(s):
+        h = ctypes.c_void_p(s.cuda_stream)
+        for per in descs:
+            for arr in per:
+                calls.grouped(arr, 1, h)
+
+    g = capture(torch, steps, stream)
+    reps = 16
+    ms = time_graph(torch, g, reps, 2, stream)
+    us_step = ms * 1e3 / (reps * n_sets)
+    step_bytes = sum(fused_bytes(1, d["n"], d["k"]) for d in mats)
+    out = {"decode_t1_layer": {"us_per_step": round(us_step, 2),
+                               "gb_s": round(step_bytes / us_step / 1e3, 1),
+                               "frac_of_hbm_peak": round(step_bytes / us_step / 1e3 / HBM_PEAK_GBS, 4),
+                               "step_bytes": int(step_bytes), "layer_sets_rotated": n_sets}}
+    del descs, sets, g
+    torch.cuda.empty_cache()
+    t = 2048
+    for mi in (4, 6):
+        d = mats[mi]
+        k, n = d["k"], d["n"]
+        copies = [d["packed"]] + [d["packed"].clone() for _ in range(int(np.ceil(ROT_BYTES / d["packed"].numel())) - 1)]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7100 + mi)
+        x = torch.randn((t, k), device=dev, generator=gen).to(torch.bfloat16)
+        xq = torch.empty((t, k), dtype=torch.int8, device=dev)
+        am = torch.empty(t, dtype=torch.float32, device=dev)
+        y = torch.empty((t, n), dtype=torch.float32, device=dev)
+        P = [ptr(c) for c in copies]
+        calls.quant(ptr(x), ptr(xq), ptr(am), t, k, ctypes.c_void_p(stream.cuda_stream))
+        us1 = rotated_time_us(
+            torch, lambda s, i: calls.forward(P[i], ptr(d["gamma"]), ptr(xq), ptr(am), t, n, k, ptr(y),
+                                              0, ctypes.c_void_p(s.cuda_stream)),
+            len(copies), stream, reps=4)
+
+        def both(s, i):
+            h = ctypes.c_void_p(s.cuda_stream)
+            calls.quant(ptr(x), ptr(xq), ptr(am), t, k, h)
+            calls.forward(P[i], ptr(d["gamma"]), ptr(xq), ptr(am), t, n, k, ptr(y), 0, h)
+
+        us2 = rotated_time_us(torch, both, len(copies), stream, reps=4)
+        ops = 2.0 * t * n * k
+        out[f"prefill_t2048_{k}->{n}"] = {
+            "gemm_us": round(us1, 2), "gemm_tops": round(ops / us1 / 1e6, 1),
+            "gemm_frac_of_int8_peak": round(ops / us1 / 1e6 / INT8_PEAK_TOPS, 4),
+            "quant_plus_gemm_us": round(us2, 2), "quant_plus_gemm_tops": round(ops / us2 / 1e6, 1),
+            "rotated_copies": len(copies)}
+        del copies
+        torch.cuda.empty_cache()
+    return out
+
+
 def crossover_extra(torch, mats, sets, dev, stream, calls):
     """Batched decode: the decode kernel against the tiled MFMA kernel on
     2560->6912 and 6912->2560 for T in {1, 8, 32, 64, 128, 256} (int8 input,
@@ -1017,7 +1118,8 @@ def main():
                   "rotated_packed_bytes": int(sum(p.numel() for p in sets[0]) * n_sets),
                   "pack_ms_per_matrix": [round(v, 3) for v in pack_ms]})
     want = set(args.extra.split(",")) if args.extra != "all" else {
-        "calib", "toy", "prefill", "crossover", "70b", "subln", "gated", "lut", "binary", "pack"}
+        "calib", "toy", "prefill", "crossover", "70b", "3b", "subln", "gated", "lut", "binary",
+        "pack"}
     if not args.no_extra:
         if "calib" in want:
             extra["device_ceilings"] = calibration(torch, binding, dev, stream)
@@ -1031,6 +1133,8 @@ def main():
             extra["batched_decode_crossover"] = crossover_extra(torch, mats, sets, dev, stream, calls)
         if "70b" in want:
             extra["70b_class"] = big_extra(torch, binding, wl, dev, stream)
+        if "3b" in want:
+            extra["3b_class"] = three_b_extra(torch, binding, dev, stream)
         if "subln" in want:
             extra["subln_act_quant"] = subln_extra(torch, binding, dev, stream)
         if "pack" in want:

@@ -766,13 +766,19 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
   const int64_t wide = m128 * ((n + 511) / 512), narrow = m128 * ((n + 255) / 256);
   const int64_t w256 = m64 * ((n + 255) / 256), w128 = m64 * ((n + 127) / 128);
   const bool rows_used = 10 * t >= 9 * 128 * m128;   // 128-row tiles at least 90% full
-  if (wide >= BL_GEMM_WIDE_MIN_TILES) return Tiles::kWide;
-  if (narrow >= BL_GEMM_NARROW_MIN_TILES && rows_used) return Tiles::kNarrow;
-  if (w256 >= BL_GEMM_M64_MIN_TILES || !allow_w128) {
+  const int64_t cus = device_cus();
+  // 128-row tiles that would leave a second round less than a quarter full
+  // take 64 x 256 tiles, several blocks of which share a CU in one round
+  // (T = 2048, 3200 -> 8640: 272 tiles of 128 x 512, 83.5 us; 544 of
+  // 128 x 256, 92.6 us; 1088 of 64 x 256, 71.1 us)
+  const bool wide_spills = wide > cus && 4 * wide < 5 * cus;
+  if (wide >= BL_GEMM_WIDE_MIN_TILES && !wide_spills) return Tiles::kWide;
+  if (narrow >= BL_GEMM_NARROW_MIN_TILES && rows_used && !wide_spills) return Tiles::kNarrow;
+  if (w256 >= BL_GEMM_M64_MIN_TILES || !allow_w128 || wide_spills) {
     // 64 x 256 tiles that would spill into a second round, where 64 x 320
     // tiles fill the CUs once (2048 x 6912 -> 2560: 320 against 256 tiles,
     // 48.5 -> 43.9 us; 128 x 160 tiles measured 46.0 us)
-    const int64_t cus = device_cus(), w320 = m64 * ((n + 319) / 320);
+    const int64_t w320 = m64 * ((n + 319) / 320);
     if (allow_w320 && w256 > cus && 8 * w320 >= 7 * cus && w320 <= cus) return Tiles::kM64W320;
     return Tiles::kM64W256;
   }

@@ -281,6 +281,9 @@ def test_forward_shapes(bl, t, n, k, algo):
 # tiles in both directions), K steps 1, 4 and 5 (a whole three-stage cycle,
 # one and two steps past it)
 WIDE_SHAPES = [(2085, 6976, 512), (2048, 6500, 640), (2304, 6400, 128),
+               # 272 tiles of 128 x 512 (a second round under a quarter full):
+               # 64 x 256 tiles instead
+               (2048, 8300, 384),
                # 64 x 320 tiles (256 of them, the last ones ragged in T and N)
                (2000, 2500, 1024)]
 
