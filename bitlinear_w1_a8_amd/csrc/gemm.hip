@@ -248,6 +248,9 @@ __device__ __forceinline__ int exact_sum(int acc, int qsum) {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
+// 64 lanes x 16 bytes of zeros: the activation source of K-step slots past K
+__device__ __align__(16) int8_t kZeroPage[1024];
+
 // Each stage is its own static LDS object and every step below names its
 // stages at compile time, so the compiler can tell that the loads landing in
 // one stage do not alias reads of another and does not drain every
@@ -264,8 +267,11 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // and writes the bfloat16 gated ReLU^2 of output i to h (y is not used).
 // RS: each token's sum of q comes from rowsum[] (subtracted by the first K
 // part only) instead of being summed from the activation tiles in the loop.
+// TAIL: K % 128 == 64, so the last K step holds 64 k: its activation slots
+// past K are read from a page of zeros and its weight loads past the row end
+// reload the step's first half (multiplied by those zeros).
 template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED,
-          int WBITS = 2, bool RS = false>
+          int WBITS = 2, bool RS = false, bool TAIL = false>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
                                                          const float* __restrict__ gamma,
                                                          const int8_t* __restrict__ xq,
@@ -280,6 +286,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
   static_assert(!(RS && (GATED || WBITS != 2)), "rowsum: plain two-bit kernels only");
   static_assert(!(SPLIT && GATED), "the gated epilogue needs whole sums");
+  static_assert(!(TAIL && (SPLIT || GATED || WBITS != 2)), "a half last K step: plain two-bit kernels");
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 
   // 32-bit offsets from the uniform bases (the host keeps T*K and N*K/16
   // below 2^31), so each load is a scalar base plus one VGPR offset
-  uint32_t aoff[kAChunks];
+  uint32_t aoff[kAChunks], aslot[kAChunks];
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int c = min(wave * kAChunks + i, kATot - 1);
@@ -384,6 +391,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     int tok = m0 + r;
     tok = tok < T ? tok : T - 1;
     aoff[i] = (uint32_t)tok * (uint32_t)K + 16u * slot;
+    aslot[i] = 16u * slot;
   }
   uint32_t boff[kBChunks];
 #pragma unroll
@@ -411,24 +419,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
     }
   }
   uint4 breg[kBReg ? STAGES : 1][kBReg ? WNF : 1];
+  const uint32_t h_of_lane = (uint32_t)lane >> 5;
   auto issue = [&](int kt, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
     unsigned char* As = abuf(stage_c);
     const uint32_t k0 = kbase + (uint32_t)kt * BK;
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(xq + (aoff[i] + k0)),
+    for (int i = 0; i < kAChunks; ++i) {
+      const int8_t* src = xq + (aoff[i] + k0);
+      if constexpr (TAIL) src = k0 + aslot[i] < (uint32_t)K ? src : kZeroPage + 16 * lane;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)src,
                                        (lds_ptr_t)(As + min(wave * kAChunks + i, kATot - 1) * 1024),
                                        16, 0, 0);
+    }
     if constexpr (kBReg) {
+      // the step's second half (h = 1) past the row end: the first half again
+      const uint32_t back = TAIL && k0 + 64u * h_of_lane >= (uint32_t)K ? 4u : 0u;
 #pragma unroll
       for (int j = 0; j < WNF; ++j)
-        breg[S][j] = *reinterpret_cast<const uint4*>(packed + (roff[j] + (k0 >> 4)));
+        breg[S][j] = *reinterpret_cast<const uint4*>(packed + (roff[j] + (k0 >> 4) - back));
     } else {
       unsigned char* Bs = bbuf(stage_c);
+      const uint32_t back = TAIL && k0 + 64u * (lane & 1) >= (uint32_t)K ? 4u : 0u;
 #pragma unroll
       for (int i = 0; i < kBChunks; ++i)
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)))),
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(packed + (boff[i] + (k0 >> (WBITS == 2 ? 4 : 5)) - back)),
                                          (lds_ptr_t)(Bs + min(wave * kBChunks + i, kBTot - 1) * 1024),
                                          16, 0, 0);
     }
@@ -446,7 +461,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) qpart[i] = 0;
 
-  const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : K / BK;   // >= 1 (host)
+  const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : (K + BK - 1) / BK;   // >= 1 (host)
   constexpr int kLoads = kAChunks + (kBReg ? WNF : kBChunks);   // this wave's loads per tile
   static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
@@ -672,6 +687,9 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>;
     else if constexpr (GATED)
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, true>;
+    else if (k % BK != 0)   // K % 128 == 64 (host): a half last step, never split
+      return rowsum ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true, true>
+                    : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, false, true>;
     else if (rowsum)
       return splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false, 2, true>
                         : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true>;
@@ -801,15 +819,16 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
                        int64_t k, float* y, int32_t* acc, hipStream_t stream) {
-  const bool lds_ok = k % BK == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
+  // K % 128 == 64 takes the same kernels with a half last step (no K split)
+  const bool lds_ok = k % 64 == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
   if (!lds_ok) {
-    // K % 128 != 0 (or offsets beyond 32 bits): the register-staged kernel
+    // K % 64 != 0 (or offsets beyond 32 bits): the register-staged kernel
     const int64_t big = ((n + 127) / 128) * ((t + 255) / 256);
     if (big >= BL_GEMM_BIG_MIN_TILES)
       return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
     return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   }
-  const Tiles choice = choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true, true);
+  const Tiles choice = choose_tiles(t, n, k, t * n < (int64_t(1) << 31) && k % BK == 0, true, true);
   switch (choice) {
     case Tiles::kWide:
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,

@@ -285,7 +285,12 @@ WIDE_SHAPES = [(2085, 6976, 512), (2048, 6500, 640), (2304, 6400, 128),
                # 64 x 256 tiles instead
                (2048, 8300, 384),
                # 64 x 320 tiles (256 of them, the last ones ragged in T and N)
-               (2000, 2500, 1024)]
+               (2000, 2500, 1024),
+               # K % 128 == 64, a half last K step on every tile shape: the
+               # 3B-class down projection (64 x 256), 128 x 512 (ragged),
+               # 128 x 256, 64 x 320, 64 x 128 (four stages)
+               (2048, 3200, 8640), (2085, 6976, 704), (2048, 3500, 320), (2000, 2500, 1088),
+               (256, 3000, 8640)]
 
 
 @pytest.mark.parametrize("algo", ["gemm", "auto"])
