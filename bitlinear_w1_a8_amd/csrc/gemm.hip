@@ -269,7 +269,8 @@ __device__ __align__(16) int8_t kZeroPage[1024];
 // part only) instead of being summed from the activation tiles in the loop.
 // TAIL: K % 128 == 64, so the last K step holds 64 k: its activation slots
 // past K are read from a page of zeros and its weight loads past the row end
-// reload the step's first half (multiplied by those zeros).
+// reload the step's first half (multiplied by those zeros).  With K in parts
+// the half step falls in the last part.
 template <int WAVES, int WAVES_M, int WMF, int WNF, int STAGES, bool SPLIT, bool GATED,
           int WBITS = 2, bool RS = false, bool TAIL = false>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restrict__ packed,
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four stages");
   static_assert(!(RS && (GATED || WBITS != 2)), "rowsum: plain two-bit kernels only");
   static_assert(!(SPLIT && GATED), "the gated epilogue needs whole sums");
-  static_assert(!(TAIL && (SPLIT || GATED || WBITS != 2)), "a half last K step: plain two-bit kernels");
+  static_assert(!(TAIL && (GATED || WBITS != 2)), "a half last K step: plain two-bit kernels");
   constexpr int NT = WAVES * 64;
   constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int BM = WAVES_M * 32 * WMF, BN = WAVES_N * 32 * WNF;
@@ -461,7 +462,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_lds(const uint32_t* __restr
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) qpart[i] = 0;
 
-  const int nk = SPLIT ? min(ksteps, K / BK - part * ksteps) : (K + BK - 1) / BK;   // >= 1 (host)
+  const int nkall = (K + BK - 1) / BK;             // K steps, a half last one included
+  const int nk = SPLIT ? min(ksteps, nkall - part * ksteps) : nkall;   // >= 1 (host)
   constexpr int kLoads = kAChunks + (kBReg ? WNF : kBChunks);   // this wave's loads per tile
   static_assert(kLoads * (STAGES - 2) < 64, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0);                  // the scale loads
@@ -687,9 +689,11 @@ hipError_t run_lds(const uint8_t* packed, const float* gamma, const int8_t* xq,
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 1>;
     else if constexpr (GATED)
       return k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, true>;
-    else if (k % BK != 0)   // K % 128 == 64 (host): a half last step, never split
-      return rowsum ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true, true>
-                    : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, false, true>;
+    else if (k % BK != 0)   // K % 128 == 64 (host): a half last step
+      return rowsum ? (splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false, 2, true, true>
+                                  : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true, true>)
+                    : (splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false, 2, false, true>
+                                  : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, false, true>);
     else if (rowsum)
       return splits > 1 ? k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, true, false, 2, true>
                         : k_gemm_lds<WAVES, WAVES_M, WMF, WNF, STAGES, false, false, 2, true>;
@@ -819,7 +823,7 @@ Tiles choose_tiles(int64_t t, int64_t n, int64_t k, bool allow_split, bool allow
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq,
                        const float* absmax, const int32_t* rowsum, int64_t t, int64_t n,
                        int64_t k, float* y, int32_t* acc, hipStream_t stream) {
-  // K % 128 == 64 takes the same kernels with a half last step (no K split)
+  // K % 128 == 64 takes the same kernels with a half last step
   const bool lds_ok = k % 64 == 0 && t * k < (int64_t(1) << 31) && n * (k / 16) < (int64_t(1) << 31);
   if (!lds_ok) {
     // K % 64 != 0 (or offsets beyond 32 bits): the register-staged kernel
@@ -828,7 +832,7 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run<4, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
     return run<2, 2>(packed, gamma, xq, absmax, t, n, k, y, acc, stream);
   }
-  const Tiles choice = choose_tiles(t, n, k, t * n < (int64_t(1) << 31) && k % BK == 0, true, true);
+  const Tiles choice = choose_tiles(t, n, k, t * n < (int64_t(1) << 31), true, true);
   switch (choice) {
     case Tiles::kWide:
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
@@ -851,7 +855,7 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       // cleared, takes the exact int32 partial sums by atomics and is
       // rescaled in place
       const bool t64 = choice == Tiles::kSplit64;
-      const int64_t nkt = k / BK;
+      const int64_t nkt = (k + BK - 1) / BK;        // a half last step (K % 128 == 64) included
       const int64_t tl = t64 ? ((t + 63) / 64) * ((n + 127) / 128)
                              : ((t + 127) / 128) * ((n + 511) / 512);
       int64_t parts = (BL_GEMM_SPLIT_ITEMS + tl - 1) / tl;

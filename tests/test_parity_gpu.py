@@ -253,7 +253,11 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # 8640), one partial chunk only, T = 16, two row tiles per
               # block (several tokens; one token over 513 tiles)
               (1, 3200, 3200), (1, 3200, 8640), (4, 300, 64), (3, 100, 128),
-              (16, 40, 448), (9, 4100, 576), (1, 8200, 704)]
+              (16, 40, 448), (9, 4100, 576), (1, 8200, 704),
+              # K % 128 == 64 with K in parts (the half step in the last
+              # part): 64 x 128 tiles at up to 64 tokens and over few tiles
+              # of long rows
+              (33, 200, 2368), (64, 2560, 8640), (128, 3200, 8640), (200, 1500, 16448)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
