@@ -14,8 +14,9 @@ namespace bl {
 constexpr float kEps = 1e-5f;
 constexpr float kQb = 127.0f;
 
-// Largest T that the automatic choice sends to the decode kernel (auto_algo).
-constexpr int64_t kGemvMaxTokens = 32;
+// Largest T that the automatic choice sends to the decode kernel (auto_algo:
+// 64 for matrices of up to 2 MB packed, 32 up to 16 MB, 6 beyond).
+constexpr int64_t kGemvMaxTokens = 64;
 
 // Compute units of the current device (looked up once per device).
 int device_cus();

@@ -1475,14 +1475,24 @@ hipError_t gemv_any(const uint8_t* packed, const float* gamma, const int8_t* xq,
 }  // namespace
 
 int auto_algo(int64_t t, int64_t n, int64_t k) {
-  // Measured against the tiled MFMA kernel with its own tile choice: the
-  // decode kernels win through T = 32 on the 2B shapes (2560 -> 6912 at
-  // T = 32: 8.5 against 12.6 us; 6912 -> 2560: 11.4 against 11.9, the tiled
-  // kernel splitting K there); from T = 64 on the tiled kernel wins on both
-  // (12.4 against 12.6 us; 14.1 against 17.6).
-  (void)n;
-  (void)k;
-  return t <= kGemvMaxTokens ? BL_ALGO_GEMV : BL_ALGO_GEMM;
+  // The token count up to which the decode kernels beat the tiled MFMA
+  // kernel (with its own tile choice and K split) depends on the matrix,
+  // measured with weights rotated cold (decode / tiled, us):
+  //  - up to 2 MB of packed weights, T = 64: 2560 -> 2560 9.1 / 11.3,
+  //    2560 -> 640 9.0 / 10.5; at T = 96 the tiled kernel wins (14.9 / 11.9);
+  //  - up to 16 MB, T = 32: 2560 -> 6912 8.6 / 11.9, 6912 -> 2560 11.6 / 12.1,
+  //    3200 -> 8640 13.5 / 13.7, 8640 -> 3200 11.3 / 13.7; at T = 48 or 64
+  //    the tiled kernel wins or ties (12.7 / 12.3, 14.7 / 13.2, 21.7 / 13.9,
+  //    14.9 / 14.8);
+  //  - larger (the 70B-class 58.7 MB), T = 6: 8192 -> 28672 23.3 / 25.5,
+  //    28672 -> 8192 25.4 / 28.2; at T = 8 26.3 / 25.5 and 27.6 / 28.2, at
+  //    T = 12 the tiled kernel wins on both (33.5 / 26.0, 34.1 / 29.2): past
+  //    the decode kernel's LDS staging the 64-token kernel streams a large
+  //    matrix slowly.
+  const int64_t wbytes = n * (k / 4);
+  const int64_t tmax = wbytes <= (int64_t(2) << 20) ? kGemvMaxTokens
+                       : wbytes <= (int64_t(16) << 20) ? 32 : 6;
+  return t <= tmax ? BL_ALGO_GEMV : BL_ALGO_GEMM;
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq,

@@ -89,8 +89,9 @@ typedef enum {
 typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 
 typedef enum {
-  BL_ALGO_AUTO = 0, /* decode kernel for T <= bitlinear_gemv_max_tokens() (32), else GEMM
-                       (measured crossovers) */
+  BL_ALGO_AUTO = 0, /* decode kernel for T up to a limit set by the matrix's packed size
+                       (64 up to 2 MB, 32 up to 16 MB, 6 beyond: measured crossovers),
+                       else GEMM */
   BL_ALGO_GEMV = 1, /* streaming decode kernel, any T (tokens taken 64 at a time) */
   BL_ALGO_GEMM = 2, /* LDS-tiled int8 MFMA kernel, any T */
   BL_ALGO_LUT = 3   /* table-lookup decode kernel in the style of bitnet.cpp's TL1/TL2
@@ -108,7 +109,9 @@ int bitlinear_abi_version(void);
  * The pointer stays valid until the next call on the same thread. */
 const char* bitlinear_last_error(void);
 
-/* Largest T that BL_ALGO_AUTO sends to the decode (GEMV) kernel. */
+/* Largest T that BL_ALGO_AUTO sends to the decode (GEMV) kernel for any
+ * matrix (64); larger matrices switch to the tiled kernel earlier (see
+ * BL_ALGO_AUTO). */
 int64_t bitlinear_gemv_max_tokens(void);
 
 /* Bytes of device workspace that bitlinear_pack_weights needs for an N x K

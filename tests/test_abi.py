@@ -49,7 +49,7 @@ def test_binding_covers_header():
 
 def test_constants(lib):
     assert lib.bitlinear_abi_version() == 3
-    assert lib.bitlinear_gemv_max_tokens() == 32
+    assert lib.bitlinear_gemv_max_tokens() == 64
     assert lib.bitlinear_pack_workspace_bytes(2560, 2560) == 2048
     assert lib.bitlinear_pack_workspace_bytes(28672, 8192) == 2048
 
