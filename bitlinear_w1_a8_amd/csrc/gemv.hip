@@ -1132,6 +1132,13 @@ namespace {
 #ifndef BL_GEMV_DEC_XLDS
 #define BL_GEMV_DEC_XLDS 32768    // largest T*K of int8 activations staged in LDS
 #endif
+#ifndef BL_GEMV_DEC_XLDS_FEW
+// ... and at up to four int8 tokens, whose long rows would otherwise take
+// the 64-token kernel (28672 -> 8192 at T = 2 / 4: 22.0 / 23.9 -> 14.8 /
+// 17.7 us; from T = 8 on the larger staging measured slower or equal, e.g.
+// 8192 -> 28672 at T = 12 33.3 against 47.7 us, one block per CU)
+#define BL_GEMV_DEC_XLDS_FEW 131072
+#endif
 #ifndef BL_GEMV_DEC_RAWLDS
 #define BL_GEMV_DEC_RAWLDS 32768  // largest raw activation bytes (fused act-quant) in LDS
 #endif
@@ -1191,8 +1198,11 @@ bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
   // rows of whole 64-k quads; those not a multiple of 256 (a short last
   // chunk) with int8 input or one raw token
   const int64_t kp = (k + 255) / 256 * 256;
-  if ((k % 64) != 0 || t * kp > BL_GEMV_DEC_XLDS) return false;
-  if (raw_bytes == 0) return t <= 16;
+  // at most 128 chunks: 16 waves of at most 8
+  if ((k % 64) != 0 || kp > 32768) return false;
+  if (raw_bytes == 0)
+    return t <= 16 && (t * kp <= BL_GEMV_DEC_XLDS || (t <= 4 && t * kp <= BL_GEMV_DEC_XLDS_FEW));
+  if (t * kp > BL_GEMV_DEC_XLDS) return false;
   if (t == 1) return true;
   return k % 256 == 0 && t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
 }

@@ -257,7 +257,10 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # K % 128 == 64 with K in parts (the half step in the last
               # part): 64 x 128 tiles at up to 64 tokens and over few tiles
               # of long rows
-              (33, 200, 2368), (64, 2560, 8640), (128, 3200, 8640), (200, 1500, 16448)]
+              (33, 200, 2368), (64, 2560, 8640), (128, 3200, 8640), (200, 1500, 16448),
+              # up to four int8 tokens over long rows: the decode kernel
+              # stages up to 128 KiB of activations (a short last chunk too)
+              (2, 300, 28672), (4, 1000, 28672), (3, 64, 24640)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
