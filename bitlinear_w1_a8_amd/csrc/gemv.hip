@@ -284,12 +284,11 @@ __device__ __forceinline__ float raw_elem(const uint4& v, int e) {
   }
 }
 
-// TAIL: some problem's K is not a multiple of 256 (int8 input or one raw
-// token only); the index clamps and zeros it needs stay out of the other
-// launches (measured: 1.2% on the 2B layer)
+// TAIL: some problem's K is not a multiple of 256; the index clamps and
+// zeros it needs stay out of the other launches (measured: 1.2% on the 2B
+// layer)
 template <int CPW, int MODE, bool ONE, bool GATED, int RT, bool TAIL>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu(CPW, MODE, RT)))) void k_gemv_dec(const DecGroup grp) {
-  static_assert(!TAIL || MODE == kInt8 || ONE, "short last chunks: int8 input or one raw token");
   constexpr int kRows = 16 * RT;                    // weight rows of a block (RT tiles of 16)
   extern __shared__ __align__(16) unsigned char smem[];
   const DecProblem pr = grp.p[blockIdx.y];
@@ -570,16 +569,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
     for (int i = lane; i < T * ru; i += 64) {
       const int t = ONE ? 0 : (i >= ru) + (i >= 2 * ru) + (i >= 3 * ru);
       const int k0 = run0 + (i - t * ru) * 4;       // first k of the unit
+      // a short last chunk: units past K read the row's last four values
+      // and quantise zeros instead
+      const int kl = TAIL ? min(k0, K - 4) : k0;
       float f[4];
       if constexpr (MODE == kBf16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(raw + 2 * ((int64_t)t * K + k0));
+        const uint2 v = *reinterpret_cast<const uint2*>(raw + 2 * ((int64_t)t * K + kl));
         f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
         f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
       } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(raw + 4 * ((int64_t)t * K + k0));
+        const uint4 v = *reinterpret_cast<const uint4*>(raw + 4 * ((int64_t)t * K + kl));
         f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
       }
+      if (TAIL && k0 != kl) f[0] = f[1] = f[2] = f[3] = 0.0f;
       float s = sc[0];
       if constexpr (!ONE) {
 #pragma unroll
@@ -603,7 +606,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
           if (t == tt) tsum[tt] += part;
       }
       *reinterpret_cast<uint32_t*>(xs8 + t * tstride + k0) = word;
-      if (first && pr.xq_out) *reinterpret_cast<uint32_t*>(pr.xq_out + (int64_t)t * K + k0) = word;
+      if (first && pr.xq_out && (!TAIL || k0 < K))
+        *reinterpret_cast<uint32_t*>(pr.xq_out + (int64_t)t * K + k0) = word;
     }
 #pragma unroll
     for (int tt = 0; tt < (ONE ? 1 : 4); ++tt) {
@@ -1195,16 +1199,15 @@ DecShape dec_shape(int64_t tiles, int64_t kmax, int64_t t) {
 // the size of one raw activation (step A1 fused, at most 4 tokens; one token
 // keeps its raw activations in registers, more are staged in LDS).
 bool dec_shape_ok(int64_t t, int64_t k, int raw_bytes) {
-  // rows of whole 64-k quads; those not a multiple of 256 (a short last
-  // chunk) with int8 input or one raw token
+  // rows of whole 64-k quads (those not a multiple of 256 end in a short
+  // chunk)
   const int64_t kp = (k + 255) / 256 * 256;
   // at most 128 chunks: 16 waves of at most 8
   if ((k % 64) != 0 || kp > 32768) return false;
   if (raw_bytes == 0)
     return t <= 16 && (t * kp <= BL_GEMV_DEC_XLDS || (t <= 4 && t * kp <= BL_GEMV_DEC_XLDS_FEW));
   if (t * kp > BL_GEMV_DEC_XLDS) return false;
-  if (t == 1) return true;
-  return k % 256 == 0 && t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS;
+  return t == 1 || (t <= 4 && t * k * raw_bytes <= BL_GEMV_DEC_RAWLDS);
 }
 
 // Fused launches redo the token absmax in every block: worth it while that
@@ -1236,9 +1239,7 @@ void launch_dec_rt(const DecGroup& grp, int count, dim3 grid, const DecShape& sh
                    hipStream_t stream) {
   bool tail = false;
   for (int i = 0; i < count; ++i) tail = tail || (grp.p[i].K % 256) != 0;
-  if constexpr (MODE == kInt8 || ONE) {
-    if (tail) return launch_dec_cpw<MODE, ONE, GATED, RT, true>(grp, grid, sh, lds, stream);
-  }
+  if (tail) return launch_dec_cpw<MODE, ONE, GATED, RT, true>(grp, grid, sh, lds, stream);
   launch_dec_cpw<MODE, ONE, GATED, RT, false>(grp, grid, sh, lds, stream);
 }
 

@@ -248,9 +248,9 @@ typedef struct bl_linear {
  * by bitlinear_forward on each problem (same operations, same rounding), for
  * callers that run several projections of one layer back to back (e.g. the
  * query/key/value or gate/up projections of a decoder layer).  For decode
- * shapes (one token with K % 64 == 0, or T <= 4 with K % 256 == 0; T times K
- * rounded up to a multiple of 256 at most 32768, raw activation rows of at
- * most 32 KiB when T > 1, and a modest total of weight rows times K) one kernel
+ * shapes (T <= 4, K % 64 == 0, T times K rounded up to a multiple of 256 at
+ * most 32768, raw activation rows of at most 32 KiB when T > 1, and a modest
+ * total of weight rows times K) one kernel
  * does all of it: each block quantises the activations it needs (one token:
  * from registers; more: from rows staged in LDS), then streams its weight
  * rows; otherwise the steps run per problem (act-quant, then the kernel that
@@ -322,10 +322,9 @@ bl_status bitlinear_interleave_rows(const uint8_t* a, const uint8_t* b, int64_t 
  *   h[t,n] = bf16_round_nearest_even((max(g, 0) * max(g, 0)) * u)
  *       (two binary32 products in that order).
  * The activations are quantised once (step A1) and shared by both
- * projections; for decode shapes (one token with K % 64 == 0, or T <= 4 with
- * K % 256 == 0; T times K rounded up to a multiple of 256 at most 32768, raw
- * rows of at most 32 KiB when T > 1, and a modest total of weight rows times
- * K) one kernel does everything, otherwise act-quant runs first and the
+ * projections; for decode shapes (T <= 4, K % 64 == 0, T times K rounded up
+ * to a multiple of 256 at most 32768, raw rows of at most 32 KiB when T > 1,
+ * and a modest total of weight rows times K) one kernel does everything, otherwise act-quant runs first and the
  * contraction kernel (chosen by T) writes h in its epilogue.  The gate/up
  * outputs are never stored in binary32.
  *

@@ -537,6 +537,11 @@ GROUPS = {
     "t1_bf16_3b_gateup": (1, "bf16", [(3200, 8640), (3200, 8640)]),
     "t1_f32_3b_down": (1, "f32", [(8640, 3200)]),
     "t1_bf16_short_chunks_mixed": (1, "bf16", [(320, 100), (2560, 37), (64, 20), (448, 300)]),
+    # two to four tokens, rows not a multiple of 256 k: the staged raw rows
+    # quantised with zeros past K (two row tiles per block in the second)
+    "t3_bf16_3b_qkv": (3, "bf16", [(3200, 3200), (3200, 3200), (3200, 3200)]),
+    "t4_f32_short_chunks_many_tiles": (4, "f32", [(576, 4100), (320, 37)]),
+    "t2_bf16_3b_down": (2, "bf16", [(8640, 3200)]),
 }
 
 
@@ -599,7 +604,8 @@ GATED_CASES = [(1, 6912, 2560, "bf16"), (3, 100, 512, "f32"), (4, 37, 256, "bf16
                (8, 6912, 2560, "bf16"), (3, 2100, 1024, "f32"), (32, 2100, 512, "bf16"),
                # rows not a multiple of 256 k: fused at one token, and int8
                # after a separate act-quant at five
-               (1, 8640, 3200, "bf16"), (1, 100, 448, "f32"), (5, 300, 320, "bf16")]
+               (1, 8640, 3200, "bf16"), (1, 100, 448, "f32"), (5, 300, 320, "bf16"),
+               (3, 200, 576, "bf16")]
 
 
 def _gated_inputs(bl, t, n, k, dtype, seed):
