@@ -760,6 +760,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 // rows, seven chunks per wave, it measured 14.85 against 14.4 us)
 #define BL_GEMV_PERSIST_INT8_MAX_K 8192
 #endif
+#ifndef BL_GEMV_PERSIST_INT8_MAX_T
+#define BL_GEMV_PERSIST_INT8_MAX_T 4    // int8 tokens the persistent kernel takes (at most 4)
+#endif
 #ifndef BL_GEMV_PERSIST_EARLY
 #define BL_GEMV_PERSIST_EARLY 2         // weight chunks per wave issued ahead of step A1
 #endif
@@ -784,7 +787,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(dec_waves_
 // hold the four dwords {4u + j : u = 0..3} of the group's 64 k, so one
 // ds_read_b128 is one MFMA B operand.  Each wave writes and reads only its
 // own k run (no block barrier between them).
-constexpr int persist_head(int tpb) { return ((16 + 17 * tpb + 1) * 4 + 15) / 16 * 16; }
+constexpr int persist_head(int tpb, int nt) {
+  return ((16 + (16 * nt + 1) * tpb + 1) * 4 + 15) / 16 * 16;
+}
 
 // byte offset, in a chunk's 256 bytes, of dword d (k = 4d .. 4d + 3) in the
 // slice-major order
@@ -801,9 +806,13 @@ __device__ __forceinline__ void for_each_c(F&& f, std::integer_sequence<int, J..
 // HOLD_B: the B operands (the wave's int8 activations, the same for every
 // tile) may stay in registers across tiles; otherwise they are read from LDS
 // again for every tile (long K: 16 registers per chunk would not fit).
-template <int CPW, int MODE, int DEPTH, bool HOLD_B>
+// NT: int8 input only, one to four tokens; token t's row is its own
+// slice-major row in LDS, lanes (qg, r) of token column r < NT read it, and a
+// tile's partial sums hold 16 rows per token.
+template <int CPW, int MODE, int DEPTH, bool HOLD_B, int NT>
 __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int nwaves, int tpb) {
   static_assert(DEPTH >= 2 && DEPTH <= 4 && DEPTH * CPW < 64, "tiles in flight");
+  static_assert(NT == 1 || (MODE == kInt8 && NT <= 4), "several tokens: int8 input, at most four");
   extern __shared__ __align__(16) unsigned char smem[];
   __asm__ volatile("" ::"s"(pr.packed), "s"(pr.gamma), "s"(pr.x), "s"(pr.absmax), "s"(pr.y),
                    "s"(pr.acc), "s"(pr.xq_out), "s"(pr.absmax_out), "s"(pr.N), "s"(pr.K),
@@ -820,12 +829,13 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
   const int c0 = wave * per;
   const int cnt = min(per, nchunks - c0);           // >= 1: the host sizes nwaves to the chunks
 
-  // LDS: 16 zero ints | tpb x 16 partial sums | tpb counters | absmax bits | int8 row
+  // LDS: 16 zero ints | tpb x 16 NT partial sums | tpb counters | absmax bits |
+  //      NT int8 rows of K
   int* zero = reinterpret_cast<int*>(smem);
   int* slot = zero + 16;
-  int* counter = slot + 16 * tpb;
+  int* counter = slot + 16 * NT * tpb;
   int* amax = counter + tpb;
-  unsigned char* xs8 = smem + persist_head(tpb);
+  unsigned char* xs8 = smem + persist_head(tpb, NT);
 
   // the raw token first (vector memory returns in issue order): the four
   // values per chunk this lane quantises, into registers (slots past cnt
@@ -838,7 +848,11 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     for (int u = 0; u < CPW; ++u) {
       const int k0 = min(c0 + u, nchunks - 1) * 256 + 4 * lane;
       if constexpr (MODE == kInt8) {
-        xin[u] = make_uint4(*reinterpret_cast<const uint32_t*>(xr + k0), 0u, 0u, 0u);
+        // token t's four codes in component t
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) c[t] = *reinterpret_cast<const uint32_t*>(xr + (int64_t)t * K + k0);
+        xin[u] = make_uint4(c[0], c[1], c[2], c[3]);
       } else if constexpr (MODE == kBf16) {
         const uint2 v = *reinterpret_cast<const uint2*>(xr + 2 * k0);
         xin[u] = make_uint4(v.x, v.y, 0u, 0u);
@@ -848,13 +862,15 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     }
   }
   const float g = pr.gamma[0];
-  float a_in = 0.0f;   // int8 input: the token's absmax (and, given, its row sum)
+  // int8 input: the absmax of the token whose outputs this lane writes
+  // (token lane / 16), and, given, the row sum of its token column r
+  float a_in = 0.0f;
   int rs_in = 0;
   if constexpr (MODE == kInt8) {
-    a_in = pr.absmax[0];
-    if (pr.rowsum) rs_in = pr.rowsum[0];
+    a_in = pr.absmax[min(lane >> 4, NT - 1)];
+    if (pr.rowsum) rs_in = pr.rowsum[min(r, NT - 1)];
   }
-  for (int i = threadIdx.x; i < 16 + 17 * tpb + 1; i += nthreads) zero[i] = 0;
+  for (int i = threadIdx.x; i < 16 + (16 * NT + 1) * tpb + 1; i += nthreads) zero[i] = 0;
   lds_sync();   // every activation load of the block is issued ahead of every weight load
 
   // weight loads of one tile into buffer D: this lane's 16 bytes of each of
@@ -895,19 +911,27 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     // int8 input: the codes go into the wave's run of the row as they are;
     // the sum of q over the run unless the token's row sum is given
     a_t = a_in;
-    int tsum = 0;
+    int tsum[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tsum[t] = 0;
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       if (u >= cnt) break;                          // wave-uniform
-      const uint32_t word = xin[u].x;
-      tsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, tsum, false);
-      *reinterpret_cast<uint32_t*>(xs8 + run0 + u * 256 + slice_off(lane)) = word;
+      const uint32_t words[4] = {xin[u].x, xin[u].y, xin[u].z, xin[u].w};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        tsum[t] = __builtin_amdgcn_sdot4((int)words[t], 0x01010101, tsum[t], false);
+        *reinterpret_cast<uint32_t*>(xs8 + t * K + run0 + u * 256 + slice_off(lane)) = words[t];
+      }
     }
     if (pr.rowsum) {
-      if (wave == 0 && r == 0) qsum = rs_in;       // the total once, on one wave's lanes
+      if (wave == 0 && r < NT) qsum = rs_in;       // each total once, on one wave's lanes
     } else {
-      const int sum = wave_sum_i(tsum);
-      if (r == 0) qsum = sum;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int sum = wave_sum_i(tsum[t]);
+        if (r == t) qsum = sum;
+      }
     }
   } else {
     uint32_t mx = 0;
@@ -975,7 +999,9 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
   // conditional inside a step: the compiler's own waits after a branch that
   // may or may not have issued loads assume the worst and would wait for the
   // loads just issued.
-  auto step = [&](auto dc, auto wc, auto rc, int it) {
+  // (always inlined: an outlined step, seen at seven chunks per wave, keeps
+  // its weight buffers in scratch memory)
+  auto step = [&](auto dc, auto wc, auto rc, int it) __attribute__((always_inline)) {
     constexpr int D = decltype(dc)::value;
     constexpr int WAIT = decltype(wc)::value;
     constexpr bool REFILL = decltype(rc)::value;
@@ -984,10 +1010,10 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
     for_each_c([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       wait_vmem<WAIT + CPW - 1 - i>();              // chunk i of this tile landed
-      const unsigned char* xb = (r == 0 && i < cnt) ? xs8 + (run0 + i * 256 + qg * 64)
+      const unsigned char* xb = (r < NT && i < cnt) ? xs8 + (r * K + run0 + i * 256 + qg * 64)
                                                     : reinterpret_cast<const unsigned char*>(zero);
       auto xs = [&](int j) {
-        return *reinterpret_cast<const v4i*>(xb + ((r == 0 && i < cnt) ? 16 * j : 0));
+        return *reinterpret_cast<const v4i*>(xb + ((r < NT && i < cnt) ? 16 * j : 0));
       };
       const uint4 w4 = buf[D][i];
       a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
@@ -1009,24 +1035,26 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const DecProblem pr, int 
       __builtin_amdgcn_sched_barrier(0);
     }, std::make_integer_sequence<int, CPW>{});
     if constexpr (REFILL) issue(dc, it + DEPTH);   // ahead of the epilogue's LDS and store work
-    // lane (qg, 0) holds rows 4qg + v of token 0
-    if (r == 0) {
+    // lane (qg, r) holds rows 4qg + v of token r
+    if (r < NT) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        atomicAdd(&slot[16 * it + 4 * qg + v], a1[v] + (a4[v] >> 2) + (a16[v] >> 4) - qsum);
+        atomicAdd(&slot[16 * NT * it + 16 * r + 4 * qg + v],
+                  a1[v] + (a4[v] >> 2) + (a16[v] >> 4) - qsum);
     }
     int ticket = 0;
     if (lane == 0)
       ticket = __hip_atomic_fetch_add(&counter[it], 1, __ATOMIC_ACQ_REL,
                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     ticket = __builtin_amdgcn_readfirstlane(ticket);
-    if (ticket == nwaves - 1 && lane < 16) {
-      const int n = 16 * (b + it * G) + lane;
+    if (ticket == nwaves - 1 && lane < 16 * NT) {   // token lane / 16, row lane % 16
+      const int n = 16 * (b + it * G) + (lane & 15);
       if (n < N) {
-        const int sum = __hip_atomic_load(&slot[16 * it + lane], __ATOMIC_RELAXED,
+        const int sum = __hip_atomic_load(&slot[16 * NT * it + lane], __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (pr.acc) pr.acc[n] = sum;
-        pr.y[n] = (float)sum * sc;
+        const int64_t o = (int64_t)(lane >> 4) * N + n;
+        if (pr.acc) pr.acc[o] = sum;
+        pr.y[o] = (float)sum * sc;
       }
     }
   };
@@ -1310,17 +1338,18 @@ constexpr int persist_depth(int cpw) {
                                : cpw <= 2 ? 4 : cpw <= 4 ? 3 : 2;
 }
 
-template <int MODE, int CPW>
+template <int MODE, int CPW, int NT = 1>
 hipError_t launch_persist_cpw(const DecProblem& pr, int g, int nw, int tpb, size_t lds,
                               hipStream_t stream) {
-  k_gemv_persist<CPW, MODE, persist_depth(CPW), (CPW <= 2)>
+  k_gemv_persist<CPW, MODE, persist_depth(CPW), (CPW <= 2), NT>
       <<<g, nw * 64, lds, stream>>>(pr, nw, tpb);
   return hipGetLastError();
 }
 
-// One raw token, one problem (plain outputs), many tiles: the persistent kernel.
+// One raw token, or one to four int8 tokens with at most 32 chunks per row
+// (nt), one problem (plain outputs), many tiles: the persistent kernel.
 template <int MODE>
-hipError_t run_persist(DecProblem pr, hipStream_t stream) {
+hipError_t run_persist(DecProblem pr, hipStream_t stream, int nt = 1) {
   const int tiles = (pr.N + 15) / 16, nchunks = pr.K / 256;
   int per = BL_GEMV_PERSIST_CPW;
   if ((nchunks + per - 1) / per > 16) per = (nchunks + 15) / 16;
@@ -1330,7 +1359,13 @@ hipError_t run_persist(DecProblem pr, hipStream_t stream) {
   int g = device_cus() * BL_GEMV_PERSIST_BPC;
   if (g > tiles / persist_depth(cpw)) g = tiles / persist_depth(cpw);   // DEPTH tiles per block at least
   const int tpb = (tiles + g - 1) / g;
-  const size_t lds = persist_head(tpb) + (size_t)pr.K;
+  const size_t lds = persist_head(tpb, nt) + (size_t)nt * pr.K;
+  if constexpr (MODE == kInt8) {
+    if (nt > 1 && cpw != 2) return hipErrorInvalidValue;   // the host keeps K <= 8192
+    if (nt == 2) return launch_persist_cpw<MODE, 2, 2>(pr, g, nw, tpb, lds, stream);
+    if (nt == 3) return launch_persist_cpw<MODE, 2, 3>(pr, g, nw, tpb, lds, stream);
+    if (nt == 4) return launch_persist_cpw<MODE, 2, 4>(pr, g, nw, tpb, lds, stream);
+  }
   if (cpw == 2) return launch_persist_cpw<MODE, 2>(pr, g, nw, tpb, lds, stream);
   if (cpw == 4) return launch_persist_cpw<MODE, 4>(pr, g, nw, tpb, lds, stream);
   return launch_persist_cpw<MODE, 7>(pr, g, nw, tpb, lds, stream);
@@ -1348,12 +1383,13 @@ hipError_t run_dec_int8(const uint8_t* packed, const float* gamma, const int8_t*
   grp.T = t;
   grp.p[0] = DecProblem{reinterpret_cast<const uint32_t*>(packed), gamma, xq, absmax, y, acc,
                         nullptr, nullptr, gamma2, h, n, k, 0, 0, rowsum};
-  if (h == nullptr && k <= BL_GEMV_PERSIST_INT8_MAX_K && persist_ok(t, n, k)) {
-    // one token over many tiles: the persistent kernel (the int8 row staged
-    // once per block)
+  if (h == nullptr && t <= BL_GEMV_PERSIST_INT8_MAX_T && k <= BL_GEMV_PERSIST_INT8_MAX_K &&
+      persist_ok(1, n, k)) {
+    // one to four tokens over many tiles: the persistent kernel (the int8
+    // rows staged once per block)
     DecProblem pr = grp.p[0];
     pr.ldy = n;
-    return run_persist<kInt8>(pr, stream);
+    return run_persist<kInt8>(pr, stream, t);
   }
   const int blocks = (n + 15) / 16;
   const DecShape sh = dec_shape(blocks, k, t);

@@ -260,7 +260,11 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               (33, 200, 2368), (64, 2560, 8640), (128, 3200, 8640), (200, 1500, 16448),
               # up to four int8 tokens over long rows: the decode kernel
               # stages up to 128 KiB of activations (a short last chunk too)
-              (2, 300, 28672), (4, 1000, 28672), (3, 64, 24640)]
+              (2, 300, 28672), (4, 1000, 28672), (3, 64, 24640),
+              # two to four int8 tokens over 512 tiles and more: the
+              # persistent kernel with one LDS row per token (ragged last
+              # tiles, one chunk per row)
+              (2, 8200, 2304), (3, 12288, 1024), (4, 9000, 8192), (4, 30000, 256)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
