@@ -847,7 +847,11 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run_lds<4, 2, 1, 5, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W128:
-      return run_lds<4, 2, 1, 2, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+      // eight waves of 32 x 32 (two per SIMD) rather than four of 32 x 64:
+      // 70B T = 256, 28672 -> 8192 78.6 -> 75.2 us; T = 64, 2560 -> 6912
+      // 12.1 -> 10.7 us; T = 200, 8192 -> 4000 25.3 -> 23.2 us (the K split
+      // keeps four waves: equal or 4% slower with eight)
+      return run_lds<8, 2, 1, 1, 4>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                     1, 0, nullptr, nullptr, rowsum);
     case Tiles::kSplit:
     case Tiles::kSplit64: {

@@ -264,7 +264,9 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # two to four int8 tokens over 512 tiles and more: the
               # persistent kernel with one LDS row per token (ragged last
               # tiles, one chunk per row)
-              (2, 8200, 2304), (3, 12288, 1024), (4, 9000, 8192), (4, 30000, 256)]
+              (2, 8200, 2304), (3, 12288, 1024), (4, 9000, 8192), (4, 30000, 256),
+              # 64 x 128 tiles on eight waves of 32 x 32 (unsplit; ragged T and N)
+              (200, 4000, 8192), (77, 1000, 1024)]
 
 
 def _forward_inputs(t, n, k, seed, zero_rows=True):
