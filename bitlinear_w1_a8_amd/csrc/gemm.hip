@@ -838,7 +838,11 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run_lds<8, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kNarrow:
-      return run_lds<4, 1, 4, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+      // eight waves of 128 x 32 (two per SIMD) rather than four of 128 x 64:
+      // 70B T = 256, 8192 -> 28672 62.4-65.6 -> 58.9-60.2 us; T = 512,
+      // 4096 -> 14336 37.7 -> 34.3 us; T = 2048, 320 -> 3500 16.8 -> 12.5 us
+      // (two rows of four waves with the weights through LDS: 60.9 us)
+      return run_lds<8, 1, 4, 1, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W256:
       return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
