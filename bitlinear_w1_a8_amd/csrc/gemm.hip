@@ -848,8 +848,11 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
       return run_lds<4, 1, 2, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W320:
-      return run_lds<4, 2, 1, 5, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
-                                                 1, 0, nullptr, nullptr, rowsum);
+      // ten waves of 32 x 64 (2 x 5; two or three per SIMD) rather than four
+      // of 32 x 160: T = 2048, 6912 -> 2560 44.3 -> 43.2 us, 8192 -> 2560
+      // 50.0 -> 49.0 us, T = 2000, 1024 -> 2500 15.5 -> 13.1 us
+      return run_lds<10, 2, 1, 2, BL_GEMM_STAGES>(packed, gamma, xq, absmax, t, n, k, y, acc, stream,
+                                                  1, 0, nullptr, nullptr, rowsum);
     case Tiles::kM64W128:
       // eight waves of 32 x 32 (two per SIMD) rather than four of 32 x 64:
       // 70B T = 256, 28672 -> 8192 78.6 -> 75.2 us; T = 64, 2560 -> 6912
