@@ -590,6 +590,19 @@ def big_extra(torch, binding, wl, dev, stream):
                 rec["t256_forward_tops"] = round(ops / us_fwd / 1e6, 1)
                 rec["t256_forward_frac_of_int8_peak"] = round(ops / us_fwd / 1e6 / INT8_PEAK_TOPS, 4)
                 rec["t256_forward_rowsum_given_us"] = round(us_rs, 2)
+        # small batches of int8 tokens (the persistent kernel takes up to
+        # four over rows of up to 8192; longer rows stage up to 128 KiB)
+        for t in (2, 4):
+            xq = torch.randint(-127, 128, (t, m.k), dtype=torch.int8, device=dev)
+            am = torch.rand(t, device=dev) * 4 + 1
+            y = torch.empty((t, m.n), dtype=torch.float32, device=dev)
+            P = [ptr(c) for c in copies]
+            us = rotated_time_us(
+                torch, lambda s, i: calls.forward(P[i], ptr(gamma), ptr(xq), ptr(am), t, m.n, m.k,
+                                                  ptr(y), 0, ctypes.c_void_p(s.cuda_stream)),
+                len(copies), stream)
+            rec[f"t{t}_int8_forward_us"] = round(us, 2)
+            rec[f"t{t}_int8_forward_gb_s"] = round(gemv_bytes(t, m.n, m.k) / us / 1e3, 1)
         out[f"{m.k}->{m.n}"] = rec
         del copies, packed
         torch.cuda.empty_cache()
