@@ -265,6 +265,8 @@ FWD_SHAPES = [(1, 1, 16), (1, 16, 64), (2, 17, 48), (3, 5, 16), (4, 512, 256), (
               # persistent kernel with one LDS row per token (ragged last
               # tiles, one chunk per row)
               (2, 8200, 2304), (3, 12288, 1024), (4, 9000, 8192), (4, 30000, 256),
+              # ... and at the largest tile count it takes (64 tiles per block)
+              (4, 524288, 256),
               # 64 x 128 tiles on eight waves of 32 x 32 (unsplit; ragged T and N)
               (200, 4000, 8192), (77, 1000, 1024)]
 
